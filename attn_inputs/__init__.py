@@ -1,0 +1,153 @@
+"""Seeded synthetic inputs for the attention forward pass.
+
+This module is shared by the oracle's tests, the GPU parity tests and the
+bench. It holds none of the attention arithmetic: it only draws numbers,
+rounds them to the storage type and converts storage types to float64.
+
+Draws: numpy's Philox counter-based generator keyed by (seed, stream), so
+every tensor has its own independent stream and the same numbers come out on
+any machine with the same numpy. Normal samples are float32 N(0, 1); bf16
+tensors are those samples rounded to nearest-even and held as raw uint16 bit
+patterns.
+
+Stream ids: Q=0, K=1, V=2, integers (kv_len) = 3.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+import hashlib
+
+import numpy as np
+
+STREAM_Q, STREAM_K, STREAM_V, STREAM_INT = 0, 1, 2, 3
+
+
+def _gen(seed: int, stream: int) -> np.random.Generator:
+    return np.random.Generator(
+        np.random.Philox(key=np.array([seed, stream], dtype=np.uint64)))
+
+
+def normal_f32(shape, seed: int, stream: int) -> np.ndarray:
+    """float32 N(0,1) samples of `shape` from stream (seed, stream)."""
+    n = int(np.prod(shape))
+    return _gen(seed, stream).standard_normal(n, dtype=np.float32).reshape(shape)
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 to bfloat16 (nearest, ties to even); return uint16 bits.
+
+    Inputs here are finite normal samples, so NaN handling is not needed; an
+    infinity stays an infinity.
+    """
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    lsb = (u >> np.uint32(16)) & np.uint32(1)
+    return ((u + np.uint32(0x7FFF) + lsb) >> np.uint32(16)).astype(np.uint16)
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    """Exact widening of bfloat16 bit patterns to float32."""
+    return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def to_f64(x: np.ndarray, dtype: str) -> np.ndarray:
+    """Exact float64 view of a stored tensor ("bf16" bits or "f32")."""
+    if dtype == "bf16":
+        return bf16_bits_to_f32(x).astype(np.float64)
+    return np.asarray(x, dtype=np.float32).astype(np.float64)
+
+
+def sha256(a: np.ndarray) -> str:
+    return hashlib.sha256(np.ascontiguousarray(a).tobytes()).hexdigest()
+
+
+@dataclass
+class AttnInputs:
+    """One attention problem. q/k/v are uint16 bf16 bits or float32 arrays.
+
+    Dense:     q [B,H,Lq,d], k/v [B,Hkv,Lk,d], kv_len [B] or None.
+    Broadcast: q [B_c,H,Lq,d], k/v [B_u,Hkv,Lk,d], cand2user [B_c],
+               kv_len [B_u] or None.
+    """
+    q: np.ndarray
+    k: np.ndarray
+    v: np.ndarray
+    dtype: str
+    causal: bool = False
+    kv_len: np.ndarray | None = None
+    cand2user: np.ndarray | None = None
+    scale: float | None = None
+    meta: dict = field(default_factory=dict)
+
+    def f64(self):
+        return to_f64(self.q, self.dtype), to_f64(self.k, self.dtype), to_f64(self.v, self.dtype)
+
+
+def _draw(shape, dtype, seed, stream):
+    x = normal_f32(shape, seed, stream)
+    return f32_to_bf16_bits(x) if dtype == "bf16" else x
+
+
+def make_dense(B, H, Hkv, Lq, Lk, d, *, dtype="bf16", causal=False, seed=0,
+               kv_len_range=None, scale=None) -> AttnInputs:
+    """Dense / causal / GQA / kv_len-masked problem with iid N(0,1) entries.
+
+    kv_len_range=(lo, hi) draws kv_len[b] uniformly from the integers lo..hi
+    inclusive on the integer stream.
+    """
+    q = _draw((B, H, Lq, d), dtype, seed, STREAM_Q)
+    k = _draw((B, Hkv, Lk, d), dtype, seed, STREAM_K)
+    v = _draw((B, Hkv, Lk, d), dtype, seed, STREAM_V)
+    kv_len = None
+    if kv_len_range is not None:
+        lo, hi = kv_len_range
+        kv_len = _gen(seed, STREAM_INT).integers(lo, hi + 1, size=B).astype(np.int32)
+    return AttnInputs(q, k, v, dtype, causal=causal, kv_len=kv_len, scale=scale,
+                      meta=dict(kind="dense", B=B, H=H, Hkv=Hkv, Lq=Lq, Lk=Lk, d=d))
+
+
+def make_bcast(B_c, B_u, H, Hkv, Lq, Lk, d, *, dtype="bf16", causal=False, seed=0,
+               cand2user=None, kv_len_range=None, scale=None) -> AttnInputs:
+    """Broadcast problem: B_c candidates' queries, B_u users' keys/values.
+
+    cand2user defaults to the contiguous grouping c -> c // (B_c // B_u).
+    """
+    q = _draw((B_c, H, Lq, d), dtype, seed, STREAM_Q)
+    k = _draw((B_u, Hkv, Lk, d), dtype, seed, STREAM_K)
+    v = _draw((B_u, Hkv, Lk, d), dtype, seed, STREAM_V)
+    if cand2user is None:
+        per = max(1, B_c // B_u)
+        cand2user = np.minimum(np.arange(B_c) // per, B_u - 1)
+    cand2user = np.asarray(cand2user, dtype=np.int32)
+    kv_len = None
+    if kv_len_range is not None:
+        lo, hi = kv_len_range
+        kv_len = _gen(seed, STREAM_INT).integers(lo, hi + 1, size=B_u).astype(np.int32)
+    return AttnInputs(q, k, v, dtype, causal=causal, kv_len=kv_len, cand2user=cand2user,
+                      scale=scale,
+                      meta=dict(kind="bcast", B_c=B_c, B_u=B_u, H=H, Hkv=Hkv, Lq=Lq, Lk=Lk, d=d))
+
+
+# The workloads the method is measured on: tiny fp32 parity case, dense causal,
+# in-kernel broadcast, kv_len-masked, long-sequence GQA causal.
+WORKLOADS = {
+    "fp32_tiny": dict(kind="dense", B=1, H=1, Hkv=1, Lq=128, Lk=128, d=64, dtype="f32",
+                      causal=False),
+    "dense_causal_L2048": dict(kind="dense", B=4, H=16, Hkv=16, Lq=2048, Lk=2048, d=128,
+                               dtype="bf16", causal=True),
+    "bcast_Bc1024_Bu32": dict(kind="bcast", B_c=1024, B_u=32, H=8, Hkv=8, Lq=64, Lk=1024,
+                              d=128, dtype="bf16", causal=False),
+    "masked_kvlen_L4096_d64": dict(kind="dense", B=8, H=16, Hkv=16, Lq=4096, Lk=4096, d=64,
+                                   dtype="bf16", causal=False, kv_len_range=(2048, 4096)),
+    "gqa_causal_L16384": dict(kind="dense", B=1, H=32, Hkv=8, Lq=16384, Lk=16384, d=128,
+                              dtype="bf16", causal=True),
+}
+
+
+def make_workload(name: str, seed: int = 0) -> AttnInputs:
+    w = dict(WORKLOADS[name])
+    kind = w.pop("kind")
+    if kind == "dense":
+        return make_dense(w.pop("B"), w.pop("H"), w.pop("Hkv"), w.pop("Lq"), w.pop("Lk"),
+                          w.pop("d"), seed=seed, **w)
+    return make_bcast(w.pop("B_c"), w.pop("B_u"), w.pop("H"), w.pop("Hkv"), w.pop("Lq"),
+                      w.pop("Lk"), w.pop("d"), seed=seed, **w)

@@ -1,0 +1,158 @@
+"""Plain float64 CPU oracle for the attention forward pass.
+
+TEST INFRASTRUCTURE ONLY. Nothing on the product path imports, calls or
+links this package; only the tests, the package smoke check and the bench's
+CPU-baseline leg use it. It shares no code with the HIP path.
+
+What it computes (plain definition, full softmax materialised on purpose):
+
+  For every batch b, head h, query row i, with g = h // (H // Hkv):
+    s[i, j] = scale * sum_t q[b,h,i,t] * k[b,g,j,t]             j < Lk
+    s[i, j] = -inf  where (causal and j > i) or (kv_len given and
+                                              j >= clamp(kv_len[b], 0, Lk))
+    p[i, j] = exp(s[i,j] - max_j s[i,j]) / sum_j exp(s[i,j] - max_j s[i,j])
+    o[b,h,i,:] = sum_j p[i,j] * v[b,g,j,:]      (o = 0 when no key is valid)
+
+Sources. The tutorial page "Guide de programmation pour la programmation GPU
+par tuiles de NVIDIA : de cuTile et des noyaux Triton à Flash Attention"
+(flash-attention paragraph and conclusion) fixes the operation: attention
+checked against PyTorch's scaled-dot-product attention, which a tiled kernel
+computes with an online softmax so the score matrix is never stored. This
+oracle is that comparator's definition written out and does store it. The
+broadcast variant follows "How We Built TLX" (Chinese translation, section
+"Case study 2: in-kernel broadcast optimisation for RecSys"): candidate
+queries read their user's keys/values at the users' own batch size, with no
+replication; here that is q[c] attending over k[cand2user[c]],
+v[cand2user[c]].
+
+Readings where the pages are silent (each is also listed with the design
+notes): scale defaults to 1/sqrt(d); the mask is additive -inf; causal is
+top-left (key j allowed iff j <= i); kv_len is one value per K/V batch entry,
+clamped to [0, Lk], masking keys only; a row with no valid key outputs 0; GQA
+maps query head h to K/V head h // (H // Hkv); a candidate whose cand2user is
+out of range gets NaN rows.
+
+Parity pins: every function here is pinned by tests/test_oracle_pins.py
+(closed forms, exact rational golden fixture, invariants, brute force in
+40-digit decimal arithmetic, PyTorch float64 SDPA special cases) and
+tests/test_oracle_mutants.py shows that plausible planted mistakes fail at
+least one pin. No function is parity-unpinned.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+__all__ = ["attention", "attention_rows", "attention_bcast", "probabilities"]
+
+
+def _default_scale(d: int, scale) -> float:
+    # Scale reading: 1/sqrt(d) unless the caller gives one; 0 also means default.
+    if scale is None or scale == 0:
+        return 1.0 / math.sqrt(d)
+    return float(scale)
+
+
+def _allowed(rows: np.ndarray, Lk: int, causal: bool, kv_len_b) -> np.ndarray:
+    """Boolean [len(rows), Lk]: which (query i, key j) pairs are not masked."""
+    j = np.arange(Lk)[None, :]
+    i = np.asarray(rows)[:, None]
+    ok = np.ones((len(rows), Lk), dtype=bool)
+    if kv_len_b is not None:
+        n = min(max(int(kv_len_b), 0), Lk)
+        ok &= j < n
+    if causal:
+        ok &= j <= i
+    return ok
+
+
+def _softmax_rows(s: np.ndarray, ok: np.ndarray) -> np.ndarray:
+    """Row softmax of s over the allowed entries; rows with none give zeros."""
+    s = np.where(ok, s, -np.inf)
+    m = s.max(axis=1, keepdims=True)
+    m = np.where(np.isfinite(m), m, 0.0)
+    e = np.where(ok, np.exp(s - m), 0.0)
+    z = e.sum(axis=1, keepdims=True)
+    return np.divide(e, z, out=np.zeros_like(e), where=z > 0)
+
+
+def _head_rows(q_bh, k_bg, v_bg, rows, causal, kv_len_b, scale):
+    s = scale * (q_bh[rows] @ k_bg.T)          # [R, Lk] scores
+    p = _softmax_rows(s, _allowed(rows, k_bg.shape[0], causal, kv_len_b))
+    return p @ v_bg, p
+
+
+def probabilities(q, k, v, *, causal=False, kv_len=None, scale=None, b=0, h=0):
+    """The full softmax matrix P [Lq, Lk] of one (b, h); used by the invariant pins."""
+    q, k = np.asarray(q, np.float64), np.asarray(k, np.float64)
+    B, H, Lq, d = q.shape
+    g = h // (H // k.shape[1])
+    kvl = None if kv_len is None else kv_len[b]
+    _, p = _head_rows(q[b, h], k[b, g], np.asarray(v, np.float64)[b, g], np.arange(Lq),
+                      causal, kvl, _default_scale(d, scale))
+    return p
+
+
+def attention(q, k, v, *, causal=False, kv_len=None, scale=None):
+    """Dense / causal / kv_len-masked / GQA attention forward, float64.
+
+    q [B,H,Lq,d], k and v [B,Hkv,Lk,d] (any real dtype, widened exactly to
+    float64), kv_len None or int array [B]. Returns o [B,H,Lq,d] float64.
+    """
+    q, k, v = (np.asarray(x, np.float64) for x in (q, k, v))
+    B, H, Lq, d = q.shape
+    Hkv, Lk = k.shape[1], k.shape[2]
+    assert H % Hkv == 0 and k.shape == v.shape == (B, Hkv, Lk, d)
+    group = H // Hkv
+    sc = _default_scale(d, scale)
+    o = np.zeros((B, H, Lq, d))
+    rows = np.arange(Lq)
+    for b in range(B):
+        kvl = None if kv_len is None else kv_len[b]
+        for h in range(H):
+            g = h // group
+            o[b, h], _ = _head_rows(q[b, h], k[b, g], v[b, g], rows, causal, kvl, sc)
+    return o
+
+
+def attention_rows(q, k, v, b, h, rows, *, causal=False, kv_len=None, scale=None):
+    """Output rows o[b, h, rows, :] only (for sampled checks at full size)."""
+    q_bh = np.asarray(q[b, h], np.float64)
+    H, Hkv = q.shape[1], k.shape[1]
+    g = h // (H // Hkv)
+    k_bg, v_bg = np.asarray(k[b, g], np.float64), np.asarray(v[b, g], np.float64)
+    kvl = None if kv_len is None else kv_len[b]
+    out, _ = _head_rows(q_bh, k_bg, v_bg, np.asarray(rows), causal, kvl,
+                        _default_scale(q.shape[3], scale))
+    return out
+
+
+def attention_bcast(q, k, v, cand2user, *, causal=False, kv_len=None, scale=None,
+                    cands=None, rows=None):
+    """In-kernel-broadcast attention: candidate c attends to user cand2user[c].
+
+    q [B_c,H,Lq,d]; k, v [B_u,Hkv,Lk,d]; cand2user [B_c]; kv_len None or [B_u].
+    Candidates whose user index is outside [0, B_u) get NaN rows.
+    cands / rows optionally restrict the candidates and query rows computed;
+    the result then has shape [len(cands), H, len(rows), d].
+    """
+    B_c, H, Lq, d = q.shape
+    B_u, Hkv = k.shape[0], k.shape[1]
+    group = H // Hkv
+    sc = _default_scale(d, scale)
+    cands = np.arange(B_c) if cands is None else np.asarray(cands)
+    rows = np.arange(Lq) if rows is None else np.asarray(rows)
+    o = np.zeros((len(cands), H, len(rows), d))
+    for n, c in enumerate(cands):
+        u = int(cand2user[c])
+        if not 0 <= u < B_u:
+            o[n] = np.nan
+            continue
+        kvl = None if kv_len is None else kv_len[u]
+        for h in range(H):
+            g = h // group
+            o[n, h], _ = _head_rows(np.asarray(q[c, h], np.float64),
+                                    np.asarray(k[u, g], np.float64),
+                                    np.asarray(v[u, g], np.float64), rows, causal, kvl, sc)
+    return o

@@ -1,0 +1,304 @@
+"""Pins for the float64 oracle: facts fixed by the mathematics, not by the oracle.
+
+Each pin takes an implementation namespace `impl` (the oracle package, or a
+mutant of it built in tests/test_oracle_mutants.py) and raises AssertionError
+when `impl` disagrees with the fact. The pins are chosen so that a plausible
+slip anywhere in the oracle (a dropped scale, a wrong mask bound, a wrong
+head or user index, the wrong operand or reduction axis) fails at least one.
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+from decimal import Decimal, getcontext
+from fractions import Fraction
+
+import numpy as np
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+def _rand(shape, seed):
+    return _rng(seed).standard_normal(shape)
+
+
+# --- exact worked example ---------------------------------------------------
+
+def pin_golden_rational(impl):
+    """Hand-derived rational outputs (tests/golden/rational_case.json)."""
+    with open(os.path.join(GOLDEN, "rational_case.json")) as f:
+        g = json.load(f)
+    q = np.array(g["q"], float)[None, None]
+    k = np.array(g["k"], float)[None, None]
+    v = np.array(g["v"], float)[None, None]
+    for case in g["cases"]:
+        kv = None if case["kv_len"] is None else np.array([case["kv_len"]])
+        o = impl.attention(q, k, v, causal=case["causal"], kv_len=kv, scale=math.log(2))
+        want = np.array([[float(Fraction(x)) for x in row] for row in case["o"]])
+        np.testing.assert_allclose(o[0, 0], want, rtol=0, atol=1e-14, err_msg=str(case))
+
+
+# --- closed forms -------------------------------------------------------------
+
+def pin_two_key_sigmoid(impl):
+    """Two keys: o = sigma(D) v0 + sigma(-D) v1 with D = scale (q.k0 - q.k1)."""
+    d = 8
+    q, k, v = _rand((2, 3, 5, d), 1), _rand((2, 3, 2, d), 2), _rand((2, 3, 2, d), 3)
+    sc = 0.37
+    o = impl.attention(q, k, v, scale=sc)
+    for b in range(2):
+        for h in range(3):
+            for i in range(5):
+                D = sc * (float(np.dot(q[b, h, i], k[b, h, 0])) - float(np.dot(q[b, h, i], k[b, h, 1])))
+                w0 = 0.5 * (1.0 + math.tanh(D / 2))
+                want = w0 * v[b, h, 0] + (1.0 - w0) * v[b, h, 1]
+                np.testing.assert_allclose(o[b, h, i], want, rtol=0, atol=1e-13)
+
+
+def pin_default_scale(impl):
+    """scale None and 0 both mean 1/sqrt(d) (checked on two keys, closed form)."""
+    d = 16
+    q, k, v = _rand((1, 1, 3, d), 4), _rand((1, 1, 2, d), 5), _rand((1, 1, 2, d), 6)
+    for s in (None, 0.0):
+        o = impl.attention(q, k, v, scale=s)
+        for i in range(3):
+            D = (float(np.dot(q[0, 0, i], k[0, 0, 0])) - float(np.dot(q[0, 0, i], k[0, 0, 1]))) / math.sqrt(d)
+            w0 = 0.5 * (1.0 + math.tanh(D / 2))
+            np.testing.assert_allclose(o[0, 0, i], w0 * v[0, 0, 0] + (1 - w0) * v[0, 0, 1],
+                                       rtol=0, atol=1e-13)
+
+
+def pin_constant_v(impl):
+    """Every v_j equal to c gives o = c for every row with a valid key."""
+    B, H, L, d = 2, 2, 9, 4
+    q, k = _rand((B, H, L, d), 7), _rand((B, H, L, d), 8)
+    c = _rand((d,), 9)
+    v = np.broadcast_to(c, (B, H, L, d)).copy()
+    for causal in (False, True):
+        for kv in (None, np.array([9, 3])):
+            o = impl.attention(q, k, v, causal=causal, kv_len=kv)
+            np.testing.assert_allclose(o, np.broadcast_to(c, o.shape), rtol=0, atol=1e-14)
+
+
+def pin_single_key(impl):
+    """Lk = 1: o = v_0 whatever q, k and the scale are."""
+    q, k, v = _rand((2, 4, 6, 8), 10), _rand((2, 2, 1, 8), 11), _rand((2, 2, 1, 8), 12)
+    o = impl.attention(q, k, v, scale=3.0)
+    want = np.repeat(v, 2, axis=1)  # heads 0,1 -> kv 0; heads 2,3 -> kv 1
+    np.testing.assert_allclose(o, np.broadcast_to(want, o.shape), rtol=0, atol=1e-14)
+
+
+def pin_zero_query_mean(impl):
+    """q = 0: all valid scores are equal, so o is the plain mean of the valid v_j.
+
+    With causal (top-left) row i sees keys 0..i; with kv_len n sees keys 0..n-1.
+    """
+    B, H, Lq, Lk, d = 2, 1, 7, 6, 3
+    q = np.zeros((B, H, Lq, d))
+    k, v = _rand((B, H, Lk, d), 13), _rand((B, H, Lk, d), 14)
+    kv = np.array([4, 6])
+    for causal in (False, True):
+        o = impl.attention(q, k, v, causal=causal, kv_len=kv)
+        for b in range(B):
+            for i in range(Lq):
+                n = kv[b] if not causal else min(kv[b], i + 1)
+                np.testing.assert_allclose(o[b, 0, i], v[b, 0, :n].mean(axis=0), rtol=0, atol=1e-14)
+
+
+def pin_fully_masked_zero(impl):
+    """kv_len = 0 leaves no valid key: the output row is exactly 0."""
+    q, k, v = _rand((2, 2, 5, 4), 15), _rand((2, 2, 5, 4), 16), _rand((2, 2, 5, 4), 17)
+    o = impl.attention(q, k, v, kv_len=np.array([0, 5]))
+    assert np.all(o[0] == 0.0)
+    assert np.all(np.abs(o[1]) > 0)
+
+
+def pin_causal_first_row(impl):
+    """Causal row 0 sees key 0 only: o[.,.,0] = v_0 exactly."""
+    q, k, v = _rand((2, 4, 5, 8), 18), _rand((2, 2, 7, 8), 19), _rand((2, 2, 7, 8), 20)
+    o = impl.attention(q, k, v, causal=True)
+    np.testing.assert_allclose(o[:, :, 0], np.repeat(v[:, :, 0], 2, axis=1), rtol=0, atol=1e-15)
+
+
+def pin_hard_max_limit(impl):
+    """Large scale with distinct logits: softmax -> one-hot at argmax_j q.k_j."""
+    q, k, v = _rand((1, 2, 6, 8), 21), _rand((1, 2, 9, 8), 22), _rand((1, 2, 9, 8), 23)
+    o = impl.attention(q, k, v, scale=1e4)
+    for h in range(2):
+        for i in range(6):
+            j = int(np.argmax(k[0, h] @ q[0, h, i]))
+            np.testing.assert_allclose(o[0, h, i], v[0, h, j], rtol=0, atol=1e-12)
+
+
+# --- invariants -----------------------------------------------------------------
+
+def pin_probabilities_rows(impl):
+    """P rows sum to 1 over valid keys; masked entries are exactly 0."""
+    q, k, v = _rand((2, 2, 8, 4), 24), _rand((2, 2, 8, 4), 25), _rand((2, 2, 8, 4), 26)
+    kv = np.array([5, 8])
+    for causal in (False, True):
+        for b in range(2):
+            p = impl.probabilities(q, k, v, causal=causal, kv_len=kv, b=b, h=1)
+            np.testing.assert_allclose(p.sum(axis=1), 1.0, rtol=0, atol=1e-14)
+            i, j = np.meshgrid(np.arange(8), np.arange(8), indexing="ij")
+            masked = (j >= kv[b]) | ((j > i) if causal else False)
+            assert np.all(p[masked] == 0.0) and np.all(p[~masked] > 0.0)
+
+
+def pin_key_permutation(impl):
+    """No mask: permuting the keys and values together leaves o unchanged."""
+    q, k, v = _rand((2, 2, 5, 8), 27), _rand((2, 2, 11, 8), 28), _rand((2, 2, 11, 8), 29)
+    perm = _rng(30).permutation(11)
+    o1 = impl.attention(q, k, v)
+    o2 = impl.attention(q, k[:, :, perm], v[:, :, perm])
+    np.testing.assert_allclose(o1, o2, rtol=0, atol=1e-13)
+
+
+def pin_key_shift(impl):
+    """k_j += w for all j adds the same constant to a row's scores: o unchanged."""
+    q, k, v = _rand((1, 2, 6, 8), 31), _rand((1, 2, 6, 8), 32), _rand((1, 2, 6, 8), 33)
+    w = _rand((8,), 34)
+    for causal in (False, True):
+        o1 = impl.attention(q, k, v, causal=causal, kv_len=np.array([4]))
+        o2 = impl.attention(q, k + w, v, causal=causal, kv_len=np.array([4]))
+        np.testing.assert_allclose(o1, o2, rtol=0, atol=1e-12)
+
+
+def pin_scale_homogeneity(impl):
+    """attention(a*q, scale=s) equals attention(q, scale=a*s)."""
+    q, k, v = _rand((1, 2, 5, 8), 35), _rand((1, 2, 7, 8), 36), _rand((1, 2, 7, 8), 37)
+    o1 = impl.attention(2.5 * q, k, v, scale=0.2)
+    o2 = impl.attention(q, k, v, scale=0.5)
+    np.testing.assert_allclose(o1, o2, rtol=0, atol=1e-13)
+
+
+def pin_gqa_is_head_repeat(impl):
+    """GQA equals multi-head attention with each K/V head repeated H/Hkv times
+    in contiguous groups (query head h uses K/V head h // (H/Hkv))."""
+    q, k, v = _rand((2, 6, 5, 4), 38), _rand((2, 2, 7, 4), 39), _rand((2, 2, 7, 4), 40)
+    for causal in (False, True):
+        o1 = impl.attention(q, k, v, causal=causal)
+        o2 = impl.attention(q, np.repeat(k, 3, axis=1), np.repeat(v, 3, axis=1), causal=causal)
+        np.testing.assert_allclose(o1, o2, rtol=0, atol=1e-14)
+    # the grouped heads must really differ from an interleaved (h % Hkv) map
+    o_wrong = impl.attention(q, np.tile(k, (1, 3, 1, 1)), np.tile(v, (1, 3, 1, 1)))
+    assert np.abs(impl.attention(q, k, v) - o_wrong).max() > 1e-3
+
+
+def pin_kv_len_is_truncation(impl):
+    """kv_len = n equals dense attention over the first n keys; kv_len = Lk equals no mask."""
+    q, k, v = _rand((3, 2, 6, 4), 41), _rand((3, 2, 9, 4), 42), _rand((3, 2, 9, 4), 43)
+    kv = np.array([1, 5, 9])
+    for causal in (False, True):
+        o = impl.attention(q, k, v, causal=causal, kv_len=kv)
+        for b, n in enumerate(kv):
+            ref = impl.attention(q[b:b + 1], k[b:b + 1, :, :n], v[b:b + 1, :, :n], causal=causal)
+            np.testing.assert_allclose(o[b:b + 1], ref, rtol=0, atol=1e-14)
+    o_full = impl.attention(q, k, v, kv_len=np.array([9, 9, 9]))
+    np.testing.assert_allclose(o_full, impl.attention(q, k, v), rtol=0, atol=0)
+    o_over = impl.attention(q, k, v, kv_len=np.array([50, -3, 9]))  # clamped to [0, Lk]
+    np.testing.assert_allclose(o_over[0], impl.attention(q, k, v)[0], rtol=0, atol=0)
+    assert np.all(o_over[1] == 0.0)
+
+
+def pin_bcast_is_replication(impl):
+    """Broadcast equals explicit replication k[cand2user], v[cand2user] (bit-equal);
+    an out-of-range user index yields NaN rows."""
+    B_c, B_u = 7, 3
+    q = _rand((B_c, 4, 5, 8), 44)
+    k, v = _rand((B_u, 2, 6, 8), 45), _rand((B_u, 2, 6, 8), 46)
+    c2u = np.array([2, 0, 0, 1, 2, 1, 0])
+    kv = np.array([6, 2, 4])
+    for causal in (False, True):
+        o1 = impl.attention_bcast(q, k, v, c2u, causal=causal, kv_len=kv)
+        o2 = impl.attention(q, k[c2u], v[c2u], causal=causal, kv_len=kv[c2u])
+        assert np.array_equal(o1, o2)
+    bad = c2u.copy()
+    bad[3] = B_u
+    o3 = impl.attention_bcast(q, k, v, bad)
+    assert np.all(np.isnan(o3[3])) and not np.any(np.isnan(np.delete(o3, 3, axis=0)))
+    sub = impl.attention_bcast(q, k, v, c2u, cands=[4, 1], rows=[3, 0])
+    full = impl.attention_bcast(q, k, v, c2u)
+    np.testing.assert_array_equal(sub, full[[4, 1]][:, :, [3, 0]])
+
+
+def pin_rows_subset(impl):
+    """attention_rows returns exactly the requested rows of attention()."""
+    q, k, v = _rand((2, 4, 9, 8), 47), _rand((2, 2, 9, 8), 48), _rand((2, 2, 9, 8), 49)
+    kv = np.array([7, 3])
+    for causal in (False, True):
+        full = impl.attention(q, k, v, causal=causal, kv_len=kv)
+        rows = np.array([8, 0, 4])
+        for b in range(2):
+            for h in range(4):
+                part = impl.attention_rows(q, k, v, b, h, rows, causal=causal, kv_len=kv)
+                np.testing.assert_array_equal(part, full[b, h, rows])
+
+
+# --- brute force ------------------------------------------------------------------
+
+def _brute_decimal(q, k, v, causal, kv_len, scale):
+    """Direct 40-digit evaluation: exp of the raw scores (no max shift), explicit loops."""
+    getcontext().prec = 40
+    B, H, Lq, d = q.shape
+    Hkv, Lk = k.shape[1], k.shape[2]
+    sc = Decimal(repr(scale))
+    o = np.zeros(q.shape)
+    for b in range(B):
+        for h in range(H):
+            g = (h * Hkv) // H
+            for i in range(Lq):
+                ws, num = [], [Decimal(0)] * d
+                for j in range(Lk):
+                    if causal and j > i:
+                        continue
+                    if kv_len is not None and j >= kv_len[b]:
+                        continue
+                    s = sum(Decimal(repr(float(q[b, h, i, t]))) * Decimal(repr(float(k[b, g, j, t])))
+                            for t in range(d))
+                    w = (sc * s).exp()
+                    ws.append(w)
+                    for t in range(d):
+                        num[t] += w * Decimal(repr(float(v[b, g, j, t])))
+                z = sum(ws, Decimal(0))
+                if z > 0:
+                    o[b, h, i] = [float(x / z) for x in num]
+    return o
+
+
+def pin_brute_force(impl):
+    """Tiny shapes, every mask combination and GQA: 40-digit brute force."""
+    q, k, v = _rand((2, 4, 5, 3), 50), _rand((2, 2, 6, 3), 51), _rand((2, 2, 6, 3), 52)
+    for causal in (False, True):
+        for kv in (None, np.array([6, 2])):
+            for sc in (0.7, 1.0 / math.sqrt(3)):
+                o = impl.attention(q, k, v, causal=causal, kv_len=kv, scale=sc)
+                ref = _brute_decimal(q, k, v, causal, kv, sc)
+                np.testing.assert_allclose(o, ref, rtol=0, atol=1e-12)
+
+
+# --- library special case -------------------------------------------------------------
+
+def pin_torch_sdpa(impl):
+    """PyTorch's float64 CPU scaled_dot_product_attention on the cases it expresses."""
+    import torch
+    import torch.nn.functional as F
+    q, k, v = _rand((2, 4, 6, 8), 53), _rand((2, 2, 9, 8), 54), _rand((2, 2, 9, 8), 55)
+    tq, tk, tv = (torch.from_numpy(x) for x in (q, k, v))
+    kv = np.array([9, 4])
+    for causal in (False, True):
+        ref = F.scaled_dot_product_attention(tq, tk, tv, is_causal=causal, scale=0.3,
+                                             enable_gqa=True).numpy()
+        np.testing.assert_allclose(impl.attention(q, k, v, causal=causal, scale=0.3), ref,
+                                   rtol=0, atol=1e-13)
+    mask = torch.from_numpy(np.arange(9)[None, :] < kv[:, None])[:, None, None, :]
+    ref = F.scaled_dot_product_attention(tq, tk, tv, attn_mask=mask, enable_gqa=True).numpy()
+    np.testing.assert_allclose(impl.attention(q, k, v, kv_len=kv), ref, rtol=0, atol=1e-13)
+
+
+ALL_PINS = [v for n, v in sorted(globals().items()) if n.startswith("pin_")]

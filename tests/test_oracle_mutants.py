@@ -1,0 +1,57 @@
+"""Planted mistakes in a copy of the oracle must each fail at least one pin.
+
+Each mutant is the oracle's source with one plausible slip substituted in
+(CPU only, nothing touches the GPU). If a mutant passed every pin, the pins
+would not be strong enough to trust the oracle.
+"""
+import inspect
+import types
+
+import pytest
+
+import oracle
+from pins import ALL_PINS
+
+MUTANTS = {
+    "causal_off_by_one": ("ok &= j <= i", "ok &= j < i"),
+    "causal_bottom_right": ("ok &= j <= i", "ok &= j <= i + (Lk - 1 - i.max())"),
+    "kv_len_inclusive": ("ok &= j < n", "ok &= j <= n"),
+    "kv_len_ignored": ("n = min(max(int(kv_len_b), 0), Lk)", "n = Lk"),
+    "kv_len_masks_queries": ("ok &= j < n", "ok &= i < n"),
+    "scale_dropped": ("s = scale * (q_bh[rows] @ k_bg.T)", "s = (q_bh[rows] @ k_bg.T)"),
+    "default_scale_1_over_d": ("return 1.0 / math.sqrt(d)", "return 1.0 / d"),
+    "max_wrong_axis": ("m = s.max(axis=1, keepdims=True)", "m = s.max(axis=0, keepdims=True)"),
+    "sum_wrong_axis": ("z = e.sum(axis=1, keepdims=True)", "z = e.sum(axis=0, keepdims=True)"),
+    "values_are_keys": ("return p @ v_bg, p", "return p @ k_bg, p"),
+    "gqa_interleaved": ("g = h // group", "g = h % Hkv"),
+    "gqa_rows_interleaved": ("g = h // (H // Hkv)", "g = h % Hkv"),
+    "bcast_ignores_map": ("u = int(cand2user[c])", "u = int(c) % B_u"),
+    "bcast_kvlen_by_candidate": ("kvl = None if kv_len is None else kv_len[u]",
+                                 "kvl = None if kv_len is None else kv_len[min(c, B_u - 1)]"),
+    "bcast_no_nan": ("o[n] = np.nan", "o[n] = 0.0"),
+    "masked_row_not_zero": ("where=z > 0)", "where=z >= 0)"),
+    "exp_base_2": ("np.exp(s - m)", "np.exp2(s - m)"),
+}
+
+
+def _mutant(name):
+    src = inspect.getsource(oracle)
+    old, new = MUTANTS[name]
+    assert old in src, f"mutation anchor missing for {name}: {old!r}"
+    mod = types.ModuleType(f"oracle_mutant_{name}")
+    exec(compile(src.replace(old, new), mod.__name__, "exec"), mod.__dict__)
+    return mod
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name):
+    mod = _mutant(name)
+    caught = []
+    for pin in ALL_PINS:
+        if pin.__name__ in ("pin_brute_force",):   # slow; the others suffice
+            continue
+        try:
+            pin(mod)
+        except Exception:
+            caught.append(pin.__name__)
+    assert caught, f"mutant {name} passed every pin"
