@@ -1,0 +1,102 @@
+/*
+ * attn.h - C ABI of the MI355X (gfx950) fused tiled attention forward pass.
+ *
+ * Operation. For every batch entry b, query head h and query row i,
+ *     O[b,h,i,:] = sum_j softmax_j( scale * <Q[b,h,i,:], K[b,g,j,:]> + mask[i,j] ) * V[b,g,j,:]
+ * with g = h / (H / Hkv) (grouped-query heads: contiguous groups of H/Hkv
+ * query heads share one K/V head). The tutorial page "Guide de programmation
+ * pour la programmation GPU par tuiles de NVIDIA : de cuTile et des noyaux
+ * Triton a Flash Attention" (flash-attention paragraph and conclusion) gives
+ * the method: attention computed tile by tile with an online softmax so the
+ * Lq x Lk score matrix is never materialised, checked against PyTorch's
+ * scaled-dot-product attention. The in-kernel broadcast variant follows "How
+ * We Built TLX" (Chinese translation, "Case study 2: in-kernel broadcast
+ * optimisation for RecSys"): candidates and users arrive at their own batch
+ * sizes and the kernel reads each candidate's user K/V through an index, with
+ * no replicated copy in memory.
+ *
+ * Mask (additive -inf, so masked probabilities are exactly 0):
+ *   - causal != 0: key j is allowed for query row i iff j <= i (top-left
+ *     alignment, the same as PyTorch SDPA's is_causal, also when Lq != Lk);
+ *   - kv_len != NULL: key j is allowed iff j < clamp(kv_len[kv batch], 0, Lk);
+ *     it masks keys only, every query row is computed;
+ *   - the two combine by AND. A row with no allowed key is written as 0.
+ *
+ * Layout. Every tensor is contiguous row-major [batch, heads, seq, d], d
+ * fastest (the PyTorch SDPA layout). q/k/v/o all have the element type
+ * `dtype`: ATTN_BF16 (bfloat16; products accumulate in fp32 and the output is
+ * rounded to nearest-even) or ATTN_F32. Base pointers must be 16-byte aligned.
+ * All pointers are DEVICE pointers (HIP device memory of the current device).
+ *
+ * Ownership and concurrency. The caller owns every buffer. The library keeps
+ * no state between calls and allocates nothing; calls are reentrant. Work is
+ * enqueued on `stream` (a hipStream_t; NULL = the default stream) and the
+ * call returns without synchronising. o must not alias q, k or v.
+ *
+ * Errors. The return value is an attn_status. All argument checks run before
+ * any HIP call. Device-resident values cannot be checked without a sync, so:
+ * kv_len values are clamped to [0, Lk]; a cand2user value outside [0, B_u)
+ * makes that candidate's output rows NaN.
+ */
+#ifndef ATTN_H_
+#define ATTN_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  ATTN_OK = 0,
+  ATTN_EINVAL = -1,       /* bad argument: NULL pointer, negative size, H % Hkv != 0,
+                             misaligned pointer, non-finite or negative scale, size overflow */
+  ATTN_EUNSUPPORTED = -2, /* head dim d not in {64, 128}, or unknown dtype */
+  ATTN_ELAUNCH = -3       /* the HIP launch reported an error */
+} attn_status;
+
+typedef enum { ATTN_F32 = 0, ATTN_BF16 = 1 } attn_dtype;
+
+/*
+ * Dense / causal / kv_len-masked / grouped-query attention forward.
+ *   q      [B, H,   Lq, d]   queries
+ *   k, v   [B, Hkv, Lk, d]   keys and values
+ *   o      [B, H,   Lq, d]   output (written)
+ *   kv_len [B] int32 or NULL (NULL: all Lk keys valid)
+ *   scale  softmax scale; 0 means 1/sqrt(d); must be finite and >= 0
+ * B, H, Lq, Lk >= 0 (an empty problem returns ATTN_OK and launches nothing;
+ * Lk == 0 writes zeros), Hkv >= 1 with H % Hkv == 0.
+ */
+int attn_fwd(const void* q, const void* k, const void* v, void* o,
+             int B, int H, int Hkv, int Lq, int Lk, int d,
+             int causal, const int32_t* kv_len, float scale,
+             int dtype, void* stream);
+
+/*
+ * In-kernel broadcast attention forward: candidate c attends over the K/V of
+ * user cand2user[c], read in place (never replicated).
+ *   q         [B_c, H,   Lq, d]  candidate queries
+ *   k, v      [B_u, Hkv, Lk, d]  user keys and values
+ *   o         [B_c, H,   Lq, d]  output (written)
+ *   cand2user [B_c] int32, values in [0, B_u) (others give NaN rows)
+ *   kv_len    [B_u] int32 or NULL, indexed by user
+ * Other arguments as attn_fwd. The result is bit-identical to attn_fwd on
+ * the replicated inputs k[cand2user], v[cand2user], kv_len[cand2user].
+ */
+int attn_fwd_bcast(const void* q, const void* k, const void* v, void* o,
+                   const int32_t* cand2user, int B_c, int B_u,
+                   int H, int Hkv, int Lq, int Lk, int d,
+                   int causal, const int32_t* kv_len, float scale,
+                   int dtype, void* stream);
+
+/* Static, human-readable text for a status code (never NULL). */
+const char* attn_strerror(int status);
+
+/* ABI version: major * 100 + minor. */
+int attn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_H_ */

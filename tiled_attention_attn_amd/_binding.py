@@ -1,0 +1,146 @@
+"""ctypes binding of libattn.so with the same entry-point names as include/attn.h.
+
+Argument marshalling only: shapes, dtypes and devices of torch tensors are
+checked and their device pointers handed to the C ABI. Every step of the
+computation runs in the library's HIP kernels; there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libattn.so")
+
+ATTN_OK, ATTN_EINVAL, ATTN_EUNSUPPORTED, ATTN_ELAUNCH = 0, -1, -2, -3
+ATTN_F32, ATTN_BF16 = 0, 1
+
+_lib = None
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"attention library error {status}: {msg}")
+        self.status = status
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libattn.so (once). Raises RuntimeError when it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is missing: build it with `python -m tiled_attention_attn_amd.build` "
+            "(hipcc, gfx950). There is no fallback implementation.")
+    lib = ctypes.CDLL(path)
+    vp, i32, f32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    lib.attn_fwd.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, vp, f32, i32, vp]
+    lib.attn_fwd.restype = i32
+    lib.attn_fwd_bcast.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32,
+                                   vp, f32, i32, vp]
+    lib.attn_fwd_bcast.restype = i32
+    lib.attn_strerror.argtypes = [i32]
+    lib.attn_strerror.restype = ctypes.c_char_p
+    lib.attn_version.argtypes = []
+    lib.attn_version.restype = i32
+    _lib = lib
+    return lib
+
+
+def attn_strerror(status: int) -> str:
+    return load_library().attn_strerror(int(status)).decode()
+
+
+def attn_version() -> int:
+    return int(load_library().attn_version())
+
+
+def _check(status: int):
+    if status != ATTN_OK:
+        raise AttnError(status, attn_strerror(status))
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return ATTN_BF16
+    if t.dtype == torch.float32:
+        return ATTN_F32
+    raise TypeError(f"unsupported dtype {t.dtype}: use bfloat16 or float32")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _prep(q, k, v, o, extra):
+    import torch
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a device tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous [batch, heads, seq, d]")
+        if t.dim() != 4:
+            raise ValueError(f"{name} must be 4-D [batch, heads, seq, d]")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k and v must share one dtype")
+    if k.shape != v.shape:
+        raise ValueError("k and v must have the same shape")
+    if q.shape[3] != k.shape[3]:
+        raise ValueError("q and k must have the same head dimension")
+    if o is None:
+        o = torch.empty_like(q)
+    elif o.shape != q.shape or o.dtype != q.dtype or not o.is_contiguous() or not o.is_cuda:
+        raise ValueError("o must be a contiguous device tensor shaped and typed like q")
+    for name, t in extra.items():
+        if t is not None and (t.dtype != torch.int32 or not t.is_cuda or not t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous int32 device tensor")
+    return o
+
+
+def _stream(stream):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def attn_fwd(q, k, v, o=None, *, causal=False, kv_len=None, scale=0.0, stream=None):
+    """O = softmax(scale * Q K^T + mask) V on the GPU; returns o.
+
+    q [B,H,Lq,d], k/v [B,Hkv,Lk,d] (bf16 or fp32, contiguous, on the device);
+    kv_len: int32 [B] device tensor or None; scale 0 means 1/sqrt(d).
+    Enqueued on `stream` (default: torch's current stream); not synchronised.
+    """
+    lib = load_library()
+    o = _prep(q, k, v, o, {"kv_len": kv_len})
+    B, H, Lq, d = q.shape
+    if k.shape[0] != B:
+        raise ValueError("k/v batch must equal q batch (use attn_fwd_bcast for a broadcast)")
+    if kv_len is not None and kv_len.numel() != B:
+        raise ValueError("kv_len must have one entry per batch element")
+    _check(lib.attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), B, H, k.shape[1], Lq, k.shape[2], d,
+                        int(bool(causal)), _ptr(kv_len), float(scale), _dtype_code(q),
+                        _stream(stream)))
+    return o
+
+
+def attn_fwd_bcast(q, k, v, cand2user, o=None, *, causal=False, kv_len=None, scale=0.0,
+                   stream=None):
+    """In-kernel broadcast attention: candidate c uses user cand2user[c]'s K/V.
+
+    q [B_c,H,Lq,d], k/v [B_u,Hkv,Lk,d], cand2user int32 [B_c] device tensor,
+    kv_len int32 [B_u] device tensor or None. Returns o [B_c,H,Lq,d].
+    """
+    lib = load_library()
+    o = _prep(q, k, v, o, {"cand2user": cand2user, "kv_len": kv_len})
+    B_c, H, Lq, d = q.shape
+    B_u = k.shape[0]
+    if cand2user.numel() != B_c:
+        raise ValueError("cand2user must have one entry per candidate")
+    if kv_len is not None and kv_len.numel() != B_u:
+        raise ValueError("kv_len must have one entry per user")
+    _check(lib.attn_fwd_bcast(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(cand2user), B_c, B_u, H,
+                              k.shape[1], Lq, k.shape[2], d, int(bool(causal)), _ptr(kv_len),
+                              float(scale), _dtype_code(q), _stream(stream)))
+    return o

@@ -1,0 +1,122 @@
+// C ABI front end (include/attn.h): argument checks, work decomposition and
+// launch. Every check runs before the first HIP call, so bad arguments are
+// reported without touching a device.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/attn.h"
+#include "attn_params.h"
+
+namespace attn {
+hipError_t launch_bf16(const Params& p, int D, bool causal, hipStream_t stream);
+hipError_t launch_f32(const Params& p, int D, bool causal, hipStream_t stream);
+int bf16_rows_per_workgroup();
+}  // namespace attn
+
+namespace {
+
+constexpr int kRowsPerWave = 32;
+constexpr int kWavesPerGroup = 4;
+constexpr int kF32Rows = 64;
+
+bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15u) == 0; }
+
+// Shared by both entry points. kv_batches = number of K/V batch entries.
+int check_and_launch(const void* q, const void* k, const void* v, void* o,
+                     const int32_t* cand2user, int NB, int NKV, int H, int Hkv, int Lq, int Lk,
+                     int d, int causal, const int32_t* kv_len, float scale, int dtype,
+                     void* stream) {
+  if (dtype != ATTN_F32 && dtype != ATTN_BF16) return ATTN_EUNSUPPORTED;
+  if (d != 64 && d != 128) return ATTN_EUNSUPPORTED;
+  if (NB < 0 || NKV < 0 || H < 0 || Lq < 0 || Lk < 0 || Hkv < 1) return ATTN_EINVAL;
+  if (H % Hkv != 0) return ATTN_EINVAL;
+  if (!isfinite(scale) || scale < 0.f) return ATTN_EINVAL;
+  if ((int64_t)NB * H * Lq == 0) return ATTN_OK;  // nothing to compute
+  if (q == nullptr || o == nullptr) return ATTN_EINVAL;
+  if (Lk > 0 && (k == nullptr || v == nullptr || NKV < 1)) return ATTN_EINVAL;
+  if (!aligned16(q) || !aligned16(o) || !aligned16(k) || !aligned16(v)) return ATTN_EINVAL;
+  // Element counts must stay addressable; grid size must fit an int.
+  const int64_t q_elems = (int64_t)NB * H * Lq * d;
+  const int64_t kv_elems = (int64_t)NKV * Hkv * Lk * d;
+  if (q_elems > ((int64_t)1 << 46) || kv_elems > ((int64_t)1 << 46)) return ATTN_EINVAL;
+
+  attn::Params p{};
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.kv_len = kv_len;
+  p.cand2user = cand2user;
+  p.NB = NB;
+  p.NKV = NKV;
+  p.H = H;
+  p.Hkv = Hkv;
+  p.Lq = Lq;
+  p.Lk = Lk;
+  const float sc = (scale == 0.f) ? 1.0f / sqrtf((float)d) : scale;
+  p.c = sc * 1.4426950408889634f;  // log2(e): the kernels use exp2
+
+  const bool is_causal = causal != 0;
+  hipError_t err;
+  if (dtype == ATTN_BF16) {
+    const int64_t nrb = ((int64_t)Lq + kRowsPerWave - 1) / kRowsPerWave;
+    if (nrb >= kWavesPerGroup) {
+      p.P = (int)(((nrb + kWavesPerGroup - 1) / kWavesPerGroup) * kWavesPerGroup);
+      p.G = 1;
+      p.nMT = p.P / kWavesPerGroup;
+      p.NG = NB;
+    } else {
+      p.P = (nrb == 3) ? 4 : (int)nrb;  // 1, 2 or 4 blocks: whole entries per workgroup
+      p.G = kWavesPerGroup / p.P;
+      p.nMT = 1;
+      p.NG = (NB + p.G - 1) / p.G;
+    }
+    const int64_t T = (int64_t)p.NG * H * p.nMT;
+    if (T > 0x7fffffff) return ATTN_EINVAL;
+    p.T = (int)T;
+    p.chunk = 16;
+    err = attn::launch_bf16(p, d, is_causal, (hipStream_t)stream);
+  } else {
+    const int64_t T = (int64_t)NB * H * ((Lq + kF32Rows - 1) / kF32Rows);
+    if (T > 0x7fffffff) return ATTN_EINVAL;
+    p.T = (int)T;
+    err = attn::launch_f32(p, d, is_causal, (hipStream_t)stream);
+  }
+  return err == hipSuccess ? ATTN_OK : ATTN_ELAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_fwd(const void* q, const void* k, const void* v, void* o, int B, int H, int Hkv, int Lq,
+             int Lk, int d, int causal, const int32_t* kv_len, float scale, int dtype,
+             void* stream) {
+  return check_and_launch(q, k, v, o, nullptr, B, B, H, Hkv, Lq, Lk, d, causal, kv_len, scale,
+                          dtype, stream);
+}
+
+int attn_fwd_bcast(const void* q, const void* k, const void* v, void* o,
+                   const int32_t* cand2user, int B_c, int B_u, int H, int Hkv, int Lq, int Lk,
+                   int d, int causal, const int32_t* kv_len, float scale, int dtype,
+                   void* stream) {
+  if (B_c > 0 && B_u < 1) return ATTN_EINVAL;
+  if (B_c > 0 && H > 0 && Lq > 0 && cand2user == nullptr) return ATTN_EINVAL;
+  return check_and_launch(q, k, v, o, cand2user, B_c, B_u, H, Hkv, Lq, Lk, d, causal, kv_len,
+                          scale, dtype, stream);
+}
+
+const char* attn_strerror(int status) {
+  switch (status) {
+    case ATTN_OK: return "ok";
+    case ATTN_EINVAL: return "invalid argument";
+    case ATTN_EUNSUPPORTED: return "unsupported head dimension or dtype";
+    case ATTN_ELAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+int attn_version(void) { return 100; }
+
+}  // extern "C"

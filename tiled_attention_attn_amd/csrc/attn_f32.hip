@@ -1,0 +1,113 @@
+// fp32 tiled attention forward (fp32 in, fp32 out, fp32 arithmetic).
+//
+// Same operation and online softmax as the bf16 kernel (tutorial page "Guide
+// de programmation pour la programmation GPU par tuiles de NVIDIA : de cuTile
+// et des noyaux Triton a Flash Attention", flash-attention paragraph), kept in
+// fp32 end to end so the result stays within 1e-4 of the exact value. This
+// path serves small fp32 problems: one thread per query row, K/V tiles of 32
+// keys staged in LDS and read as broadcasts, VALU FMAs for both products.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "attn_params.h"
+
+namespace attn {
+
+constexpr int kF32Rows = 64;  // query rows per workgroup (one wave)
+constexpr int kF32Keys = 32;  // keys per LDS tile
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kF32Rows) void attn_fwd_f32_kernel(const Params p) {
+  __shared__ float ks[kF32Keys][D];
+  __shared__ float vs[kF32Keys][D];
+  const int tid = threadIdx.x;
+  const int nrb = (p.Lq + kF32Rows - 1) / kF32Rows;
+  const int mt = blockIdx.x % nrb;
+  const int bh = blockIdx.x / nrb;
+  const int h = bh % p.H;
+  const int b = bh / p.H;
+  const int g = h / (p.H / p.Hkv);
+  const int row = mt * kF32Rows + tid;
+  const bool row_ok = row < p.Lq;
+
+  const float* __restrict__ qg = (const float*)p.q;
+  float* __restrict__ og = (float*)p.o;
+  const size_t qoff = (((size_t)b * p.H + h) * p.Lq + (row_ok ? row : 0)) * D;
+
+  int kvb = b;
+  if (p.cand2user != nullptr) {
+    kvb = p.cand2user[b];
+    if (kvb < 0 || kvb >= p.NKV) {  // out-of-range user: NaN rows
+      if (row_ok)
+        for (int d = 0; d < D; ++d) og[qoff + d] = __builtin_nanf("");
+      return;
+    }
+  }
+  int nvalid = p.Lk;
+  if (p.kv_len != nullptr) nvalid = min(max(p.kv_len[kvb], 0), p.Lk);
+  int nkeys = nvalid;
+  if (CAUSAL) nkeys = min(nkeys, min(mt * kF32Rows + kF32Rows, p.Lq));
+  const int ntiles = (nkeys + kF32Keys - 1) / kF32Keys;
+
+  float q[D], o[D];
+  for (int d = 0; d < D; ++d) {
+    q[d] = row_ok ? qg[qoff + d] : 0.f;
+    o[d] = 0.f;
+  }
+  const float* __restrict__ kg = (const float*)p.k + ((size_t)kvb * p.Hkv + g) * p.Lk * D;
+  const float* __restrict__ vg = (const float*)p.v + ((size_t)kvb * p.Hkv + g) * p.Lk * D;
+  float m_run = -INFINITY, l_run = 0.f;
+  const float c = p.c;
+
+  for (int t = 0; t < ntiles; ++t) {
+    __syncthreads();
+    for (int e = tid; e < kF32Keys * D; e += kF32Rows) {
+      const int j = e / D, d = e % D;
+      const int key = t * kF32Keys + j;
+      ks[j][d] = key < p.Lk ? kg[(size_t)key * D + d] : 0.f;
+      vs[j][d] = key < p.Lk ? vg[(size_t)key * D + d] : 0.f;
+    }
+    __syncthreads();
+    float s[kF32Keys];
+    float mx = -INFINITY;
+    for (int j = 0; j < kF32Keys; ++j) {
+      float acc = 0.f;
+      for (int d = 0; d < D; ++d) acc = __builtin_fmaf(q[d], ks[j][d], acc);
+      const int key = t * kF32Keys + j;
+      bool dead = key >= nvalid;
+      if (CAUSAL) dead = dead || key > row;
+      s[j] = dead ? -INFINITY : acc * c;  // base-2 logits
+      mx = fmaxf(mx, s[j]);
+    }
+    const float m_new = fmaxf(m_run, mx);
+    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+    const float alpha = exp2f(m_run - m_use);
+    m_run = m_new;
+    l_run *= alpha;
+    for (int d = 0; d < D; ++d) o[d] *= alpha;
+    for (int j = 0; j < kF32Keys; ++j) {
+      const float pj = exp2f(s[j] - m_use);
+      l_run += pj;
+      for (int d = 0; d < D; ++d) o[d] = __builtin_fmaf(pj, vs[j][d], o[d]);
+    }
+  }
+  if (row_ok) {
+    const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+    for (int d = 0; d < D; ++d) og[qoff + d] = o[d] * inv;
+  }
+}
+
+hipError_t launch_f32(const Params& p, int D, bool causal, hipStream_t stream) {
+  const int nrb = (p.Lq + kF32Rows - 1) / kF32Rows;
+  dim3 grid((unsigned)((size_t)p.NB * p.H * nrb)), block(kF32Rows);
+  if (D == 128) {
+    if (causal) hipLaunchKernelGGL((attn_fwd_f32_kernel<128, true>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((attn_fwd_f32_kernel<128, false>), grid, block, 0, stream, p);
+  } else {
+    if (causal) hipLaunchKernelGGL((attn_fwd_f32_kernel<64, true>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((attn_fwd_f32_kernel<64, false>), grid, block, 0, stream, p);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace attn

@@ -1,0 +1,28 @@
+// Launch parameters shared by the host dispatcher and the attention kernels.
+#pragma once
+#include <stdint.h>
+
+namespace attn {
+
+// One attention problem as the kernels see it. Dense problems have
+// cand2user == nullptr and NKV == NB; the broadcast problem indexes the K/V
+// batch of query batch entry b as cand2user[b].
+struct Params {
+  const void* q;             // [NB, H, Lq, D]
+  const void* k;             // [NKV, Hkv, Lk, D]
+  const void* v;             // [NKV, Hkv, Lk, D]
+  void* o;                   // [NB, H, Lq, D]
+  const int32_t* kv_len;     // [NKV] or nullptr
+  const int32_t* cand2user;  // [NB] or nullptr
+  int NB, NKV, H, Hkv, Lq, Lk;
+  float c;                   // scale * log2(e): softmax runs in base 2
+  // Work decomposition (filled by the host dispatcher).
+  int P;      // 32-row query blocks per (batch entry, head), padded so tiles never straddle
+  int G;      // batch entries packed into one workgroup (P < 4 only)
+  int nMT;    // workgroups per (batch group, head)
+  int NG;     // batch groups = ceil(NB / G)
+  int T;      // total workgroups
+  int chunk;  // logical tiles kept together on one XCD (0 = no remap)
+};
+
+}  // namespace attn
