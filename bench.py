@@ -1,0 +1,272 @@
+"""Benchmark of the fused tiled attention forward on one MI355X.
+
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-variants]
+                [--no-cpu-baseline]
+
+A step is one attention forward (one launch of the library's kernel) over the
+workload's synthetic, seeded inputs, which are resident in HBM before timing
+starts. Prints ONE JSON line. `value` is algorithmic TFLOP/s (4*d FLOPs per
+unmasked query/key pair) of the headline workload; `roofline` relates the
+kernel's average launch time to the bf16 MFMA peak; `cpu_baseline` times the
+float64 oracle on a bounded sample of the same workload on the host cores;
+`variants` holds the other workloads (the broadcast one also in GB/s).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import attn_inputs as ai  # noqa: E402
+
+METRIC = "attention fwd TFLOP/s (bf16) and % of MFMA peak; broadcast-path GB/s"
+HEADLINE = "gqa_causal_L16384"
+PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}   # MI355X dense MFMA / fp32 matrix peaks
+PEAK_HBM_GBS = 8000.0
+KERNEL_SOURCE = os.path.join(ROOT, "tiled_attention_attn_amd", "csrc", "attn_bf16.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def pairs(w: ai.AttnInputs) -> int:
+    """Unmasked (query, key) pairs summed over batch entries and heads."""
+    NB, H, Lq, _ = w.q.shape
+    Lk = w.k.shape[2]
+    kv_b = w.kv_len if w.cand2user is None or w.kv_len is None else w.kv_len[w.cand2user]
+    total = 0
+    for b in range(NB):
+        n = Lk if kv_b is None else int(min(max(kv_b[b], 0), Lk))
+        if w.causal:
+            i = np.arange(Lq)
+            total += int(np.minimum(i + 1, n).sum())
+        else:
+            total += Lq * n
+    return total * H
+
+
+def algorithmic_flops(w) -> int:
+    return 4 * w.q.shape[3] * pairs(w)
+
+
+def algorithmic_bytes(w) -> int:
+    """Read Q, the unique valid K/V rows and the index arrays; write O."""
+    esz = 2 if w.dtype == "bf16" else 4
+    NKV, Hkv, Lk, d = w.k.shape
+    kv_rows = 0
+    for u in range(NKV):
+        kv_rows += Lk if w.kv_len is None else int(min(max(w.kv_len[u], 0), Lk))
+    total = 2 * w.q.size * esz + 2 * kv_rows * Hkv * d * esz
+    for aux in (w.kv_len, w.cand2user):
+        if aux is not None:
+            total += 4 * aux.size
+    return total
+
+
+def kernel_source_hash() -> str:
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def to_device(x: np.ndarray, dtype: str):
+    import torch
+    if dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).cuda()
+
+
+class Runner:
+    def __init__(self, w: ai.AttnInputs):
+        import torch
+        self.w = w
+        self.q, self.k, self.v = (to_device(x, w.dtype) for x in (w.q, w.k, w.v))
+        self.o = torch.empty_like(self.q)
+        self.kv = None if w.kv_len is None else torch.from_numpy(w.kv_len).cuda()
+        self.c2u = None if w.cand2user is None else torch.from_numpy(w.cand2user).cuda()
+        import tiled_attention_attn_amd as taa
+        self.taa = taa
+
+    def __call__(self):
+        if self.c2u is None:
+            self.taa.attn_fwd(self.q, self.k, self.v, self.o, causal=self.w.causal,
+                              kv_len=self.kv)
+        else:
+            self.taa.attn_fwd_bcast(self.q, self.k, self.v, self.c2u, self.o,
+                                    causal=self.w.causal, kv_len=self.kv)
+
+
+def time_steps(fn, steps: int, warmup: int) -> float:
+    """Average milliseconds per step, from HIP events on the launch stream."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(steps):
+        fn()
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps
+
+
+def sampled_error(run: Runner, seed: int = 1, nrows: int = 4) -> float:
+    """Max abs error of a few output rows against the float64 oracle."""
+    import oracle
+    import torch
+    w = run.w
+    rng = np.random.default_rng(seed)
+    NB, H, Lq, _ = w.q.shape
+    worst = 0.0
+    for _ in range(2):
+        b, h = int(rng.integers(NB)), int(rng.integers(H))
+        rows = np.unique(np.concatenate([[0, Lq - 1], rng.integers(0, Lq, nrows)]))
+        got = run.o[b, h, torch.from_numpy(rows).cuda()].double().cpu().numpy()
+        u = b if w.cand2user is None else int(w.cand2user[b])
+        g = h // (H // w.k.shape[1])
+        kvl = None if w.kv_len is None else w.kv_len[u:u + 1]
+        ref = oracle.attention_rows(ai.to_f64(w.q[b:b + 1, h:h + 1], w.dtype),
+                                    ai.to_f64(w.k[u:u + 1, g:g + 1], w.dtype),
+                                    ai.to_f64(w.v[u:u + 1, g:g + 1], w.dtype), 0, 0, rows,
+                                    causal=w.causal, kv_len=kvl)
+        worst = max(worst, float(np.abs(got - ref).max()))
+    return worst
+
+
+def cpu_baseline(w: ai.AttnInputs, budget_s: float = 15.0) -> dict:
+    """Time the float64 oracle, as it stands, on a bounded sample of rows.
+
+    Rows are drawn uniformly over (batch entry, head, query row) so causal and
+    kv_len masking weigh in as in the full workload; the oracle computes each
+    row's full score row (masked keys included), but only unmasked pairs count
+    as algorithmic FLOPs, as on the GPU. Heads are added until the time budget is spent.
+    """
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        cores = os.cpu_count() or 1
+    NB, H, Lq, d = w.q.shape
+    Hkv, Lk = w.k.shape[1], w.k.shape[2]
+    rng = np.random.default_rng(123)
+    heads_done, flops, t_total = 0, 0, 0.0
+    rows_per_head = 256
+    while t_total < budget_s and heads_done < 4096:
+        b, h = int(rng.integers(NB)), int(rng.integers(H))
+        rows = np.sort(rng.choice(Lq, size=min(rows_per_head, Lq), replace=False))
+        u = b if w.cand2user is None else int(w.cand2user[b])
+        g = h // (H // Hkv)
+        qf = ai.to_f64(w.q[b:b + 1, h:h + 1], w.dtype)
+        kf = ai.to_f64(w.k[u:u + 1, g:g + 1], w.dtype)
+        vf = ai.to_f64(w.v[u:u + 1, g:g + 1], w.dtype)
+        kvl = None if w.kv_len is None else w.kv_len[u:u + 1]
+        t0 = time.perf_counter()
+        oracle.attention_rows(qf, kf, vf, 0, 0, rows, causal=w.causal, kv_len=kvl)
+        t_total += time.perf_counter() - t0
+        n = Lk if kvl is None else int(min(max(kvl[0], 0), Lk))
+        valid = np.minimum(rows + 1, n) if w.causal else np.full(len(rows), n)
+        flops += 4 * d * int(valid.sum())
+        heads_done += 1
+    return {"value": flops / t_total / 1e12, "unit": "TFLOP/s", "cores": int(cores),
+            "kind": "oracle",
+            "sample": f"{heads_done} random (batch, head) pairs x {rows_per_head} random query "
+                      f"rows of {w.meta} ({flops:.3e} algorithmic FLOPs in {t_total:.1f} s)"}
+
+
+def traffic_for(workload: str, flops_ms: float):
+    """HBM bytes per launch measured with rocprofv3 counters, if taken on this kernel source."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    with open(TRAFFIC_FILE) as f:
+        rec = json.load(f)
+    ent = rec.get(workload)
+    if not ent or ent.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return ent.get("hbm_bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=HEADLINE, choices=sorted(ai.WORKLOADS))
+    ap.add_argument("--no-variants", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the "
+              "method runs on one GPU's share; see the sharding notes in the design).",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a visible MI355X GPU", file=sys.stderr)
+        sys.exit(1)
+
+    w = ai.make_workload(args.workload, seed=0)
+    run = Runner(w)
+    ms = time_steps(run, args.steps, args.warmup)
+    flops = algorithmic_flops(w)
+    nbytes = algorithmic_bytes(w)
+    tflops = flops / (ms * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[w.dtype]
+    err = sampled_error(run)
+    traffic = traffic_for(args.workload, ms)
+    out = {
+        "metric": METRIC,
+        "value": round(tflops, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded N(0,1), Philox streams)",
+        "config": {"workload": args.workload, **{k: v for k, v in w.meta.items() if k != "kind"},
+                   "causal": w.causal},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 3), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(tflops / peak, 4), "traffic": traffic,
+                     "algorithmic_flops_per_launch": flops,
+                     "algorithmic_bytes_per_launch": nbytes},
+        "max_abs_err_sampled": err,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w)
+    if not args.no_variants:
+        variants = {}
+        for name in sorted(ai.WORKLOADS):
+            if name == args.workload:
+                continue
+            wv = ai.make_workload(name, seed=0)
+            rv = Runner(wv)
+            msv = time_steps(rv, max(5, args.steps // 2), 3)
+            fv, bv = algorithmic_flops(wv), algorithmic_bytes(wv)
+            tv = fv / (msv * 1e-3) / 1e12
+            ent = {"ms_per_step": round(msv, 5), "TFLOP/s": round(tv, 3),
+                   "frac_of_peak": round(tv / PEAK_TFLOPS[wv.dtype], 4), "dtype": wv.dtype,
+                   "GB/s": round(bv / (msv * 1e-3) / 1e9, 1),
+                   "max_abs_err_sampled": sampled_error(rv)}
+            if wv.cand2user is not None:
+                ent["GB/s_frac_of_hbm"] = round(ent["GB/s"] / PEAK_HBM_GBS, 4)
+                rep = 2 * wv.q.size * 2 + 2 * wv.cand2user.size * wv.k[0].size * 2
+                ent["replication_equivalent_GB/s"] = round(rep / (msv * 1e-3) / 1e9, 1)
+            variants[name] = ent
+            del rv
+            torch.cuda.empty_cache()
+        out["variants"] = variants
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()
