@@ -18,8 +18,8 @@
 // that layout and feed the second product directly as the B operand:
 //     O^T[d, query] += V^T . P^T          (v_mfma_f32_32x32x16_bf16)
 // whose accumulator again has one query per lane, so the online-softmax
-// rescale by alpha is lane-local. V^T operands come from row-major V in LDS
-// through the gfx950 transposing LDS read (ds_read_b64_tr_b16).
+// rescale is lane-local. V^T operands come from row-major V in LDS through
+// the gfx950 transposing LDS read (ds_read_b64_tr_b16).
 //
 // MFMA 32x32x16 bf16 lane layout (checked on the device):
 //   A (32 x 16): lane l holds row l%32, k-slots (l/32)*8 .. +7
@@ -28,8 +28,15 @@
 // The k-slot -> key assignment of the PV product is free as long as A and B
 // agree; it is chosen to match the C layout of S^T, so P needs no shuffle:
 //   slot j of half h in PV step t  <->  key 16t + (j/4)*8 + 4h + j%4.
+//
+// Pipeline. K/V tiles move HBM -> LDS with direct-to-LDS loads (no register
+// staging) into two buffers each. Iteration t computes S(t) = K(t) Q^T, then
+// issues O += P(t-1) V(t-1) on the MFMA pipe while the softmax of S(t) runs
+// on the VALU; meanwhile K(t+1) and V(t) stream into the other buffers.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 #include "attn_params.h"
 
@@ -39,9 +46,9 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 #define LDS_AS __attribute__((address_space(3)))
+#define GLOBAL_AS __attribute__((address_space(1)))
 
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
@@ -49,33 +56,28 @@ constexpr int kRowsPerWave = 32;
 
 template <int D>
 struct Tile {
-  static constexpr int BN = (D == 128) ? 64 : 128;  // keys per tile
+  static constexpr int BN = 64;                      // keys per tile
   static constexpr int NC = D / 8;                   // 16-byte chunks per K/V row
   static constexpr int KB = BN / 32;                 // 32-key blocks per tile
   static constexpr int DB = D / 32;                  // 32-wide d blocks of O^T
   static constexpr int QS = D / 16;                  // k-steps of the QK^T product
   static constexpr int PS = BN / 16;                 // k-steps of the PV product
-  static constexpr int CHUNKS = BN * NC;             // 16-byte chunks per K (or V) tile
-  static constexpr int LOADS = CHUNKS / kThreads;    // 16-byte loads per thread per matrix
-  static_assert(CHUNKS % kThreads == 0, "tile must split evenly over the workgroup");
+  // LDS row pitches in 16-byte chunks. K is read 16 bytes per lane with
+  // consecutive lanes on consecutive rows: one pad chunk staggers the rows
+  // by 4 banks. V is read by the transposing load, whose 16-lane groups touch
+  // 4 consecutive rows x 32 bytes: two pad chunks stagger them by 8 banks.
+  // Either way every operand address is a per-lane base plus an immediate.
+  static constexpr int KPITCH = NC + 1;
+  static constexpr int VPITCH = NC + 2;
+  static constexpr int KCHUNKS = BN * KPITCH;
+  static constexpr int VCHUNKS = BN * VPITCH;
+  static constexpr int KLOADS = KCHUNKS / 64;        // wave-wide loads per K tile
+  static constexpr int VLOADS = VCHUNKS / 64;
+  static constexpr int KPER = (KLOADS + kWaves - 1) / kWaves;  // per wave (upper bound)
+  static constexpr int VPER = (VLOADS + kWaves - 1) / kWaves;
+  static_assert(KCHUNKS % 64 == 0 && VCHUNKS % 64 == 0, "tiles fill whole wave loads");
+  static_assert(KPER <= 8 && VPER <= 8, "load offset tables hold 8 entries");
 };
-
-// LDS swizzles (16-byte chunk granularity, bijective within a row).
-// K rows are read 16 bytes per lane with consecutive lanes on consecutive
-// rows: XOR with the row index spreads them over all banks.
-template <int NC>
-__device__ __forceinline__ int k_swz(int row, int c) { return c ^ (row & (NC - 1)); }
-// V rows are read by the transposing load: a 16-lane group touches 4
-// consecutive rows x 32 bytes; XOR of the 32-byte pair index with row%4
-// keeps those 4 pairs in distinct banks.
-__device__ __forceinline__ int v_swz(int row, int c) { return c ^ ((row & 3) << 1); }
-
-__device__ __forceinline__ float wave_max_halves(float x) {
-  return fmaxf(x, __shfl_xor(x, 32, 64));
-}
-__device__ __forceinline__ float wave_sum_halves(float x) {
-  return x + __shfl_xor(x, 32, 64);
-}
 
 // Map the hardware workgroup id to a logical tile so that runs of `chunk`
 // consecutive logical tiles (which share K/V) land on one XCD. Workgroups
@@ -97,19 +99,46 @@ struct WaveTask {
   bool bad;    // kvb out of range: output NaN
 };
 
+// Cross-half exchange: lanes l and l^32 hold the same query, different keys.
+__device__ __forceinline__ float halves_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float halves_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Lazy rescaling: the running max used for the exponent is only moved when
+// some row's max grew by more than 2^kTau (base 2); until then probabilities
+// may exceed 1 by at most that factor, which bf16 and fp32 carry exactly as
+// well. The final division by the row sum uses the same reference, so the
+// result is unchanged up to rounding.
+constexpr float kTau = 8.0f;
+
+// s_waitcnt vmcnt(0): wait for this wave's direct-to-LDS loads.
+__device__ __forceinline__ void wait_vm() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(const Params p) {
   using TL = Tile<D>;
   constexpr int BN = TL::BN, NC = TL::NC, KB = TL::KB, DB = TL::DB, QS = TL::QS, PS = TL::PS;
-  constexpr int LOADS = TL::LOADS;
+  constexpr int KPITCH = TL::KPITCH, VPITCH = TL::VPITCH;
 
-  __shared__ u32x4 smem[2][2][TL::CHUNKS];  // [buffer][K=0, V=1][chunk]
+  // Four distinct LDS objects, so the compiler can tell that the loads in
+  // flight into one buffer never alias reads of another.
+  __shared__ u32x4 kbuf0[TL::KCHUNKS];
+  __shared__ u32x4 kbuf1[TL::KCHUNKS];
+  __shared__ u32x4 vbuf0[TL::VCHUNKS];
+  __shared__ u32x4 vbuf1[TL::VCHUNKS];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int half = lane >> 5;   // which k-slot half of the MFMA operands
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int half = lane >> 5;   // k-slot half of the MFMA operands
   const int col = lane & 31;    // the query this lane owns
+  const int il = lane & 15;     // index inside a 16-lane group (transposing read)
+  const int grp = lane >> 4;    // 16-lane group
 
   // ---- decode the logical tile --------------------------------------------
   const int L = xcd_remap(blockIdx.x, p.T, p.chunk);
@@ -132,7 +161,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(const Params
     int r = L / p.nMT;
     bgrp = r % p.NG;
     r /= p.NG;
-    h = r;  // g * HPG + hq
+    h = r;
     mt = CAUSAL ? (p.nMT - 1 - mtr) : mtr;
   }
   const int g = h / HPG;
@@ -174,6 +203,23 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(const Params
 
   const float c = p.c;
 
+  // Per-lane byte offsets, inside a K/V tile, of the chunks this lane loads:
+  // wave load n writes LDS chunks 64n .. 64n+63 (lane i -> chunk 64n + i);
+  // chunk q of the padded tile is row q / pitch, column q % pitch, and pad
+  // columns re-read column 0 of their row.
+  int koff[8], krow[8], voff[8], vrow[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int qk_ = (wave + j * kWaves) * 64 + lane;
+    const int rk = qk_ / KPITCH, ck = qk_ % KPITCH;
+    krow[j] = rk;
+    koff[j] = rk * (D * 2) + (ck < NC ? ck : 0) * 16;
+    const int qv_ = (wave + j * kWaves) * 64 + lane;
+    const int rv = qv_ / VPITCH, cv = qv_ % VPITCH;
+    vrow[j] = rv;
+    voff[j] = rv * (D * 2) + (cv < NC ? cv : 0) * 16;
+  }
+
   // One pass per distinct K/V batch among the waves (normally exactly one).
   for (int lead = 0; lead < kWaves; ++lead) {
     const WaveTask lt = task_of(lead);
@@ -189,7 +235,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(const Params
     int nvalid = p.Lk;
     if (p.kv_len != nullptr) nvalid = min(max(p.kv_len[kvb], 0), p.Lk);
 
-    // keys needed by a wave: causal rows r allow keys <= r
+    // keys a wave needs (causal rows r allow keys <= r)
     auto keys_needed = [&](const WaveTask& t) -> int {
       int n = nvalid;
       if (CAUSAL) n = min(n, min(t.row0 + kRowsPerWave, p.Lq));
@@ -201,12 +247,51 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(const Params
       if (t.valid && !t.bad && t.kvb == kvb) ntiles = max(ntiles, (keys_needed(t) + BN - 1) / BN);
     }
     const bool active = me.valid && !me.bad && me.kvb == kvb;
-    const int my_keys = active ? keys_needed(me) : 0;
-    const int my_tiles = (my_keys + BN - 1) / BN;
+    if (ntiles == 0) {
+      if (active) {
+        const int row = me.row0 + col;  // no valid key: output rows are 0
+        if (row < p.Lq) {
+          __bf16* orow = og + (q_head + row) * D;
+          for (int d = half * (D / 2); d < (half + 1) * (D / 2); ++d) orow[d] = (__bf16)0.f;
+        }
+      }
+      continue;
+    }
+    const int my_total = active ? (keys_needed(me) + BN - 1) / BN : 0;
+    // tiles whose every key is valid for every row of this wave (no mask needed)
+    int full_keys = nvalid;
+    if (CAUSAL) full_keys = min(full_keys, me.row0 + 1);
+    const int my_full = active ? min(full_keys / BN, my_total) : 0;
 
     const size_t kv_head = ((size_t)kvb * p.Hkv + g) * (size_t)p.Lk;
-    const __bf16* __restrict__ kg = (const __bf16*)p.k + kv_head * D;
-    const __bf16* __restrict__ vg = (const __bf16*)p.v + kv_head * D;
+    const char* __restrict__ kg = (const char*)p.k + kv_head * (D * 2);
+    const char* __restrict__ vg = (const char*)p.v + kv_head * (D * 2);
+
+    // Direct-to-LDS loads of tile t. A tile wholly inside [0, Lk) uses the
+    // precomputed offsets; the last, partial tile re-reads row Lk-1 for rows
+    // past the end (finite data; those keys are masked).
+    auto load_tile = [&](const char* __restrict__ src, u32x4* dst, int t, const int (&off)[8],
+                         const int (&rows)[8], int nloads, int per) {
+      const char* base = src + (size_t)t * BN * (D * 2);
+      const bool whole = (t + 1) * BN <= p.Lk;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        if (j < per) {
+          const int n = wave + j * kWaves;
+          if (n < nloads) {
+            int o = off[j];
+            if (!whole) {
+              const int r = min(t * BN + rows[j], p.Lk - 1) - t * BN;
+              o += (r - rows[j]) * (D * 2);
+            }
+            __builtin_amdgcn_global_load_lds((const void GLOBAL_AS*)(base + o),
+                                             (void LDS_AS*)(dst + n * 64), 16, 0, 0);
+          }
+        }
+      }
+    };
+    auto load_k = [&](u32x4* dst, int t) { load_tile(kg, dst, t, koff, krow, TL::KLOADS, TL::KPER); };
+    auto load_v = [&](u32x4* dst, int t) { load_tile(vg, dst, t, voff, vrow, TL::VLOADS, TL::VPER); };
 
     // Q^T operand: lane holds query row0+col, d = 16*s + 8*half + 0..7.
     bf16x8 qreg[QS];
@@ -227,138 +312,151 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(const Params
     for (int b = 0; b < DB; ++b)
 #pragma unroll
       for (int i = 0; i < 16; ++i) oacc[b][i] = 0.f;
-    float m_run = -INFINITY;  // running max of raw scores (this lane's query)
+    float m_run = -INFINITY;  // reference max (raw scores) of this lane's query
     float l_run = 0.f;        // running sum over this lane's keys only
+    bf16x8 pprev[PS];         // probabilities of the previous tile (PV operand)
 
-    // global -> register staging of one K and one V tile
-    u32x4 kst[LOADS], vst[LOADS];
-    auto load_tile = [&](int t) {
+    // S^T(t) = K(t) . Q^T, with the next step's K operands read ahead.
+    auto qk = [&](f32x16 (&sacc)[KB], const u32x4* kb) {
+      const u32x4* kl = kb + col * KPITCH + half;
+      bf16x8 a[2][KB];
 #pragma unroll
-      for (int n = 0; n < LOADS; ++n) {
-        const int e = tid + n * kThreads;
-        const int row = e / NC, cc = e % NC;
-        const int key = t * BN + row;
-        u32x4 zk = {0u, 0u, 0u, 0u}, zv = {0u, 0u, 0u, 0u};
-        if (key < p.Lk) {
-          zk = *(const u32x4*)(kg + (size_t)key * D + cc * 8);
-          zv = *(const u32x4*)(vg + (size_t)key * D + cc * 8);
-        }
-        kst[n] = zk;
-        vst[n] = zv;
+      for (int kbk = 0; kbk < KB; ++kbk) {
+        a[0][kbk] = __builtin_bit_cast(bf16x8, kl[kbk * 32 * KPITCH]);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sacc[kbk][i] = 0.f;
       }
-    };
-    auto store_tile = [&](int buf) {
-#pragma unroll
-      for (int n = 0; n < LOADS; ++n) {
-        const int e = tid + n * kThreads;
-        const int row = e / NC, cc = e % NC;
-        smem[buf][0][row * NC + k_swz<NC>(row, cc)] = kst[n];
-        smem[buf][1][row * NC + v_swz(row, cc)] = vst[n];
-      }
-    };
-
-    auto compute_tile = [&](int t, int buf) {
-      // ---- S^T = K . Q^T -------------------------------------------------
-      f32x16 sacc[KB];
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) sacc[kb][i] = 0.f;
 #pragma unroll
       for (int s = 0; s < QS; ++s) {
+        if (s + 1 < QS) {
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-          const int row = kb * 32 + col;
-          const int cc = 2 * s + half;
-          const bf16x8 a = __builtin_bit_cast(bf16x8, smem[buf][0][row * NC + k_swz<NC>(row, cc)]);
-          sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[s], sacc[kb], 0, 0, 0);
+          for (int kbk = 0; kbk < KB; ++kbk)
+            a[(s + 1) & 1][kbk] = __builtin_bit_cast(bf16x8, kl[kbk * 32 * KPITCH + 2 * (s + 1)]);
         }
-      }
-      // ---- mask (boundary tiles only) ---------------------------------------
-      const int key0 = t * BN;
-      const int qrow = me.row0 + col;
-      const bool need_mask = (key0 + BN > nvalid) || (CAUSAL && key0 + BN - 1 > me.row0);
-      if (need_mask) {
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
+        for (int kbk = 0; kbk < KB; ++kbk)
+          sacc[kbk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[s & 1][kbk], qreg[s], sacc[kbk], 0, 0, 0);
+      }
+    };
+    // O^T += V^T . P^T; V^T operands through the transposing LDS read:
+    // source role il addresses V[row][dcol .. dcol+3], result lane il then
+    // holds V[key0 + s][dbase + il] for s = 0..3. Next step read ahead.
+    const int vlane = (half * 4 + (il >> 2)) * (VPITCH * 16) + ((grp & 1) * 16 + 4 * (il & 3)) * 2;
+    auto pv = [&](const u32x4* vb32) {
+      const LDS_AS char* vb = (const LDS_AS char*)vb32 + vlane;
+      auto vread = [&](int ps, int b) -> bf16x8 {
+        const int o1 = (ps * 16) * (VPITCH * 16) + b * 64;
+        const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)(vb + o1));
+        const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+            (LDS_AS bf16x4*)(vb + o1 + 8 * (VPITCH * 16)));
+        return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      };
+      bf16x8 a[2];
+      a[0] = vread(0, 0);
+#pragma unroll
+      for (int step = 0; step < PS * DB; ++step) {
+        const int ps = step / DB, b = step % DB;
+        if (step + 1 < PS * DB) a[(step + 1) & 1] = vread((step + 1) / DB, (step + 1) % DB);
+        oacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[step & 1], pprev[ps], oacc[b], 0, 0, 0);
+      }
+    };
+    // Online softmax of tile t (base 2, scale folded into c); produces the
+    // next PV operand and returns the rescale factor of O (1 if unchanged).
+    auto softmax = [&](f32x16 (&sacc)[KB], int t, bool masked, bf16x8 (&pout)[PS]) -> float {
+      if (masked) {
+        const int key0 = t * BN;
+        const int qrow = me.row0 + col;
+#pragma unroll
+        for (int kbk = 0; kbk < KB; ++kbk)
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
-            const int key = key0 + kb * 32 + (i >> 2) * 8 + half * 4 + (i & 3);
+            const int key = key0 + kbk * 32 + (i >> 2) * 8 + half * 4 + (i & 3);
             bool dead = key >= nvalid;
             if (CAUSAL) dead = dead || key > qrow;
-            if (dead) sacc[kb][i] = -INFINITY;
+            if (dead) sacc[kbk][i] = -INFINITY;
           }
       }
-      // ---- online softmax (base 2, scale folded into c) --------------------
       float mx = -INFINITY;
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
+      for (int kbk = 0; kbk < KB; ++kbk)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
-      mx = wave_max_halves(mx);
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kbk][i]);
+      mx = halves_max(mx);
       const float m_new = fmaxf(m_run, mx);
-      const float mc = (m_new == -INFINITY) ? 0.f : m_new * c;
-      const float alpha = __builtin_amdgcn_exp2f(m_run * c - mc);
-      m_run = m_new;
+      const bool grow = (m_new - m_run) * c > kTau;  // false for -inf - -inf (NaN)
+      const bool move = __ballot(grow) != 0;
+      const float m_use = move ? m_new : m_run;
+      const float alpha = (!move || m_use == -INFINITY) ? 1.f
+                                                        : __builtin_amdgcn_exp2f((m_run - m_use) * c);
+      const float mc = (m_use == -INFINITY) ? 0.f : m_use * c;
+      m_run = m_use;
       float rs = 0.f;
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
+      for (int kbk = 0; kbk < KB; ++kbk)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][i], c, -mc));
-          sacc[kb][i] = pv;
-          rs += pv;
+          const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kbk][i], c, -mc));
+          sacc[kbk][i] = e;
+          rs += e;
         }
       l_run = l_run * alpha + rs;
+#pragma unroll
+      for (int ps = 0; ps < PS; ++ps)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) pout[ps][j] = (__bf16)sacc[ps >> 1][(ps & 1) * 8 + j];
+      return alpha;
+    };
+    auto rescale = [&](float alpha) {
       if (__ballot(alpha != 1.f)) {
 #pragma unroll
         for (int b = 0; b < DB; ++b)
 #pragma unroll
           for (int i = 0; i < 16; ++i) oacc[b][i] *= alpha;
       }
-      // ---- O^T += V^T . P^T --------------------------------------------------
-      const int il = lane & 15;
-      const int grp = lane >> 4;  // 16-lane group: d half = grp & 1, k half = grp >> 1
-#pragma unroll
-      for (int ps = 0; ps < PS; ++ps) {
-        bf16x8 pb;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) pb[j] = (__bf16)sacc[ps >> 1][(ps & 1) * 8 + j];
-#pragma unroll
-        for (int b = 0; b < DB; ++b) {
-          // transposing read: source role il addresses V[row][dcol .. dcol+3];
-          // result lane il gets V[key0 + s][dbase + il] for s = 0..3.
-          const int dcol = b * 32 + (grp & 1) * 16 + 4 * (il & 3);
-          const int cc = dcol >> 3, within = (dcol & 7) * 2;
-          const int r1 = ps * 16 + half * 4 + (il >> 2);
-          const int r2 = r1 + 8;
-          const LDS_AS char* vb = (const LDS_AS char*)&smem[buf][1][0];
-          const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-              (LDS_AS bf16x4*)(vb + (r1 * NC + v_swz(r1, cc)) * 16 + within));
-          const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-              (LDS_AS bf16x4*)(vb + (r2 * NC + v_swz(r2, cc)) * 16 + within));
-          const bf16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-          oacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, oacc[b], 0, 0, 0);
-        }
-      }
     };
 
-    if (ntiles > 0) {
-      load_tile(0);
-      store_tile(0);
-      __syncthreads();
-      for (int t = 0; t < ntiles; ++t) {
-        const bool more = t + 1 < ntiles;
-        if (more) load_tile(t + 1);
-        if (t < my_tiles) compute_tile(t, t & 1);
-        if (more) store_tile((t + 1) & 1);
-        __syncthreads();
+    // ---- software-pipelined tile loop ----------------------------------------
+    // Iteration t reads K(t) and V(t-1) while K(t+1) and V(t) stream into the
+    // other buffers; the loop is unrolled by two so every access names one
+    // fixed LDS buffer.
+    f32x16 sacc[KB];
+    auto iteration = [&](auto parity, int t) {
+      constexpr int PAR = decltype(parity)::value;
+      u32x4* kcur = PAR ? kbuf1 : kbuf0;
+      u32x4* knext = PAR ? kbuf0 : kbuf1;
+      u32x4* vprev = PAR ? vbuf0 : vbuf1;
+      u32x4* vcur = PAR ? vbuf1 : vbuf0;
+      if (t + 1 < ntiles) load_k(knext, t + 1);
+      if (t < ntiles) load_v(vcur, t);
+      if (active) {
+        const bool do_pv = t >= 1 && t <= my_total;
+        const bool do_sm = t < my_total;
+        if (do_sm) qk(sacc, kcur);
+        if (do_pv) pv(vprev);
+        if (do_sm) {
+          bf16x8 pnew[PS];
+          const float alpha = softmax(sacc, t, t >= my_full, pnew);
+          rescale(alpha);
+#pragma unroll
+          for (int ps = 0; ps < PS; ++ps) pprev[ps] = pnew[ps];
+        }
       }
+      wait_vm();
+      __syncthreads();
+    };
+    load_k(kbuf0, 0);
+    wait_vm();
+    __syncthreads();
+    int t = 0;
+    for (; t + 1 <= ntiles; t += 2) {
+      iteration(std::integral_constant<int, 0>{}, t);
+      iteration(std::integral_constant<int, 1>{}, t + 1);
     }
+    if (t <= ntiles) iteration(std::integral_constant<int, 0>{}, t);
 
     // ---- epilogue: O = O^T / l, round to bf16, store ---------------------------
     if (active) {
-      const float l = wave_sum_halves(l_run);
+      const float l = halves_sum(l_run);
       const float inv = (l > 0.f) ? 1.f / l : 0.f;
       const int row = me.row0 + col;
       if (row < p.Lq) {
