@@ -1,0 +1,104 @@
+"""The C ABI on the CPU: the library loads, exports every declared entry point,
+and rejects bad arguments before making any HIP call (no GPU needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import tiled_attention_attn_amd as taa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(attn_\w+)\s*\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(taa.LIB_PATH):   # build only when nothing is built yet
+        from tiled_attention_attn_amd.build import build
+        build()
+    return taa.load_library()
+
+
+def test_header_declares_the_entry_points():
+    assert declared_functions() == ["attn_fwd", "attn_fwd_bcast", "attn_strerror", "attn_version"]
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    assert lib.attn_version() == 100
+
+
+def test_strerror_covers_every_status(lib):
+    for code in (0, -1, -2, -3):
+        assert taa.attn_strerror(code) not in ("", "unknown status")
+    assert taa.attn_strerror(12345) == "unknown status"
+
+
+# A fake, 16-byte aligned, never-dereferenced device address: every case below
+# must be rejected (or be an empty no-op) before the library touches it.
+FAKE = ctypes.c_void_p(0x1000)
+MISALIGNED = ctypes.c_void_p(0x1008)
+
+
+def fwd(lib, q=FAKE, k=FAKE, v=FAKE, o=FAKE, B=1, H=2, Hkv=1, Lq=16, Lk=16, d=64, causal=0,
+        kv_len=None, scale=0.0, dtype=taa.ATTN_BF16):
+    return lib.attn_fwd(q, k, v, o, B, H, Hkv, Lq, Lk, d, causal, kv_len, scale, dtype, None)
+
+
+def bcast(lib, c2u=FAKE, B_c=4, B_u=2, H=2, Hkv=2, Lq=16, Lk=16, d=128, scale=0.0,
+          dtype=taa.ATTN_BF16):
+    return lib.attn_fwd_bcast(FAKE, FAKE, FAKE, FAKE, c2u, B_c, B_u, H, Hkv, Lq, Lk, d, 0, None,
+                              scale, dtype, None)
+
+
+@pytest.mark.parametrize("kwargs,status", [
+    (dict(d=96), taa.ATTN_EUNSUPPORTED),
+    (dict(d=256), taa.ATTN_EUNSUPPORTED),
+    (dict(dtype=7), taa.ATTN_EUNSUPPORTED),
+    (dict(H=3, Hkv=2), taa.ATTN_EINVAL),
+    (dict(Hkv=0), taa.ATTN_EINVAL),
+    (dict(B=-1), taa.ATTN_EINVAL),
+    (dict(Lq=-5), taa.ATTN_EINVAL),
+    (dict(Lk=-1), taa.ATTN_EINVAL),
+    (dict(scale=-1.0), taa.ATTN_EINVAL),
+    (dict(scale=float("inf")), taa.ATTN_EINVAL),
+    (dict(scale=float("nan")), taa.ATTN_EINVAL),
+    (dict(q=None), taa.ATTN_EINVAL),
+    (dict(o=None), taa.ATTN_EINVAL),
+    (dict(k=None), taa.ATTN_EINVAL),
+    (dict(q=MISALIGNED), taa.ATTN_EINVAL),
+    (dict(v=MISALIGNED), taa.ATTN_EINVAL),
+    (dict(B=1 << 20, H=1 << 10, Lq=1 << 20, d=128), taa.ATTN_EINVAL),   # size overflow
+    (dict(B=0), taa.ATTN_OK),             # empty problems launch nothing
+    (dict(Lq=0), taa.ATTN_OK),
+    (dict(H=0), taa.ATTN_OK),
+    (dict(B=0, q=None, o=None), taa.ATTN_OK),
+])
+def test_attn_fwd_argument_checks(lib, kwargs, status):
+    assert fwd(lib, **kwargs) == status
+
+
+@pytest.mark.parametrize("kwargs,status", [
+    (dict(B_u=0), taa.ATTN_EINVAL),
+    (dict(c2u=None), taa.ATTN_EINVAL),
+    (dict(d=32), taa.ATTN_EUNSUPPORTED),
+    (dict(H=4, Hkv=3), taa.ATTN_EINVAL),
+    (dict(B_c=0, c2u=None), taa.ATTN_OK),
+])
+def test_attn_fwd_bcast_argument_checks(lib, kwargs, status):
+    assert bcast(lib, **kwargs) == status
+
+
+def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
+    import tiled_attention_attn_amd._binding as b
+    monkeypatch.setattr(b, "_lib", None)
+    with pytest.raises(RuntimeError, match="no fallback"):
+        b.load_library(str(tmp_path / "missing.so"))
