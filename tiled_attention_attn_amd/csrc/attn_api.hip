@@ -11,13 +11,11 @@
 namespace attn {
 hipError_t launch_bf16(const Params& p, int D, bool causal, hipStream_t stream);
 hipError_t launch_f32(const Params& p, int D, bool causal, hipStream_t stream);
-int bf16_rows_per_workgroup();
+bool plan_bf16(Params& p);
 }  // namespace attn
 
 namespace {
 
-constexpr int kRowsPerWave = 32;
-constexpr int kWavesPerGroup = 4;
 constexpr int kF32Rows = 64;
 
 bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15u) == 0; }
@@ -60,22 +58,7 @@ int check_and_launch(const void* q, const void* k, const void* v, void* o,
   const bool is_causal = causal != 0;
   hipError_t err;
   if (dtype == ATTN_BF16) {
-    const int64_t nrb = ((int64_t)Lq + kRowsPerWave - 1) / kRowsPerWave;
-    if (nrb >= kWavesPerGroup) {
-      p.P = (int)(((nrb + kWavesPerGroup - 1) / kWavesPerGroup) * kWavesPerGroup);
-      p.G = 1;
-      p.nMT = p.P / kWavesPerGroup;
-      p.NG = NB;
-    } else {
-      p.P = (nrb == 3) ? 4 : (int)nrb;  // 1, 2 or 4 blocks: whole entries per workgroup
-      p.G = kWavesPerGroup / p.P;
-      p.nMT = 1;
-      p.NG = (NB + p.G - 1) / p.G;
-    }
-    const int64_t T = (int64_t)p.NG * H * p.nMT;
-    if (T > 0x7fffffff) return ATTN_EINVAL;
-    p.T = (int)T;
-    p.chunk = 16;
+    if (!attn::plan_bf16(p)) return ATTN_EINVAL;
     err = attn::launch_bf16(p, d, is_causal, (hipStream_t)stream);
   } else {
     const int64_t T = (int64_t)NB * H * ((Lq + kF32Rows - 1) / kF32Rows);

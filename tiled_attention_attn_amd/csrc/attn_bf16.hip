@@ -9,8 +9,10 @@
 // broadcast optimisation for RecSys"): K/V reads are shared by candidates of
 // the same user and indexed in-kernel instead of being replicated.
 //
-// Work decomposition. A workgroup is 4 waves; each wave owns 32 query rows of
-// one (batch entry, head). The wave computes the transposed score tile
+// Work decomposition. A workgroup is 4 waves, one per SIMD; each wave owns 64
+// query rows of one (batch entry, head) as two 32-query blocks, so every K or
+// V operand read from LDS feeds two MFMAs. For each block the wave computes
+// the transposed score tile
 //     S^T[key, query] = K_tile . Q^T      (v_mfma_f32_32x32x16_bf16)
 // so that in the MFMA accumulator layout each lane holds ONE query (column
 // lane%32) and 16 keys per 32-key block: the row max and row sum are in-lane
@@ -30,9 +32,10 @@
 //   slot j of half h in PV step t  <->  key 16t + (j/4)*8 + 4h + j%4.
 //
 // Pipeline. K/V tiles move HBM -> LDS with direct-to-LDS loads (no register
-// staging) into two buffers each. Iteration t computes S(t) = K(t) Q^T, then
-// issues O += P(t-1) V(t-1) on the MFMA pipe while the softmax of S(t) runs
-// on the VALU; meanwhile K(t+1) and V(t) stream into the other buffers.
+// staging) into two buffers each. Iteration t computes S(t) = K(t) Q^T for
+// both blocks, then issues O += P(t-1) V(t-1) on the MFMA pipe while the
+// softmax of S(t) runs on the VALU; meanwhile K(t+1) and V(t) stream into the
+// other buffers.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -52,30 +55,35 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
-constexpr int kRowsPerWave = 32;
+constexpr int kQB = 1;                        // 32-query blocks per wave
+constexpr int kRowsPerWave = 32 * kQB;        // query rows per wave
+constexpr int kWavesPerSimd = kQB == 1 ? 2 : 1;  // occupancy the register budget allows
 
 template <int D>
 struct Tile {
-  static constexpr int BN = 64;                      // keys per tile
+  static constexpr int BN = (D == 128 && kQB > 1) ? 32 : 64;  // keys per tile
   static constexpr int NC = D / 8;                   // 16-byte chunks per K/V row
   static constexpr int KB = BN / 32;                 // 32-key blocks per tile
   static constexpr int DB = D / 32;                  // 32-wide d blocks of O^T
   static constexpr int QS = D / 16;                  // k-steps of the QK^T product
   static constexpr int PS = BN / 16;                 // k-steps of the PV product
-  // LDS row pitches in 16-byte chunks. K is read 16 bytes per lane with
-  // consecutive lanes on consecutive rows: one pad chunk staggers the rows
-  // by 4 banks. V is read by the transposing load, whose 16-lane groups touch
-  // 4 consecutive rows x 32 bytes: two pad chunks stagger them by 8 banks.
-  // Either way every operand address is a per-lane base plus an immediate.
+  // LDS row pitches in 16-byte chunks (LDS: 64 banks x 4 bytes). K is read
+  // 16 bytes per lane with consecutive lanes on consecutive rows: one pad
+  // chunk staggers the rows by 4 banks, so 16 lanes cover all 64 banks. V is
+  // read by the transposing load, where a half-wave touches 4 consecutive
+  // rows x 64 bytes: four pad chunks put those rows 64 bytes apart modulo
+  // 256. Either way every operand address is a per-lane base plus an
+  // immediate.
   static constexpr int KPITCH = NC + 1;
-  static constexpr int VPITCH = NC + 2;
-  static constexpr int KCHUNKS = BN * KPITCH;
-  static constexpr int VCHUNKS = BN * VPITCH;
+  static constexpr int VPITCH = NC + 4;
+  // Buffers are whole wave loads (64 chunks); chunks past the last row land
+  // in the allocation's tail and are never read.
+  static constexpr int KCHUNKS = (BN * KPITCH + 63) / 64 * 64;
+  static constexpr int VCHUNKS = (BN * VPITCH + 63) / 64 * 64;
   static constexpr int KLOADS = KCHUNKS / 64;        // wave-wide loads per K tile
   static constexpr int VLOADS = VCHUNKS / 64;
   static constexpr int KPER = (KLOADS + kWaves - 1) / kWaves;  // per wave (upper bound)
   static constexpr int VPER = (VLOADS + kWaves - 1) / kWaves;
-  static_assert(KCHUNKS % 64 == 0 && VCHUNKS % 64 == 0, "tiles fill whole wave loads");
   static_assert(KPER <= 8 && VPER <= 8, "load offset tables hold 8 entries");
 };
 
@@ -116,11 +124,16 @@ __device__ __forceinline__ float halves_sum(float x) {
 // result is unchanged up to rounding.
 constexpr float kTau = 8.0f;
 
+// Word 3 of a raw buffer descriptor (gfx9 family): 32-bit data format, no
+// swizzle; with stride 0 an access is in range iff offset < num_records, and
+// out-of-range loads return zero.
+constexpr int kBufferWord3 = 0x00020000;
+
 // s_waitcnt vmcnt(0): wait for this wave's direct-to-LDS loads.
 __device__ __forceinline__ void wait_vm() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(const Params p) {
+__global__ __launch_bounds__(kThreads, kWavesPerSimd) void attn_fwd_bf16_kernel(const Params p) {
   using TL = Tile<D>;
   constexpr int BN = TL::BN, NC = TL::NC, KB = TL::KB, DB = TL::DB, QS = TL::QS, PS = TL::PS;
   constexpr int KPITCH = TL::KPITCH, VPITCH = TL::VPITCH;
@@ -206,18 +219,19 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(const Params
   // Per-lane byte offsets, inside a K/V tile, of the chunks this lane loads:
   // wave load n writes LDS chunks 64n .. 64n+63 (lane i -> chunk 64n + i);
   // chunk q of the padded tile is row q / pitch, column q % pitch, and pad
-  // columns re-read column 0 of their row.
-  int koff[8], krow[8], voff[8], vrow[8];
+  // columns re-read column 0 of their row. Wave w issues loads w, w+4, ...
+  uint32_t koff[TL::KPER], voff[TL::VPER];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int qk_ = (wave + j * kWaves) * 64 + lane;
-    const int rk = qk_ / KPITCH, ck = qk_ % KPITCH;
-    krow[j] = rk;
-    koff[j] = rk * (D * 2) + (ck < NC ? ck : 0) * 16;
-    const int qv_ = (wave + j * kWaves) * 64 + lane;
-    const int rv = qv_ / VPITCH, cv = qv_ % VPITCH;
-    vrow[j] = rv;
-    voff[j] = rv * (D * 2) + (cv < NC ? cv : 0) * 16;
+  for (int j = 0; j < TL::KPER; ++j) {
+    const int q = (wave + j * kWaves) * 64 + lane;
+    const int r = q / KPITCH, cc = q % KPITCH;
+    koff[j] = (uint32_t)(r * (D * 2) + (cc < NC ? cc : 0) * 16);
+  }
+#pragma unroll
+  for (int j = 0; j < TL::VPER; ++j) {
+    const int q = (wave + j * kWaves) * 64 + lane;
+    const int r = q / VPITCH, cc = q % VPITCH;
+    voff[j] = (uint32_t)(r * (D * 2) + (cc < NC ? cc : 0) * 16);
   }
 
   // One pass per distinct K/V batch among the waves (normally exactly one).
@@ -267,64 +281,77 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(const Params
     const char* __restrict__ kg = (const char*)p.k + kv_head * (D * 2);
     const char* __restrict__ vg = (const char*)p.v + kv_head * (D * 2);
 
-    // Direct-to-LDS loads of tile t. A tile wholly inside [0, Lk) uses the
-    // precomputed offsets; the last, partial tile re-reads row Lk-1 for rows
-    // past the end (finite data; those keys are masked).
-    auto load_tile = [&](const char* __restrict__ src, u32x4* dst, int t, const int (&off)[8],
-                         const int (&rows)[8], int nloads, int per) {
-      const char* base = src + (size_t)t * BN * (D * 2);
-      const bool whole = (t + 1) * BN <= p.Lk;
+    // Direct-to-LDS buffer loads of tile t. The buffer descriptor spans this
+    // (batch, head)'s Lk rows, so chunks of rows past the end read as zero
+    // (those keys are masked or never read); the tile offset is a scalar.
+    const uint32_t kv_bytes = (uint32_t)p.Lk * (D * 2);
+    const __amdgpu_buffer_rsrc_t krsrc =
+        __builtin_amdgcn_make_buffer_rsrc((void*)kg, (short)0, (int)kv_bytes, kBufferWord3);
+    const __amdgpu_buffer_rsrc_t vrsrc =
+        __builtin_amdgcn_make_buffer_rsrc((void*)vg, (short)0, (int)kv_bytes, kBufferWord3);
+    auto load_tile = [&](__amdgpu_buffer_rsrc_t rsrc, u32x4* dst, int t, const uint32_t* off,
+                         auto per_c, auto nloads_c) {
+      constexpr int PER = decltype(per_c)::value, NLOADS = decltype(nloads_c)::value;
+      const uint32_t tile_off = (uint32_t)t * (BN * D * 2);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        if (j < per) {
-          const int n = wave + j * kWaves;
-          if (n < nloads) {
-            int o = off[j];
-            if (!whole) {
-              const int r = min(t * BN + rows[j], p.Lk - 1) - t * BN;
-              o += (r - rows[j]) * (D * 2);
-            }
-            __builtin_amdgcn_global_load_lds((const void GLOBAL_AS*)(base + o),
-                                             (void LDS_AS*)(dst + n * 64), 16, 0, 0);
-          }
-        }
+      for (int j = 0; j < PER; ++j) {
+        const int n = wave + j * kWaves;
+        if (j < PER - 1 || n < NLOADS)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (void LDS_AS*)(dst + n * 64), 16, off[j],
+                                                   tile_off, 0, 0);
       }
     };
-    auto load_k = [&](u32x4* dst, int t) { load_tile(kg, dst, t, koff, krow, TL::KLOADS, TL::KPER); };
-    auto load_v = [&](u32x4* dst, int t) { load_tile(vg, dst, t, voff, vrow, TL::VLOADS, TL::VPER); };
+    auto load_k = [&](u32x4* dst, int t) {
+      load_tile(krsrc, dst, t, koff, std::integral_constant<int, TL::KPER>{},
+                std::integral_constant<int, TL::KLOADS>{});
+    };
+    auto load_v = [&](u32x4* dst, int t) {
+      load_tile(vrsrc, dst, t, voff, std::integral_constant<int, TL::VPER>{},
+                std::integral_constant<int, TL::VLOADS>{});
+    };
 
-    // Q^T operand: lane holds query row0+col, d = 16*s + 8*half + 0..7.
-    bf16x8 qreg[QS];
-    {
-      const int row = me.row0 + col;
+    // Q^T operands: block qb, lane holds query row0+32qb+col, d = 16*s + 8*half + 0..7.
+    bf16x8 qreg[kQB][QS];
+#pragma unroll
+    for (int qb = 0; qb < kQB; ++qb) {
+      const int row = me.row0 + 32 * qb + col;
       const bool ok = active && row < p.Lq;
       const __bf16* qrow = qg + (q_head + (ok ? row : 0)) * D;
 #pragma unroll
       for (int s = 0; s < QS; ++s) {
         u32x4 x = {0u, 0u, 0u, 0u};
         if (ok) x = *(const u32x4*)(qrow + 16 * s + 8 * half);
-        qreg[s] = __builtin_bit_cast(bf16x8, x);
+        qreg[qb][s] = __builtin_bit_cast(bf16x8, x);
       }
     }
 
-    f32x16 oacc[DB];
+    f32x16 oacc[kQB][DB];
 #pragma unroll
-    for (int b = 0; b < DB; ++b)
+    for (int qb = 0; qb < kQB; ++qb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) oacc[b][i] = 0.f;
-    float m_run = -INFINITY;  // reference max (raw scores) of this lane's query
-    float l_run = 0.f;        // running sum over this lane's keys only
-    bf16x8 pprev[PS];         // probabilities of the previous tile (PV operand)
+      for (int b = 0; b < DB; ++b)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[qb][b][i] = 0.f;
+    float m_run[kQB], l_run[kQB];   // reference max (raw scores) and this lane's partial sum
+#pragma unroll
+    for (int qb = 0; qb < kQB; ++qb) {
+      m_run[qb] = -INFINITY;
+      l_run[qb] = 0.f;
+    }
+    bf16x8 pprev[kQB][PS];          // probabilities of the previous tile (PV operand)
 
-    // S^T(t) = K(t) . Q^T, with the next step's K operands read ahead.
-    auto qk = [&](f32x16 (&sacc)[KB], const u32x4* kb) {
+    // S^T(t) = K(t) . Q^T for both blocks; each K operand feeds two MFMAs and
+    // the next step's operands are read ahead.
+    auto qk = [&](f32x16 (&sacc)[kQB][KB], const u32x4* kb) {
       const u32x4* kl = kb + col * KPITCH + half;
       bf16x8 a[2][KB];
 #pragma unroll
       for (int kbk = 0; kbk < KB; ++kbk) {
         a[0][kbk] = __builtin_bit_cast(bf16x8, kl[kbk * 32 * KPITCH]);
 #pragma unroll
-        for (int i = 0; i < 16; ++i) sacc[kbk][i] = 0.f;
+        for (int qb = 0; qb < kQB; ++qb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) sacc[qb][kbk][i] = 0.f;
       }
 #pragma unroll
       for (int s = 0; s < QS; ++s) {
@@ -335,7 +362,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(const Params
         }
 #pragma unroll
         for (int kbk = 0; kbk < KB; ++kbk)
-          sacc[kbk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[s & 1][kbk], qreg[s], sacc[kbk], 0, 0, 0);
+#pragma unroll
+          for (int qb = 0; qb < kQB; ++qb)
+            sacc[qb][kbk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[s & 1][kbk], qreg[qb][s],
+                                                                    sacc[qb][kbk], 0, 0, 0);
       }
     };
     // O^T += V^T . P^T; V^T operands through the transposing LDS read:
@@ -357,15 +387,18 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(const Params
       for (int step = 0; step < PS * DB; ++step) {
         const int ps = step / DB, b = step % DB;
         if (step + 1 < PS * DB) a[(step + 1) & 1] = vread((step + 1) / DB, (step + 1) % DB);
-        oacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[step & 1], pprev[ps], oacc[b], 0, 0, 0);
+#pragma unroll
+        for (int qb = 0; qb < kQB; ++qb)
+          oacc[qb][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[step & 1], pprev[qb][ps],
+                                                                oacc[qb][b], 0, 0, 0);
       }
     };
-    // Online softmax of tile t (base 2, scale folded into c); produces the
-    // next PV operand and returns the rescale factor of O (1 if unchanged).
-    auto softmax = [&](f32x16 (&sacc)[KB], int t, bool masked, bf16x8 (&pout)[PS]) -> float {
+    // Online softmax of block qb for tile t (base 2, scale folded into c);
+    // produces the next PV operand and returns the rescale factor of O.
+    auto softmax = [&](f32x16 (&sacc)[KB], int qb, int t, bool masked, bf16x8 (&pout)[PS]) -> float {
       if (masked) {
         const int key0 = t * BN;
-        const int qrow = me.row0 + col;
+        const int qrow = me.row0 + 32 * qb + col;
 #pragma unroll
         for (int kbk = 0; kbk < KB; ++kbk)
 #pragma unroll
@@ -382,14 +415,15 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(const Params
 #pragma unroll
         for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kbk][i]);
       mx = halves_max(mx);
-      const float m_new = fmaxf(m_run, mx);
-      const bool grow = (m_new - m_run) * c > kTau;  // false for -inf - -inf (NaN)
+      const float m_old = m_run[qb];
+      const float m_new = fmaxf(m_old, mx);
+      const bool grow = (m_new - m_old) * c > kTau;  // false for -inf - -inf (NaN)
       const bool move = __ballot(grow) != 0;
-      const float m_use = move ? m_new : m_run;
+      const float m_use = move ? m_new : m_old;
       const float alpha = (!move || m_use == -INFINITY) ? 1.f
-                                                        : __builtin_amdgcn_exp2f((m_run - m_use) * c);
+                                                        : __builtin_amdgcn_exp2f((m_old - m_use) * c);
       const float mc = (m_use == -INFINITY) ? 0.f : m_use * c;
-      m_run = m_use;
+      m_run[qb] = m_use;
       float rs = 0.f;
 #pragma unroll
       for (int kbk = 0; kbk < KB; ++kbk)
@@ -399,19 +433,19 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(const Params
           sacc[kbk][i] = e;
           rs += e;
         }
-      l_run = l_run * alpha + rs;
+      l_run[qb] = l_run[qb] * alpha + rs;
 #pragma unroll
       for (int ps = 0; ps < PS; ++ps)
 #pragma unroll
         for (int j = 0; j < 8; ++j) pout[ps][j] = (__bf16)sacc[ps >> 1][(ps & 1) * 8 + j];
       return alpha;
     };
-    auto rescale = [&](float alpha) {
+    auto rescale = [&](int qb, float alpha) {
       if (__ballot(alpha != 1.f)) {
 #pragma unroll
         for (int b = 0; b < DB; ++b)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) oacc[b][i] *= alpha;
+          for (int i = 0; i < 16; ++i) oacc[qb][b][i] *= alpha;
       }
     };
 
@@ -419,7 +453,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(const Params
     // Iteration t reads K(t) and V(t-1) while K(t+1) and V(t) stream into the
     // other buffers; the loop is unrolled by two so every access names one
     // fixed LDS buffer.
-    f32x16 sacc[KB];
+    f32x16 sacc[kQB][KB];
     auto iteration = [&](auto parity, int t) {
       constexpr int PAR = decltype(parity)::value;
       u32x4* kcur = PAR ? kbuf1 : kbuf0;
@@ -434,11 +468,15 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(const Params
         if (do_sm) qk(sacc, kcur);
         if (do_pv) pv(vprev);
         if (do_sm) {
-          bf16x8 pnew[PS];
-          const float alpha = softmax(sacc, t, t >= my_full, pnew);
-          rescale(alpha);
+          const bool masked = t >= my_full;
 #pragma unroll
-          for (int ps = 0; ps < PS; ++ps) pprev[ps] = pnew[ps];
+          for (int qb = 0; qb < kQB; ++qb) {
+            bf16x8 pnew[PS];
+            const float alpha = softmax(sacc[qb], qb, t, masked, pnew);
+            rescale(qb, alpha);
+#pragma unroll
+            for (int ps = 0; ps < PS; ++ps) pprev[qb][ps] = pnew[ps];
+          }
         }
       }
       wait_vm();
@@ -456,20 +494,23 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(const Params
 
     // ---- epilogue: O = O^T / l, round to bf16, store ---------------------------
     if (active) {
-      const float l = halves_sum(l_run);
-      const float inv = (l > 0.f) ? 1.f / l : 0.f;
-      const int row = me.row0 + col;
-      if (row < p.Lq) {
-        __bf16* orow = og + (q_head + row) * D;
 #pragma unroll
-        for (int b = 0; b < DB; ++b)
+      for (int qb = 0; qb < kQB; ++qb) {
+        const float l = halves_sum(l_run[qb]);
+        const float inv = (l > 0.f) ? 1.f / l : 0.f;
+        const int row = me.row0 + 32 * qb + col;
+        if (row < p.Lq) {
+          __bf16* orow = og + (q_head + row) * D;
 #pragma unroll
-          for (int m4 = 0; m4 < 4; ++m4) {
-            bf16x4 w;
+          for (int b = 0; b < DB; ++b)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) w[j] = (__bf16)(oacc[b][m4 * 4 + j] * inv);
-            *(bf16x4*)(orow + b * 32 + m4 * 8 + half * 4) = w;
-          }
+            for (int m4 = 0; m4 < 4; ++m4) {
+              bf16x4 w;
+#pragma unroll
+              for (int j = 0; j < 4; ++j) w[j] = (__bf16)(oacc[qb][b][m4 * 4 + j] * inv);
+              *(bf16x4*)(orow + b * 32 + m4 * 8 + half * 4) = w;
+            }
+        }
       }
     }
   }
@@ -488,6 +529,28 @@ hipError_t launch_bf16(const Params& p, int D, bool causal, hipStream_t stream) 
   return hipGetLastError();
 }
 
-int bf16_rows_per_workgroup() { return kWaves * kRowsPerWave; }
+// Work decomposition for the bf16 kernel: query rows are split into wave
+// blocks of kRowsPerWave; a workgroup takes 4 consecutive blocks of one
+// (batch entry, head), or, for short sequences, whole batch entries of
+// 1, 2 or 4 blocks each (packed so a workgroup never straddles an entry).
+bool plan_bf16(Params& p) {
+  const int64_t nrb = ((int64_t)p.Lq + kRowsPerWave - 1) / kRowsPerWave;
+  if (nrb >= kWaves) {
+    p.P = (int)(((nrb + kWaves - 1) / kWaves) * kWaves);
+    p.G = 1;
+    p.nMT = p.P / kWaves;
+    p.NG = p.NB;
+  } else {
+    p.P = (nrb == 3) ? 4 : (int)nrb;
+    p.G = kWaves / p.P;
+    p.nMT = 1;
+    p.NG = (p.NB + p.G - 1) / p.G;
+  }
+  const int64_t T = (int64_t)p.NG * p.H * p.nMT;
+  if (T > 0x7fffffff) return false;
+  p.T = (int)T;
+  p.chunk = 16;
+  return true;
+}
 
 }  // namespace attn
