@@ -129,6 +129,9 @@ constexpr float kTau = 8.0f;
 // out-of-range loads return zero.
 constexpr int kBufferWord3 = 0x00020000;
 
+// Instruction classes for __builtin_amdgcn_sched_group_barrier.
+constexpr int kSchedMFMA = 0x008, kSchedDSRead = 0x100;
+
 // s_waitcnt vmcnt(0): wait for this wave's direct-to-LDS loads.
 __device__ __forceinline__ void wait_vm() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
@@ -367,6 +370,15 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void attn_fwd_bf16_kernel(
             sacc[qb][kbk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[s & 1][kbk], qreg[qb][s],
                                                                     sacc[qb][kbk], 0, 0, 0);
       }
+      // Keep PF K operand reads in flight ahead of the MFMAs.
+      constexpr int R = QS * KB, PF = R < 4 ? R : 4;
+      __builtin_amdgcn_sched_group_barrier(kSchedDSRead, PF, 0);
+#pragma unroll
+      for (int i = 0; i < R - PF; ++i) {
+        __builtin_amdgcn_sched_group_barrier(kSchedMFMA, kQB, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(kSchedMFMA, kQB * PF, 0);
     };
     // O^T += V^T . P^T; V^T operands through the transposing LDS read:
     // source role il addresses V[row][dcol .. dcol+3], result lane il then
@@ -392,6 +404,15 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void attn_fwd_bf16_kernel(
           oacc[qb][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[step & 1], pprev[qb][ps],
                                                                 oacc[qb][b], 0, 0, 0);
       }
+      // Keep two steps (four transposing reads) in flight ahead of the MFMAs.
+      constexpr int STEPS = PS * DB;
+      __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 4, 0);
+#pragma unroll
+      for (int i = 0; i < STEPS - 2; ++i) {
+        __builtin_amdgcn_sched_group_barrier(kSchedMFMA, kQB, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 2, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 2 * kQB, 0);
     };
     // Online softmax of block qb for tile t (base 2, scale folded into c);
     // produces the next PV operand and returns the rescale factor of O.
