@@ -570,7 +570,10 @@ bool plan_bf16(Params& p) {
   const int64_t T = (int64_t)p.NG * p.H * p.nMT;
   if (T > 0x7fffffff) return false;
   p.T = (int)T;
-  p.chunk = 16;
+  // Keep all tiles that read one K/V head on one XCD (its L2), so each K/V
+  // head streams from memory into a single L2. Broadcast tiles of one head
+  // are ordered by candidate group; runs of 16 groups usually share a user.
+  p.chunk = (p.cand2user == nullptr) ? p.nMT * (p.H / p.Hkv) : 16;
   return true;
 }
 
