@@ -486,8 +486,18 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void attn_fwd_bf16_kernel(
       if (active) {
         const bool do_pv = t >= 1 && t <= my_total;
         const bool do_sm = t < my_total;
-        if (do_sm) qk(sacc, kcur);
-        if (do_pv) pv(vprev);
+        // Raise this wave's issue priority while it feeds the MFMA pipe, so
+        // the other wave on the SIMD fills the gaps with its softmax VALU.
+        if (do_sm) {
+          __builtin_amdgcn_s_setprio(1);
+          qk(sacc, kcur);
+          __builtin_amdgcn_s_setprio(0);
+        }
+        if (do_pv) {
+          __builtin_amdgcn_s_setprio(1);
+          pv(vprev);
+          __builtin_amdgcn_s_setprio(0);
+        }
         if (do_sm) {
           const bool masked = t >= my_full;
 #pragma unroll
