@@ -33,6 +33,11 @@
  * enqueued on `stream` (a hipStream_t; NULL = the default stream) and the
  * call returns without synchronising. o must not alias q, k or v.
  *
+ * Schedules. bf16 problems with d = 128 and Lk >= 8192 run an 8-wave
+ * workgroup schedule, others a 4-wave one; both compute the same result to
+ * within rounding. The environment variable ATTN_BF16_WAVES=4 or 8, read once
+ * per process, forces one of them.
+ *
  * Errors. The return value is an attn_status. All argument checks run before
  * any HIP call. Device-resident values cannot be checked without a sync, so:
  * kv_len values are clamped to [0, Lk]; a cand2user value outside [0, B_u)
@@ -50,7 +55,8 @@ extern "C" {
 typedef enum {
   ATTN_OK = 0,
   ATTN_EINVAL = -1,       /* bad argument: NULL pointer, negative size, H % Hkv != 0,
-                             misaligned pointer, non-finite or negative scale, size overflow */
+                             misaligned pointer, non-finite or negative scale, size overflow,
+                             bf16 with (Lk + 64) * d * 2 > 2^31 - 1 bytes per K/V head */
   ATTN_EUNSUPPORTED = -2, /* head dim d not in {64, 128}, or unknown dtype */
   ATTN_ELAUNCH = -3       /* the HIP launch reported an error */
 } attn_status;

@@ -77,6 +77,7 @@ def bcast(lib, c2u=FAKE, B_c=4, B_u=2, H=2, Hkv=2, Lq=16, Lk=16, d=128, scale=0.
     (dict(q=MISALIGNED), taa.ATTN_EINVAL),
     (dict(v=MISALIGNED), taa.ATTN_EINVAL),
     (dict(B=1 << 20, H=1 << 10, Lq=1 << 20, d=128), taa.ATTN_EINVAL),   # size overflow
+    (dict(Lk=(1 << 23) - 63, d=128), taa.ATTN_EINVAL),   # K/V head beyond 32-bit offsets
     (dict(B=0), taa.ATTN_OK),             # empty problems launch nothing
     (dict(Lq=0), taa.ATTN_OK),
     (dict(H=0), taa.ATTN_OK),

@@ -67,6 +67,12 @@ DENSE_CASES = [
     (3, 2, 2, 1, 50, 64, "bf16", False, None),          # single query row
     (1, 1, 1, 513, 1025, 128, "bf16", False, None),
     (1, 1, 1, 700, 1500, 64, "bf16", True, (1000, 1500)),
+    # d=128 with Lk >= 8192 runs the 8-wave schedule
+    (1, 2, 2, 300, 8200, 128, "bf16", False, None),
+    (1, 4, 2, 257, 8193, 128, "bf16", True, None),
+    (1, 2, 1, 100, 9000, 128, "bf16", False, (5000, 9000)),
+    (1, 1, 1, 8262, 8262, 128, "bf16", True, None),
+    (3, 2, 2, 64, 8250, 128, "bf16", False, None),
 ]
 
 
@@ -133,6 +139,8 @@ BCAST_CASES = [
     (7, 2, 2, 2, 200, 130, 128, "bf16", True, "contiguous"),
     (9, 3, 2, 1, 40, 77, 64, "bf16", False, "shuffled"),
     (6, 2, 2, 2, 50, 60, 64, "f32", False, "shuffled"),
+    (8, 2, 2, 2, 64, 8200, 128, "bf16", False, "shuffled"),   # 8-wave schedule
+    (5, 2, 4, 2, 40, 8300, 128, "bf16", True, "contiguous"),
 ]
 
 
@@ -220,3 +228,32 @@ def test_full_size_workload_sampled(lib, name):
                                     causal=w.causal, kv_len=kvl)
         worst = max(worst, max_err(got, ref))
     assert worst <= TOL[dtype], f"{name}: max abs err {worst}"
+
+
+@pytest.mark.parametrize("d,causal", [(128, True), (128, False), (64, False)])
+def test_both_schedules_agree_with_oracle(lib, d, causal, tmp_path):
+    """Force each wave schedule (child processes with ATTN_BF16_WAVES) on the same inputs."""
+    import subprocess
+    import sys
+    w = ai.make_dense(2, 4, 2, 300, 700, d, causal=causal, seed=21, kv_len_range=(400, 700))
+    ref = ref_dense(w)
+    np.savez(tmp_path / "in.npz", q=w.q, k=w.k, v=w.v, kv_len=w.kv_len)
+    script = (
+        "import sys, numpy as np, torch; sys.path.insert(0, %r); sys.path.insert(0, %r)\n"
+        "import tiled_attention_attn_amd as taa; from gpu_util import to_dev, from_dev, i32_dev\n"
+        "z = np.load(%r)\n"
+        "o = taa.attn_fwd(*(to_dev(z[n], 'bf16') for n in 'qkv'), causal=%r, kv_len=i32_dev(z['kv_len']))\n"
+        "torch.cuda.synchronize(); np.save(%r, from_dev(o))\n"
+    )
+    import os
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    outs = {}
+    for waves in ("4", "8"):
+        out = tmp_path / f"o{waves}.npy"
+        env = dict(os.environ, ATTN_BF16_WAVES=waves)
+        code = script % (root, os.path.join(root, "tests"), str(tmp_path / "in.npz"), causal, str(out))
+        r = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True,
+                           timeout=300)
+        assert r.returncode == 0, r.stderr[-2000:]
+        outs[waves] = np.load(out)
+        assert max_err(outs[waves], ref) <= TOL["bf16"], waves

@@ -9,10 +9,9 @@
 // broadcast optimisation for RecSys"): K/V reads are shared by candidates of
 // the same user and indexed in-kernel instead of being replicated.
 //
-// Work decomposition. A workgroup is 4 waves, one per SIMD; each wave owns 64
-// query rows of one (batch entry, head) as two 32-query blocks, so every K or
-// V operand read from LDS feeds two MFMAs. For each block the wave computes
-// the transposed score tile
+// Work decomposition. A workgroup is 8 waves (two per SIMD); each wave owns
+// 32 query rows of one (batch entry, head). The wave computes the transposed
+// score tile
 //     S^T[key, query] = K_tile . Q^T      (v_mfma_f32_32x32x16_bf16)
 // so that in the MFMA accumulator layout each lane holds ONE query (column
 // lane%32) and 16 keys per 32-key block: the row max and row sum are in-lane
@@ -31,13 +30,16 @@
 // agree; it is chosen to match the C layout of S^T, so P needs no shuffle:
 //   slot j of half h in PV step t  <->  key 16t + (j/4)*8 + 4h + j%4.
 //
-// Pipeline. K/V tiles move HBM -> LDS with direct-to-LDS loads (no register
-// staging) into two buffers each. Iteration t computes S(t) = K(t) Q^T for
-// both blocks, then issues O += P(t-1) V(t-1) on the MFMA pipe while the
-// softmax of S(t) runs on the VALU; meanwhile K(t+1) and V(t) stream into the
-// other buffers.
+// Pipeline. K/V tiles move HBM -> LDS with direct-to-LDS buffer loads (no
+// register staging) into two buffers each, shared by all 8 waves. The waves
+// form two groups (waves 0-3 and 4-7; waves w and w+4 share a SIMD) that
+// ping-pong in half-steps, with a workgroup barrier after every second one:
+// while one group issues its MFMA phase for tile t (S(t) = K(t) Q^T and
+// O += P(t-1) V(t-1)), the other runs the softmax of its previous tile on the
+// VALU, so each SIMD's matrix pipe and vector ALU are busy at the same time.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <stdlib.h>
 
 #include <type_traits>
 
@@ -51,15 +53,12 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 #define LDS_AS __attribute__((address_space(3)))
-#define GLOBAL_AS __attribute__((address_space(1)))
 
-constexpr int kWaves = 4;
-constexpr int kThreads = kWaves * 64;
+constexpr int kGroupWaves = 4;                // waves per ping-pong group (one per SIMD)
 constexpr int kQB = 1;                        // 32-query blocks per wave
 constexpr int kRowsPerWave = 32 * kQB;        // query rows per wave
-constexpr int kWavesPerSimd = kQB == 1 ? 2 : 1;  // occupancy the register budget allows
 
-template <int D>
+template <int D, int W>
 struct Tile {
   static constexpr int BN = (D == 128 && kQB > 1) ? 32 : 64;  // keys per tile
   static constexpr int NC = D / 8;                   // 16-byte chunks per K/V row
@@ -82,8 +81,8 @@ struct Tile {
   static constexpr int VCHUNKS = (BN * VPITCH + 63) / 64 * 64;
   static constexpr int KLOADS = KCHUNKS / 64;        // wave-wide loads per K tile
   static constexpr int VLOADS = VCHUNKS / 64;
-  static constexpr int KPER = (KLOADS + kWaves - 1) / kWaves;  // per wave (upper bound)
-  static constexpr int VPER = (VLOADS + kWaves - 1) / kWaves;
+  static constexpr int KPER = (KLOADS + W - 1) / W;  // loads per wave (upper bound)
+  static constexpr int VPER = (VLOADS + W - 1) / W;
   static_assert(KPER <= 8 && VPER <= 8, "load offset tables hold 8 entries");
 };
 
@@ -107,10 +106,16 @@ struct WaveTask {
   bool bad;    // kvb out of range: output NaN
 };
 
+// Maximum that propagates NaN. fmaxf must quiet signalling NaNs, so on
+// values the compiler cannot prove canonical (MFMA results) every operand
+// costs an extra self-max; this form maps to v_maximum3_f32 directly. A NaN
+// score gives a NaN row either way, through the exponential.
+__device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
 // Cross-half exchange: lanes l and l^32 hold the same query, different keys.
 __device__ __forceinline__ float halves_max(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return vmax(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ __forceinline__ float halves_sum(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -135,9 +140,13 @@ constexpr int kSchedMFMA = 0x008, kSchedDSRead = 0x100;
 // s_waitcnt vmcnt(0): wait for this wave's direct-to-LDS loads.
 __device__ __forceinline__ void wait_vm() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, kWavesPerSimd) void attn_fwd_bf16_kernel(const Params p) {
-  using TL = Tile<D>;
+// W = 4: one 4-wave workgroup per SIMD pair (two workgroups per CU), the
+// software-pipelined loop; W = 8: one 8-wave workgroup per CU, the ping-pong
+// loop (waves w and w+4 on one SIMD).
+template <int D, bool CAUSAL, int W>
+__global__ __launch_bounds__(W * 64, W == 4 ? 2 : 1) void attn_fwd_bf16_kernel(const Params p) {
+  using TL = Tile<D, W>;
+  constexpr int kWaves = W;
   constexpr int BN = TL::BN, NC = TL::NC, KB = TL::KB, DB = TL::DB, QS = TL::QS, PS = TL::PS;
   constexpr int KPITCH = TL::KPITCH, VPITCH = TL::VPITCH;
 
@@ -183,7 +192,7 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void attn_fwd_bf16_kernel(
   const int g = h / HPG;
 
   // Every thread can derive the task of any wave (needed for shared loop bounds).
-  auto task_of = [&](int w) -> WaveTask {
+  auto task_of = [&](int w) __attribute__((always_inline)) -> WaveTask {
     WaveTask t;
     if (p.G == 1) {
       t.batch = bgrp;
@@ -253,7 +262,7 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void attn_fwd_bf16_kernel(
     if (p.kv_len != nullptr) nvalid = min(max(p.kv_len[kvb], 0), p.Lk);
 
     // keys a wave needs (causal rows r allow keys <= r)
-    auto keys_needed = [&](const WaveTask& t) -> int {
+    auto keys_needed = [&](const WaveTask& t) __attribute__((always_inline)) -> int {
       int n = nvalid;
       if (CAUSAL) n = min(n, min(t.row0 + kRowsPerWave, p.Lq));
       return n;
@@ -293,7 +302,7 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void attn_fwd_bf16_kernel(
     const __amdgpu_buffer_rsrc_t vrsrc =
         __builtin_amdgcn_make_buffer_rsrc((void*)vg, (short)0, (int)kv_bytes, kBufferWord3);
     auto load_tile = [&](__amdgpu_buffer_rsrc_t rsrc, u32x4* dst, int t, const uint32_t* off,
-                         auto per_c, auto nloads_c) {
+                         auto per_c, auto nloads_c) __attribute__((always_inline)) {
       constexpr int PER = decltype(per_c)::value, NLOADS = decltype(nloads_c)::value;
       const uint32_t tile_off = (uint32_t)t * (BN * D * 2);
 #pragma unroll
@@ -304,15 +313,14 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void attn_fwd_bf16_kernel(
                                                    tile_off, 0, 0);
       }
     };
-    auto load_k = [&](u32x4* dst, int t) {
+    auto load_k = [&](u32x4* dst, int t) __attribute__((always_inline)) {
       load_tile(krsrc, dst, t, koff, std::integral_constant<int, TL::KPER>{},
                 std::integral_constant<int, TL::KLOADS>{});
     };
-    auto load_v = [&](u32x4* dst, int t) {
+    auto load_v = [&](u32x4* dst, int t) __attribute__((always_inline)) {
       load_tile(vrsrc, dst, t, voff, std::integral_constant<int, TL::VPER>{},
                 std::integral_constant<int, TL::VLOADS>{});
     };
-
     // Q^T operands: block qb, lane holds query row0+32qb+col, d = 16*s + 8*half + 0..7.
     bf16x8 qreg[kQB][QS];
 #pragma unroll
@@ -345,33 +353,33 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void attn_fwd_bf16_kernel(
 
     // S^T(t) = K(t) . Q^T for both blocks; each K operand feeds two MFMAs and
     // the next step's operands are read ahead.
-    auto qk = [&](f32x16 (&sacc)[kQB][KB], const u32x4* kb) {
+    auto qk = [&](f32x16 (&sacc)[kQB][KB], const u32x4* kb) __attribute__((always_inline)) {
       const u32x4* kl = kb + col * KPITCH + half;
-      bf16x8 a[2][KB];
+      // all K operands are named up front; the scheduling groups below decide
+      // how far ahead of its MFMA each read is issued
+      bf16x8 a[QS][KB];
 #pragma unroll
-      for (int kbk = 0; kbk < KB; ++kbk) {
-        a[0][kbk] = __builtin_bit_cast(bf16x8, kl[kbk * 32 * KPITCH]);
+      for (int kbk = 0; kbk < KB; ++kbk)
 #pragma unroll
         for (int qb = 0; qb < kQB; ++qb)
 #pragma unroll
           for (int i = 0; i < 16; ++i) sacc[qb][kbk][i] = 0.f;
-      }
+#pragma unroll
+      for (int s = 0; s < QS; ++s)
+#pragma unroll
+        for (int kbk = 0; kbk < KB; ++kbk)
+          a[s][kbk] = __builtin_bit_cast(bf16x8, kl[kbk * 32 * KPITCH + 2 * s]);
 #pragma unroll
       for (int s = 0; s < QS; ++s) {
-        if (s + 1 < QS) {
-#pragma unroll
-          for (int kbk = 0; kbk < KB; ++kbk)
-            a[(s + 1) & 1][kbk] = __builtin_bit_cast(bf16x8, kl[kbk * 32 * KPITCH + 2 * (s + 1)]);
-        }
 #pragma unroll
         for (int kbk = 0; kbk < KB; ++kbk)
 #pragma unroll
           for (int qb = 0; qb < kQB; ++qb)
-            sacc[qb][kbk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[s & 1][kbk], qreg[qb][s],
+            sacc[qb][kbk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[s][kbk], qreg[qb][s],
                                                                     sacc[qb][kbk], 0, 0, 0);
       }
       // Keep PF K operand reads in flight ahead of the MFMAs.
-      constexpr int R = QS * KB, PF = R < 4 ? R : 4;
+      constexpr int R = QS * KB, PF0 = W == 8 ? 2 : 4, PF = R < PF0 ? R : PF0;
       __builtin_amdgcn_sched_group_barrier(kSchedDSRead, PF, 0);
 #pragma unroll
       for (int i = 0; i < R - PF; ++i) {
@@ -384,7 +392,7 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void attn_fwd_bf16_kernel(
     // source role il addresses V[row][dcol .. dcol+3], result lane il then
     // holds V[key0 + s][dbase + il] for s = 0..3. Next step read ahead.
     const int vlane = (half * 4 + (il >> 2)) * (VPITCH * 16) + ((grp & 1) * 16 + 4 * (il & 3)) * 2;
-    auto pv = [&](const u32x4* vb32) {
+    auto pv = [&](const u32x4* vb32) __attribute__((always_inline)) {
       const LDS_AS char* vb = (const LDS_AS char*)vb32 + vlane;
       auto vread = [&](int ps, int b) -> bf16x8 {
         const int o1 = (ps * 16) * (VPITCH * 16) + b * 64;
@@ -393,30 +401,33 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void attn_fwd_bf16_kernel(
             (LDS_AS bf16x4*)(vb + o1 + 8 * (VPITCH * 16)));
         return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
       };
-      bf16x8 a[2];
-      a[0] = vread(0, 0);
+      constexpr int STEPS = PS * DB;
+      constexpr int AHEAD = 2;                // steps of V reads kept in flight
+      bf16x8 a[AHEAD];
 #pragma unroll
-      for (int step = 0; step < PS * DB; ++step) {
+      for (int i = 0; i < AHEAD - 1; ++i) a[i] = vread(i / DB, i % DB);
+#pragma unroll
+      for (int step = 0; step < STEPS; ++step) {
         const int ps = step / DB, b = step % DB;
-        if (step + 1 < PS * DB) a[(step + 1) & 1] = vread((step + 1) / DB, (step + 1) % DB);
+        const int nxt = step + AHEAD - 1;
+        if (nxt < STEPS) a[nxt % AHEAD] = vread(nxt / DB, nxt % DB);
 #pragma unroll
         for (int qb = 0; qb < kQB; ++qb)
-          oacc[qb][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[step & 1], pprev[qb][ps],
+          oacc[qb][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[step % AHEAD], pprev[qb][ps],
                                                                 oacc[qb][b], 0, 0, 0);
       }
-      // Keep two steps (four transposing reads) in flight ahead of the MFMAs.
-      constexpr int STEPS = PS * DB;
-      __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 4, 0);
+      // Keep AHEAD steps (2 transposing reads each) in flight ahead of the MFMAs.
+      __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 2 * AHEAD, 0);
 #pragma unroll
-      for (int i = 0; i < STEPS - 2; ++i) {
+      for (int i = 0; i < STEPS - AHEAD; ++i) {
         __builtin_amdgcn_sched_group_barrier(kSchedMFMA, kQB, 0);
         __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 2, 0);
       }
-      __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 2 * kQB, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedMFMA, AHEAD * kQB, 0);
     };
     // Online softmax of block qb for tile t (base 2, scale folded into c);
     // produces the next PV operand and returns the rescale factor of O.
-    auto softmax = [&](f32x16 (&sacc)[KB], int qb, int t, bool masked, bf16x8 (&pout)[PS]) -> float {
+    auto softmax = [&](f32x16 (&sacc)[KB], int qb, int t, bool masked, bf16x8 (&pout)[PS]) __attribute__((always_inline)) -> float {
       if (masked) {
         const int key0 = t * BN;
         const int qrow = me.row0 + 32 * qb + col;
@@ -430,14 +441,20 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void attn_fwd_bf16_kernel(
             if (dead) sacc[kbk][i] = -INFINITY;
           }
       }
-      float mx = -INFINITY;
+      // Row max as eight independent max chains (short dependency chains:
+      // one wave per SIMD may run this phase alone), then a tree.
+      float pm[8];
 #pragma unroll
-      for (int kbk = 0; kbk < KB; ++kbk)
+      for (int j = 0; j < 8; ++j) pm[j] = vmax(sacc[0][2 * j], sacc[0][2 * j + 1]);
 #pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kbk][i]);
+      for (int kbk = 1; kbk < KB; ++kbk)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) pm[j] = vmax(pm[j], vmax(sacc[kbk][2 * j], sacc[kbk][2 * j + 1]));
+      float mx = vmax(vmax(vmax(pm[0], pm[1]), vmax(pm[2], pm[3])),
+                      vmax(vmax(pm[4], pm[5]), vmax(pm[6], pm[7])));
       mx = halves_max(mx);
       const float m_old = m_run[qb];
-      const float m_new = fmaxf(m_old, mx);
+      const float m_new = vmax(m_old, mx);
       const bool grow = (m_new - m_old) * c > kTau;  // false for -inf - -inf (NaN)
       const bool move = __ballot(grow) != 0;
       const float m_use = move ? m_new : m_old;
@@ -445,15 +462,16 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void attn_fwd_bf16_kernel(
                                                         : __builtin_amdgcn_exp2f((m_old - m_use) * c);
       const float mc = (m_use == -INFINITY) ? 0.f : m_use * c;
       m_run[qb] = m_use;
-      float rs = 0.f;
+      float ps4[4] = {0.f, 0.f, 0.f, 0.f};   // four independent partial sums
 #pragma unroll
       for (int kbk = 0; kbk < KB; ++kbk)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kbk][i], c, -mc));
           sacc[kbk][i] = e;
-          rs += e;
+          ps4[i & 3] += e;
         }
+      const float rs = (ps4[0] + ps4[1]) + (ps4[2] + ps4[3]);
       l_run[qb] = l_run[qb] * alpha + rs;
 #pragma unroll
       for (int ps = 0; ps < PS; ++ps)
@@ -461,7 +479,7 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void attn_fwd_bf16_kernel(
         for (int j = 0; j < 8; ++j) pout[ps][j] = (__bf16)sacc[ps >> 1][(ps & 1) * 8 + j];
       return alpha;
     };
-    auto rescale = [&](int qb, float alpha) {
+    auto rescale = [&](int qb, float alpha) __attribute__((always_inline)) {
       if (__ballot(alpha != 1.f)) {
 #pragma unroll
         for (int b = 0; b < DB; ++b)
@@ -470,6 +488,85 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void attn_fwd_bf16_kernel(
       }
     };
 
+    if constexpr (W == 8) {
+    // ---- ping-pong tile loop ----------------------------------------------------
+    // Half-step h: group 0 runs its MFMA phase for tile h/2 when h is even and
+    // the softmax of tile h/2 when h is odd; group 1 lags by one half-step.
+    // Each wave issues its share of K(s+1) at the start of half-step 2s and of
+    // V(s) at the start of half-step 2s+1 (spreading the load issue, which
+    // stalls the issuing wave), and waits for both at the end of 2s+1. One
+    // workgroup barrier per tile, after odd half-steps, is enough: every
+    // buffer a load overwrites was last read in half-step 2s-1 or earlier.
+    // Between barriers the two groups keep their phase offset by themselves,
+    // since the MFMA and softmax phases take about as long. The loop is
+    // unrolled by four half-steps so that every access names one fixed LDS
+    // buffer.
+    const int grp_id = wave / kGroupWaves;
+    f32x16 sacc[kQB][KB];
+    auto mfma_phase = [&](int t, const u32x4* kb, const u32x4* vb) __attribute__((always_inline)) {
+      __builtin_amdgcn_s_setprio(1);
+      if (t < my_total) qk(sacc, kb);
+      if (t >= 1 && t <= my_total) pv(vb);
+      __builtin_amdgcn_s_setprio(0);
+    };
+    auto valu_phase = [&](int t) __attribute__((always_inline)) {
+      if (t >= 0 && t < my_total) {
+        const bool masked = t >= my_full;
+#pragma unroll
+        for (int qb = 0; qb < kQB; ++qb) {
+          bf16x8 pnew[PS];
+          const float alpha = softmax(sacc[qb], qb, t, masked, pnew);
+          rescale(qb, alpha);
+#pragma unroll
+          for (int ps = 0; ps < PS; ++ps) pprev[qb][ps] = pnew[ps];
+        }
+      }
+    };
+    const int h_end = 2 * ntiles + 1;  // last half-step (group 1's final PV)
+    // One half-step of group G (compile time): this wave's share of one tile
+    // load, then the group's phase, then (odd half-steps) the wait for the
+    // loads and the workgroup barrier. Both groups run the same sequence of
+    // barriers, each from its own copy of the loop.
+    auto half_step = [&](auto g_c, auto hp, int h) __attribute__((always_inline)) {
+      constexpr int G = decltype(g_c)::value;
+      constexpr int HP = decltype(hp)::value;   // h mod 4
+      constexpr int SP = (HP >> 1) & 1;         // parity of s = h / 2
+      constexpr bool EVEN = (HP & 1) == 0;
+      u32x4* kc = SP ? kbuf1 : kbuf0;           // K(s)
+      u32x4* kn = SP ? kbuf0 : kbuf1;           // K(s+1)
+      u32x4* vp = SP ? vbuf0 : vbuf1;           // V(s-1)
+      u32x4* vc = SP ? vbuf1 : vbuf0;           // V(s)
+      const int s2 = h >> 1;
+      if (EVEN) {
+        if (s2 + 1 < ntiles) load_k(kn, s2 + 1);
+      } else {
+        if (s2 < ntiles) load_v(vc, s2);
+      }
+      if (active) {
+        if (EVEN == (G == 0)) mfma_phase(s2, kc, vp);
+        else valu_phase(G == 0 ? s2 : s2 - 1);
+      }
+      if (!EVEN) {
+        wait_vm();
+        __syncthreads();
+      }
+    };
+    auto run_group = [&](auto g_c) __attribute__((always_inline)) {
+      for (int h = 0; h <= h_end; h += 4) {
+        half_step(g_c, std::integral_constant<int, 0>{}, h);
+        half_step(g_c, std::integral_constant<int, 1>{}, h + 1);
+        if (h + 2 > h_end) break;
+        half_step(g_c, std::integral_constant<int, 2>{}, h + 2);
+        half_step(g_c, std::integral_constant<int, 3>{}, h + 3);
+      }
+    };
+    load_k(kbuf0, 0);
+    wait_vm();
+    __syncthreads();
+    if (grp_id == 0) run_group(std::integral_constant<int, 0>{});
+    else run_group(std::integral_constant<int, 1>{});
+
+    } else {
     // ---- software-pipelined tile loop ----------------------------------------
     // Iteration t reads K(t) and V(t-1) while K(t+1) and V(t) stream into the
     // other buffers; the loop is unrolled by two so every access names one
@@ -523,6 +620,8 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void attn_fwd_bf16_kernel(
     }
     if (t <= ntiles) iteration(std::integral_constant<int, 0>{}, t);
 
+    }
+
     // ---- epilogue: O = O^T / l, round to bf16, store ---------------------------
     if (active) {
 #pragma unroll
@@ -547,33 +646,65 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void attn_fwd_bf16_kernel(
   }
 }
 
-// Host-side launchers (one per template instance).
+// Host-side launcher (one instance per head dim, causal flag and wave count).
 hipError_t launch_bf16(const Params& p, int D, bool causal, hipStream_t stream) {
-  dim3 grid(p.T), block(kThreads);
-  if (D == 128) {
-    if (causal) hipLaunchKernelGGL((attn_fwd_bf16_kernel<128, true>), grid, block, 0, stream, p);
-    else hipLaunchKernelGGL((attn_fwd_bf16_kernel<128, false>), grid, block, 0, stream, p);
+  dim3 grid(p.T), block(p.waves * 64);
+#define ATTN_LAUNCH(DD, CC, WW) \
+  hipLaunchKernelGGL((attn_fwd_bf16_kernel<DD, CC, WW>), grid, block, 0, stream, p)
+  if (p.waves == 8) {
+    if (D == 128) {
+      if (causal) ATTN_LAUNCH(128, true, 8); else ATTN_LAUNCH(128, false, 8);
+    } else {
+      if (causal) ATTN_LAUNCH(64, true, 8); else ATTN_LAUNCH(64, false, 8);
+    }
   } else {
-    if (causal) hipLaunchKernelGGL((attn_fwd_bf16_kernel<64, true>), grid, block, 0, stream, p);
-    else hipLaunchKernelGGL((attn_fwd_bf16_kernel<64, false>), grid, block, 0, stream, p);
+    if (D == 128) {
+      if (causal) ATTN_LAUNCH(128, true, 4); else ATTN_LAUNCH(128, false, 4);
+    } else {
+      if (causal) ATTN_LAUNCH(64, true, 4); else ATTN_LAUNCH(64, false, 4);
+    }
   }
+#undef ATTN_LAUNCH
   return hipGetLastError();
 }
 
+// Long d=128 key sequences run the 8-wave ping-pong schedule; shorter ones
+// (and d=64, whose softmax outweighs its MFMA work) the 4-wave schedule.
+constexpr int kPingPongMinKeys = 8192;
+
 // Work decomposition for the bf16 kernel: query rows are split into wave
-// blocks of kRowsPerWave; a workgroup takes 4 consecutive blocks of one
-// (batch entry, head), or, for short sequences, whole batch entries of
-// 1, 2 or 4 blocks each (packed so a workgroup never straddles an entry).
-bool plan_bf16(Params& p) {
+// blocks of kRowsPerWave; a workgroup takes `waves` consecutive blocks of one
+// (batch entry, head), or, for short sequences, whole batch entries of a
+// power-of-two number of blocks each (so a workgroup never straddles an entry).
+// The environment variable ATTN_BF16_WAVES=4|8 overrides the choice (for
+// tuning and for testing both schedules on the same inputs).
+static int waves_override() {
+  static const int v = [] {
+    const char* e = getenv("ATTN_BF16_WAVES");
+    if (e != nullptr && (e[0] == '4' || e[0] == '8') && e[1] == '\0') return e[0] - '0';
+    return 0;
+  }();
+  return v;
+}
+
+bool plan_bf16(Params& p, int D) {
+  // K/V of one (batch, head) are addressed through 32-bit buffer offsets;
+  // the last tile may run up to 64 rows past Lk.
+  if (((int64_t)p.Lk + 64) * D * 2 > 0x7fffffff) return false;
+  int W = (D == 128 && p.Lk >= kPingPongMinKeys) ? 8 : 4;
+  if (waves_override() != 0) W = waves_override();
+  p.waves = W;
   const int64_t nrb = ((int64_t)p.Lq + kRowsPerWave - 1) / kRowsPerWave;
-  if (nrb >= kWaves) {
-    p.P = (int)(((nrb + kWaves - 1) / kWaves) * kWaves);
+  if (nrb >= W) {
+    p.P = (int)(((nrb + W - 1) / W) * W);
     p.G = 1;
-    p.nMT = p.P / kWaves;
+    p.nMT = p.P / W;
     p.NG = p.NB;
   } else {
-    p.P = (nrb == 3) ? 4 : (int)nrb;
-    p.G = kWaves / p.P;
+    int P = 1;
+    while (P < nrb) P *= 2;   // whole entries per workgroup
+    p.P = P;
+    p.G = W / P;
     p.nMT = 1;
     p.NG = (p.NB + p.G - 1) / p.G;
   }

@@ -23,6 +23,7 @@ struct Params {
   int NG;     // batch groups = ceil(NB / G)
   int T;      // total workgroups
   int chunk;  // logical tiles kept together on one XCD (0 = no remap)
+  int waves;  // waves per workgroup of the bf16 kernel (4 or 8)
 };
 
 }  // namespace attn
