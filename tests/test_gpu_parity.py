@@ -232,7 +232,8 @@ def test_full_size_workload_sampled(lib, name):
 
 @pytest.mark.parametrize("d,causal", [(128, True), (128, False), (64, False)])
 def test_both_schedules_agree_with_oracle(lib, d, causal, tmp_path):
-    """Force each wave schedule (child processes with ATTN_BF16_WAVES) on the same inputs."""
+    """Force each wave schedule (child processes with ATTN_BF16_WAVES) on the same inputs;
+    both match the oracle."""
     import subprocess
     import sys
     w = ai.make_dense(2, 4, 2, 300, 700, d, causal=causal, seed=21, kv_len_range=(400, 700))
@@ -257,3 +258,5 @@ def test_both_schedules_agree_with_oracle(lib, d, causal, tmp_path):
         assert r.returncode == 0, r.stderr[-2000:]
         outs[waves] = np.load(out)
         assert max_err(outs[waves], ref) <= TOL["bf16"], waves
+    # the schedules keep the softmax reference differently: equal up to rounding
+    assert max_err(outs["4"], outs["8"]) <= TOL["bf16"]

@@ -122,12 +122,13 @@ __device__ __forceinline__ float halves_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// Lazy rescaling: the running max used for the exponent is only moved when
-// some row's max grew by more than 2^kTau (base 2); until then probabilities
-// may exceed 1 by at most that factor, which bf16 and fp32 carry exactly as
-// well. The final division by the row sum uses the same reference, so the
-// result is unchanged up to rounding.
+// Lazy rescaling: the reference used for the exponent stays put while every
+// probability it gives is at most 2^kTau (base 2), checked through the tile's
+// row sums; probabilities may then exceed 1 by at most that factor, which
+// bf16 and fp32 carry as well. The final division by the row sum uses the
+// same reference, so the result is unchanged up to rounding.
 constexpr float kTau = 8.0f;
+constexpr float kSumLimit = 256.0f;   // 2^kTau
 
 // Word 3 of a raw buffer descriptor (gfx9 family): 32-bit data format, no
 // swizzle; with stride 0 an access is in range iff offset < num_records, and
@@ -441,8 +442,38 @@ __global__ __launch_bounds__(W * 64, W == 4 ? 2 : 1) void attn_fwd_bf16_kernel(c
             if (dead) sacc[kbk][i] = -INFINITY;
           }
       }
-      // Row max as eight independent max chains (short dependency chains:
-      // one wave per SIMD may run this phase alone), then a tree.
+      // Exponentials against reference mc (base 2), rounded to bf16 as the
+      // next PV operand; returns this lane's partial row sum (fp32).
+      auto exps = [&](float mc) __attribute__((always_inline)) -> float {
+        float ps4[4] = {0.f, 0.f, 0.f, 0.f};   // four independent partial sums
+#pragma unroll
+        for (int ps = 0; ps < PS; ++ps)
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const float e =
+                __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[ps >> 1][(ps & 1) * 8 + j], c, -mc));
+            ps4[j & 3] += e;
+            pout[ps][j] = (__bf16)e;
+          }
+        return (ps4[0] + ps4[1]) + (ps4[2] + ps4[3]);
+      };
+      // Fast path (8-wave schedule, which has the registers to keep the raw
+      // scores beside P): keep the current reference. Every probability is
+      // at most its lane's partial sum, so if no lane's sum exceeds 2^kTau
+      // the tile is done without forming the row max and O needs no rescale.
+      // A -inf reference (first tile of a pass) gives inf or NaN sums and
+      // falls through, as does a row whose scores grew.
+      if constexpr (W == 8) {
+        const float rs = exps(m_run[qb] * c);
+        if (__ballot(!(rs <= kSumLimit)) == 0) {
+          l_run[qb] += rs;
+          return 1.f;
+        }
+      }
+      // Row max (max chains, then one exchange between the lane halves). The
+      // 8-wave schedule gets here only when the fast path failed and moves
+      // the reference to the max; the 4-wave one moves it when some row's max
+      // grew by more than 2^kTau.
       float pm[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) pm[j] = vmax(sacc[0][2 * j], sacc[0][2 * j + 1]);
@@ -455,28 +486,14 @@ __global__ __launch_bounds__(W * 64, W == 4 ? 2 : 1) void attn_fwd_bf16_kernel(c
       mx = halves_max(mx);
       const float m_old = m_run[qb];
       const float m_new = vmax(m_old, mx);
-      const bool grow = (m_new - m_old) * c > kTau;  // false for -inf - -inf (NaN)
-      const bool move = __ballot(grow) != 0;
+      bool move = true;
+      if constexpr (W != 8) move = __ballot((m_new - m_old) * c > kTau) != 0;  // NaN: false
       const float m_use = move ? m_new : m_old;
-      const float alpha = (!move || m_use == -INFINITY) ? 1.f
-                                                        : __builtin_amdgcn_exp2f((m_old - m_use) * c);
-      const float mc = (m_use == -INFINITY) ? 0.f : m_use * c;
+      const float alpha = (m_old == m_use || m_use == -INFINITY)
+                              ? 1.f : __builtin_amdgcn_exp2f((m_old - m_use) * c);
       m_run[qb] = m_use;
-      float ps4[4] = {0.f, 0.f, 0.f, 0.f};   // four independent partial sums
-#pragma unroll
-      for (int kbk = 0; kbk < KB; ++kbk)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kbk][i], c, -mc));
-          sacc[kbk][i] = e;
-          ps4[i & 3] += e;
-        }
-      const float rs = (ps4[0] + ps4[1]) + (ps4[2] + ps4[3]);
+      const float rs = exps(m_use == -INFINITY ? 0.f : m_use * c);
       l_run[qb] = l_run[qb] * alpha + rs;
-#pragma unroll
-      for (int ps = 0; ps < PS; ++ps)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) pout[ps][j] = (__bf16)sacc[ps >> 1][(ps & 1) * 8 + j];
       return alpha;
     };
     auto rescale = [&](int qb, float alpha) __attribute__((always_inline)) {
