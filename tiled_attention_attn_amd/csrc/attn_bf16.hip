@@ -426,6 +426,58 @@ __global__ __launch_bounds__(W * 64, W == 4 ? 2 : 1) void attn_fwd_bf16_kernel(c
       }
       __builtin_amdgcn_sched_group_barrier(kSchedMFMA, AHEAD * kQB, 0);
     };
+    // Both products of one half-step in a single instruction stream: first
+    // O += P(t-1) V(t-1), then S(t) = K(t) Q^T, so P(t-1) is dead before S(t)
+    // is born. Operand reads run two MFMAs ahead through the whole stream
+    // (a V^T operand is two reads, a K operand one), so the matrix pipe does
+    // not wait at the seam between the products.
+    auto pvqk = [&](f32x16 (&sacc)[kQB][KB], const u32x4* kb, const u32x4* vb32)
+                    __attribute__((always_inline)) {
+      static_assert(kQB == 1, "one query block per wave");
+      const u32x4* kl = kb + col * KPITCH + half;
+      const LDS_AS char* vb = (const LDS_AS char*)vb32 + vlane;
+      constexpr int NK = QS * KB, NV = PS * DB;
+      bf16x8 ka[QS][KB], va[NV];
+#pragma unroll
+      for (int step = 0; step < NV; ++step) {
+        const int o1 = ((step / DB) * 16) * (VPITCH * 16) + (step % DB) * 64;
+        const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)(vb + o1));
+        const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+            (LDS_AS bf16x4*)(vb + o1 + 8 * (VPITCH * 16)));
+        va[step] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      }
+#pragma unroll
+      for (int step = 0; step < NV; ++step)
+        oacc[0][step % DB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            va[step], pprev[0][step / DB], oacc[0][step % DB], 0, 0, 0);
+#pragma unroll
+      for (int s = 0; s < QS; ++s)
+#pragma unroll
+        for (int kbk = 0; kbk < KB; ++kbk)
+          ka[s][kbk] = __builtin_bit_cast(bf16x8, kl[kbk * 32 * KPITCH + 2 * s]);
+#pragma unroll
+      for (int kbk = 0; kbk < KB; ++kbk)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sacc[0][kbk][i] = 0.f;
+#pragma unroll
+      for (int s = 0; s < QS; ++s)
+#pragma unroll
+        for (int kbk = 0; kbk < KB; ++kbk)
+          sacc[0][kbk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[s][kbk], qreg[0][s],
+                                                                 sacc[0][kbk], 0, 0, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 4, 0);
+#pragma unroll
+      for (int i = 0; i < NV - 2; ++i) {
+        __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 2, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < NK; ++i) {
+        __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 2, 0);
+    };
     // Online softmax of block qb for tile t (base 2, scale folded into c);
     // produces the next PV operand and returns the rescale factor of O.
     auto softmax = [&](f32x16 (&sacc)[KB], int qb, int t, bool masked, bf16x8 (&pout)[PS]) __attribute__((always_inline)) -> float {
@@ -521,10 +573,16 @@ __global__ __launch_bounds__(W * 64, W == 4 ? 2 : 1) void attn_fwd_bf16_kernel(c
     const int grp_id = wave / kGroupWaves;
     f32x16 sacc[kQB][KB];
     auto mfma_phase = [&](int t, const u32x4* kb, const u32x4* vb) __attribute__((always_inline)) {
-      __builtin_amdgcn_s_setprio(1);
-      if (t < my_total) qk(sacc, kb);
-      if (t >= 1 && t <= my_total) pv(vb);
-      __builtin_amdgcn_s_setprio(0);
+      // One instruction stream for every tile up to my_total: at t = 0 the
+      // PV half multiplies the zeroed P by finite V data (a no-op), and at
+      // t = my_total the QK half computes a score tile nobody reads. A
+      // branch per product costs more (registers at the join) than these
+      // 32 MFMAs per pass.
+      if (t <= my_total) {
+        __builtin_amdgcn_s_setprio(1);
+        pvqk(sacc, kb, vb);
+        __builtin_amdgcn_s_setprio(0);
+      }
     };
     auto valu_phase = [&](int t) __attribute__((always_inline)) {
       if (t >= 0 && t < my_total) {
@@ -577,7 +635,12 @@ __global__ __launch_bounds__(W * 64, W == 4 ? 2 : 1) void attn_fwd_bf16_kernel(c
         half_step(g_c, std::integral_constant<int, 3>{}, h + 3);
       }
     };
+    // K(0), plus V(0) in the buffer the first (empty) PV half reads, so
+    // that it multiplies the zeroed P by finite values.
+#pragma unroll
+    for (int ps = 0; ps < PS; ++ps) pprev[0][ps] = bf16x8{};
     load_k(kbuf0, 0);
+    load_v(vbuf1, 0);
     wait_vm();
     __syncthreads();
     if (grp_id == 0) run_group(std::integral_constant<int, 0>{});
