@@ -67,6 +67,8 @@ class AttnInputs:
     Dense:     q [B,H,Lq,d], k/v [B,Hkv,Lk,d], kv_len [B] or None.
     Broadcast: q [B_c,H,Lq,d], k/v [B_u,Hkv,Lk,d], cand2user [B_c],
                kv_len [B_u] or None.
+    Jagged:    q [total_q,H,d], k/v [total_kv,Hkv,d], q_offsets and
+               kv_offsets int32 [B+1].
     """
     q: np.ndarray
     k: np.ndarray
@@ -75,6 +77,8 @@ class AttnInputs:
     causal: bool = False
     kv_len: np.ndarray | None = None
     cand2user: np.ndarray | None = None
+    q_offsets: np.ndarray | None = None
+    kv_offsets: np.ndarray | None = None
     scale: float | None = None
     meta: dict = field(default_factory=dict)
 
@@ -127,8 +131,34 @@ def make_bcast(B_c, B_u, H, Hkv, Lq, Lk, d, *, dtype="bf16", causal=False, seed=
                       meta=dict(kind="bcast", B_c=B_c, B_u=B_u, H=H, Hkv=Hkv, Lq=Lq, Lk=Lk, d=d))
 
 
+def make_jagged(B, H, Hkv, d, *, len_range=None, lengths=None, kv_lengths=None, dtype="bf16",
+                causal=False, seed=0, scale=None) -> AttnInputs:
+    """Jagged problem: B packed sequences with iid N(0,1) entries.
+
+    Query lengths are `lengths`, or drawn uniformly from the integers
+    len_range=(lo, hi) inclusive on the integer stream. Key lengths default to
+    the query lengths (self-attention over each sequence).
+    """
+    if lengths is None:
+        lo, hi = len_range
+        lengths = _gen(seed, STREAM_INT).integers(lo, hi + 1, size=B)
+    lengths = np.asarray(lengths, dtype=np.int64)
+    kv_lengths = lengths if kv_lengths is None else np.asarray(kv_lengths, dtype=np.int64)
+    q_offsets = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    kv_offsets = np.concatenate([[0], np.cumsum(kv_lengths)]).astype(np.int32)
+    q = _draw((int(q_offsets[-1]), H, d), dtype, seed, STREAM_Q)
+    k = _draw((int(kv_offsets[-1]), Hkv, d), dtype, seed, STREAM_K)
+    v = _draw((int(kv_offsets[-1]), Hkv, d), dtype, seed, STREAM_V)
+    return AttnInputs(q, k, v, dtype, causal=causal, q_offsets=q_offsets, kv_offsets=kv_offsets,
+                      scale=scale,
+                      meta=dict(kind="jagged", B=B, H=H, Hkv=Hkv, d=d,
+                                max_Lq=int(lengths.max(initial=0)),
+                                max_Lk=int(kv_lengths.max(initial=0))))
+
+
 # The workloads the method is measured on: tiny fp32 parity case, dense causal,
-# in-kernel broadcast, kv_len-masked, long-sequence GQA causal.
+# in-kernel broadcast, kv_len-masked, long-sequence GQA causal, and jagged
+# causal self-attention over sequences of uniformly drawn lengths.
 WORKLOADS = {
     "fp32_tiny": dict(kind="dense", B=1, H=1, Hkv=1, Lq=128, Lk=128, d=64, dtype="f32",
                       causal=False),
@@ -140,6 +170,8 @@ WORKLOADS = {
                                    dtype="bf16", causal=False, kv_len_range=(2048, 4096)),
     "gqa_causal_L16384": dict(kind="dense", B=1, H=32, Hkv=8, Lq=16384, Lk=16384, d=128,
                               dtype="bf16", causal=True),
+    "jagged_causal_B32": dict(kind="jagged", B=32, H=16, Hkv=16, d=128, len_range=(256, 4096),
+                              dtype="bf16", causal=True),
 }
 
 
@@ -149,5 +181,7 @@ def make_workload(name: str, seed: int = 0) -> AttnInputs:
     if kind == "dense":
         return make_dense(w.pop("B"), w.pop("H"), w.pop("Hkv"), w.pop("Lq"), w.pop("Lk"),
                           w.pop("d"), seed=seed, **w)
+    if kind == "jagged":
+        return make_jagged(w.pop("B"), w.pop("H"), w.pop("Hkv"), w.pop("d"), seed=seed, **w)
     return make_bcast(w.pop("B_c"), w.pop("B_u"), w.pop("H"), w.pop("Hkv"), w.pop("Lq"),
                       w.pop("Lk"), w.pop("d"), seed=seed, **w)

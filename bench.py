@@ -35,8 +35,21 @@ KERNEL_SOURCE = os.path.join(ROOT, "tiled_attention_attn_amd", "csrc", "attn_bf1
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
+def _seq_lengths(w: ai.AttnInputs):
+    return np.diff(w.q_offsets).astype(np.int64), np.diff(w.kv_offsets).astype(np.int64)
+
+
 def pairs(w: ai.AttnInputs) -> int:
-    """Unmasked (query, key) pairs summed over batch entries and heads."""
+    """Unmasked (query, key) pairs summed over batch entries (sequences) and heads."""
+    if w.q_offsets is not None:
+        H = w.q.shape[1]
+        total = 0
+        for lq, lk in zip(*_seq_lengths(w)):
+            if w.causal:
+                total += int(np.minimum(np.arange(lq) + 1, lk).sum())
+            else:
+                total += int(lq * lk)
+        return total * H
     NB, H, Lq, _ = w.q.shape
     Lk = w.k.shape[2]
     kv_b = w.kv_len if w.cand2user is None or w.kv_len is None else w.kv_len[w.cand2user]
@@ -52,12 +65,14 @@ def pairs(w: ai.AttnInputs) -> int:
 
 
 def algorithmic_flops(w) -> int:
-    return 4 * w.q.shape[3] * pairs(w)
+    return 4 * w.q.shape[-1] * pairs(w)
 
 
 def algorithmic_bytes(w) -> int:
     """Read Q, the unique valid K/V rows and the index arrays; write O."""
     esz = 2 if w.dtype == "bf16" else 4
+    if w.q_offsets is not None:   # jagged: every packed K/V token is read once
+        return 2 * w.q.size * esz + 2 * w.k.size * esz + 4 * (w.q_offsets.size + w.kv_offsets.size)
     NKV, Hkv, Lk, d = w.k.shape
     kv_rows = 0
     for u in range(NKV):
@@ -89,11 +104,17 @@ class Runner:
         self.o = torch.empty_like(self.q)
         self.kv = None if w.kv_len is None else torch.from_numpy(w.kv_len).cuda()
         self.c2u = None if w.cand2user is None else torch.from_numpy(w.cand2user).cuda()
+        self.qo = None if w.q_offsets is None else torch.from_numpy(w.q_offsets).cuda()
+        self.ko = None if w.kv_offsets is None else torch.from_numpy(w.kv_offsets).cuda()
         import tiled_attention_attn_amd as taa
         self.taa = taa
 
     def __call__(self):
-        if self.c2u is None:
+        if self.qo is not None:
+            self.taa.attn_fwd_jagged(self.q, self.k, self.v, self.qo, self.ko,
+                                     self.w.meta["max_Lq"], self.w.meta["max_Lk"], self.o,
+                                     causal=self.w.causal)
+        elif self.c2u is None:
             self.taa.attn_fwd(self.q, self.k, self.v, self.o, causal=self.w.causal,
                               kv_len=self.kv)
         else:
@@ -122,6 +143,8 @@ def sampled_error(run: Runner, seed: int = 1, nrows: int = 4) -> float:
     import torch
     w = run.w
     rng = np.random.default_rng(seed)
+    if w.q_offsets is not None:
+        return _sampled_error_jagged(run, rng, nrows)
     NB, H, Lq, _ = w.q.shape
     worst = 0.0
     for _ in range(2):
@@ -135,6 +158,29 @@ def sampled_error(run: Runner, seed: int = 1, nrows: int = 4) -> float:
                                     ai.to_f64(w.k[u:u + 1, g:g + 1], w.dtype),
                                     ai.to_f64(w.v[u:u + 1, g:g + 1], w.dtype), 0, 0, rows,
                                     causal=w.causal, kv_len=kvl)
+        worst = max(worst, float(np.abs(got - ref).max()))
+    return worst
+
+
+def _sampled_error_jagged(run: Runner, rng, nrows: int) -> float:
+    import oracle
+    import torch
+    w = run.w
+    H, Hkv = w.q.shape[1], w.k.shape[1]
+    worst = 0.0
+    for _ in range(2):
+        b, h = int(rng.integers(len(w.q_offsets) - 1)), int(rng.integers(H))
+        qs, qe = int(w.q_offsets[b]), int(w.q_offsets[b + 1])
+        ks, ke = int(w.kv_offsets[b]), int(w.kv_offsets[b + 1])
+        if qe == qs:
+            continue
+        rows = np.unique(np.concatenate([[0, qe - qs - 1], rng.integers(0, qe - qs, nrows)]))
+        got = run.o[torch.from_numpy(qs + rows).cuda(), h].double().cpu().numpy()
+        g = h // (H // Hkv)
+        ref = oracle.attention_jagged_rows(
+            ai.to_f64(w.q[qs:qe, h:h + 1], w.dtype), ai.to_f64(w.k[ks:ke, g:g + 1], w.dtype),
+            ai.to_f64(w.v[ks:ke, g:g + 1], w.dtype), [0, qe - qs], [0, ke - ks], 0, 0, rows,
+            causal=w.causal)
         worst = max(worst, float(np.abs(got - ref).max()))
     return worst
 
@@ -153,11 +199,35 @@ def cpu_baseline(w: ai.AttnInputs, budget_s: float = 15.0) -> dict:
         cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     except Exception:
         cores = os.cpu_count() or 1
-    NB, H, Lq, d = w.q.shape
-    Hkv, Lk = w.k.shape[1], w.k.shape[2]
     rng = np.random.default_rng(123)
     heads_done, flops, t_total = 0, 0, 0.0
     rows_per_head = 256
+    if w.q_offsets is not None:   # jagged: random (sequence, head) pairs
+        H, d, Hkv = w.q.shape[1], w.q.shape[2], w.k.shape[1]
+        while t_total < budget_s and heads_done < 4096:
+            b, h = int(rng.integers(len(w.q_offsets) - 1)), int(rng.integers(H))
+            qs, qe = int(w.q_offsets[b]), int(w.q_offsets[b + 1])
+            ks, ke = int(w.kv_offsets[b]), int(w.kv_offsets[b + 1])
+            if qe == qs:
+                continue
+            rows = np.sort(rng.choice(qe - qs, size=min(rows_per_head, qe - qs), replace=False))
+            g = h // (H // Hkv)
+            qf, kf, vf = (ai.to_f64(x, w.dtype) for x in
+                          (w.q[qs:qe, h:h + 1], w.k[ks:ke, g:g + 1], w.v[ks:ke, g:g + 1]))
+            t0 = time.perf_counter()
+            oracle.attention_jagged_rows(qf, kf, vf, [0, qe - qs], [0, ke - ks], 0, 0, rows,
+                                         causal=w.causal)
+            t_total += time.perf_counter() - t0
+            valid = np.minimum(rows + 1, ke - ks) if w.causal else np.full(len(rows), ke - ks)
+            flops += 4 * d * int(valid.sum())
+            heads_done += 1
+        return {"value": flops / t_total / 1e12, "unit": "TFLOP/s", "cores": int(cores),
+                "kind": "oracle",
+                "sample": f"{heads_done} random (sequence, head) pairs x up to {rows_per_head} "
+                          f"random query rows of {w.meta} ({flops:.3e} algorithmic FLOPs in "
+                          f"{t_total:.1f} s)"}
+    NB, H, Lq, d = w.q.shape
+    Hkv, Lk = w.k.shape[1], w.k.shape[2]
     while t_total < budget_s and heads_done < 4096:
         b, h = int(rng.integers(NB)), int(rng.integers(H))
         rows = np.sort(rng.choice(Lq, size=min(rows_per_head, Lq), replace=False))

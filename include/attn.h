@@ -56,7 +56,8 @@ typedef enum {
   ATTN_OK = 0,
   ATTN_EINVAL = -1,       /* bad argument: NULL pointer, negative size, H % Hkv != 0,
                              misaligned pointer, non-finite or negative scale, size overflow,
-                             bf16 with (Lk + 64) * d * 2 > 2^31 - 1 bytes per K/V head */
+                             bf16 with (Lk + 64) * d * 2 > 2^31 - 1 bytes per K/V head
+                             (jagged: (max_Lk + 64) * Hkv * d * 2) */
   ATTN_EUNSUPPORTED = -2, /* head dim d not in {64, 128}, or unknown dtype */
   ATTN_ELAUNCH = -3       /* the HIP launch reported an error */
 } attn_status;
@@ -95,10 +96,35 @@ int attn_fwd_bcast(const void* q, const void* k, const void* v, void* o,
                    int causal, const int32_t* kv_len, float scale,
                    int dtype, void* stream);
 
+/*
+ * Jagged (variable-length) attention forward: B sequences of different
+ * lengths packed token by token, each attending over its own keys only.
+ * The pages give this operation only as an article title ("Meta 造了个 Triton
+ * 扩展 TLX..." page, link list, "Optimizing Jagged Flash Attention with
+ * TLX"); the reading here is the plain one: offset arrays in place of B*L.
+ *   q, o       [total_q,  H,   d]  total_q  = q_offsets[B]
+ *   k, v       [total_kv, Hkv, d]  total_kv = kv_offsets[B]
+ *   q_offsets  [B+1] int32, nondecreasing, q_offsets[0] = 0: sequence b owns
+ *              query tokens q_offsets[b] .. q_offsets[b+1]-1
+ *   kv_offsets [B+1] int32, the same for keys/values
+ *   max_Lq, max_Lk  upper bounds of the lengths (the grid is sized on them);
+ *              a longer sequence is cut: rows past max_Lq are not written,
+ *              keys past max_Lk are ignored
+ * Within a sequence the operation, masks (causal is top-left in local
+ * indices) and element types are those of attn_fwd; a sequence with no keys
+ * gives zero rows. Offsets live in device memory and are not checked
+ * (lengths are clamped to [0, max]). bf16 needs (max_Lk + 64) * Hkv * d * 2
+ * below 2^31 bytes. Other arguments and errors as attn_fwd.
+ */
+int attn_fwd_jagged(const void* q, const void* k, const void* v, void* o,
+                    const int32_t* q_offsets, const int32_t* kv_offsets,
+                    int B, int H, int Hkv, int max_Lq, int max_Lk, int d,
+                    int causal, float scale, int dtype, void* stream);
+
 /* Static, human-readable text for a status code (never NULL). */
 const char* attn_strerror(int status);
 
-/* ABI version: major * 100 + minor. */
+/* ABI version: major * 100 + minor (101: attn_fwd_jagged added). */
 int attn_version(void);
 
 #ifdef __cplusplus

@@ -25,6 +25,14 @@ queries read their user's keys/values at the users' own batch size, with no
 replication; here that is q[c] attending over k[cand2user[c]],
 v[cand2user[c]].
 
+Jagged attention: the page "Meta 造了个 Triton 扩展 TLX ..." lists, among its
+links, an article on jagged flash attention and gives nothing more. The plain
+reading: B sequences packed token by token, q [total_q, H, d] and k, v
+[total_kv, Hkv, d]; sequence b owns query tokens q_offsets[b] ..
+q_offsets[b+1]-1 and key tokens kv_offsets[b] .. kv_offsets[b+1]-1, and is
+the definition above applied to its own slices (causal top-left in local
+indices; no keys gives zero rows).
+
 Readings where the pages are silent (each is also listed with the design
 notes): scale defaults to 1/sqrt(d); the mask is additive -inf; causal is
 top-left (key j allowed iff j <= i); kv_len is one value per K/V batch entry,
@@ -44,7 +52,8 @@ import math
 
 import numpy as np
 
-__all__ = ["attention", "attention_rows", "attention_bcast", "probabilities"]
+__all__ = ["attention", "attention_rows", "attention_bcast", "attention_jagged",
+           "attention_jagged_rows", "probabilities"]
 
 
 def _default_scale(d: int, scale) -> float:
@@ -69,6 +78,8 @@ def _allowed(rows: np.ndarray, Lk: int, causal: bool, kv_len_b) -> np.ndarray:
 
 def _softmax_rows(s: np.ndarray, ok: np.ndarray) -> np.ndarray:
     """Row softmax of s over the allowed entries; rows with none give zeros."""
+    if s.shape[1] == 0:                       # no keys at all: every row has none
+        return np.zeros_like(s)
     s = np.where(ok, s, -np.inf)
     m = s.max(axis=1, keepdims=True)
     m = np.where(np.isfinite(m), m, 0.0)
@@ -156,3 +167,47 @@ def attention_bcast(q, k, v, cand2user, *, causal=False, kv_len=None, scale=None
                                     np.asarray(k[u, g], np.float64),
                                     np.asarray(v[u, g], np.float64), rows, causal, kvl, sc)
     return o
+
+
+def _seq_bounds(offsets, b):
+    start = int(offsets[b])
+    return start, max(int(offsets[b + 1]) - start, 0)
+
+
+def attention_jagged(q, k, v, q_offsets, kv_offsets, *, causal=False, scale=None):
+    """Jagged attention, float64: every sequence is the dense definition on its slices.
+
+    q [total_q,H,d]; k, v [total_kv,Hkv,d]; q_offsets, kv_offsets int arrays
+    [B+1]. Returns o [total_q,H,d] float64 (tokens outside every sequence: 0).
+    """
+    q, k, v = (np.asarray(x, np.float64) for x in (q, k, v))
+    H, d = q.shape[1], q.shape[2]
+    Hkv = k.shape[1]
+    assert H % Hkv == 0 and k.shape == v.shape and k.shape[2] == d
+    group = H // Hkv
+    sc = _default_scale(d, scale)
+    o = np.zeros_like(q)
+    for b in range(len(q_offsets) - 1):
+        qs, lq = _seq_bounds(q_offsets, b)
+        ks, lk = _seq_bounds(kv_offsets, b)
+        rows = np.arange(lq)
+        for h in range(H):
+            g = h // group
+            o[qs:qs + lq, h], _ = _head_rows(q[qs:qs + lq, h], k[ks:ks + lk, g],
+                                             v[ks:ks + lk, g], rows, causal, None, sc)
+    return o
+
+
+def attention_jagged_rows(q, k, v, q_offsets, kv_offsets, b, h, rows, *, causal=False,
+                          scale=None):
+    """Rows `rows` (local to sequence b) of head h of the jagged output."""
+    H, d, Hkv = q.shape[1], q.shape[2], k.shape[1]
+    g = h // (H // Hkv)
+    qs, _ = _seq_bounds(q_offsets, b)
+    ks, lk = _seq_bounds(kv_offsets, b)
+    rows = np.asarray(rows)
+    q_bh = np.asarray(q[qs:qs + (int(rows.max()) + 1 if len(rows) else 0), h], np.float64)
+    out, _ = _head_rows(q_bh, np.asarray(k[ks:ks + lk, g], np.float64),
+                        np.asarray(v[ks:ks + lk, g], np.float64), rows, causal, None,
+                        _default_scale(d, scale))
+    return out

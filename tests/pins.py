@@ -301,4 +301,86 @@ def pin_torch_sdpa(impl):
     np.testing.assert_allclose(impl.attention(q, k, v, kv_len=kv), ref, rtol=0, atol=1e-13)
 
 
+# --- jagged ---------------------------------------------------------------------------
+
+def _jagged_case(seed, lq, lk, H=4, Hkv=2, d=3):
+    qo = np.concatenate([[0], np.cumsum(lq)]).astype(np.int64)
+    ko = np.concatenate([[0], np.cumsum(lk)]).astype(np.int64)
+    q = _rand((int(qo[-1]), H, d), seed)
+    k, v = _rand((int(ko[-1]), Hkv, d), seed + 1), _rand((int(ko[-1]), Hkv, d), seed + 2)
+    return q, k, v, qo, ko
+
+
+def _as_dense(x):
+    """One packed sequence [L, heads, d] as a one-entry dense batch [1, heads, L, d]."""
+    return np.ascontiguousarray(x.transpose(1, 0, 2))[None]
+
+
+def pin_jagged_brute_force(impl):
+    """Each sequence of a tiny jagged batch (an empty one, one without keys, Lq != Lk,
+    GQA) against the 40-digit brute force."""
+    q, k, v, qo, ko = _jagged_case(60, [3, 0, 5, 2], [4, 3, 5, 0])
+    for causal in (False, True):
+        o = impl.attention_jagged(q, k, v, qo, ko, causal=causal, scale=0.8)
+        for b in range(4):
+            qs, qe, ks, ke = qo[b], qo[b + 1], ko[b], ko[b + 1]
+            ref = _brute_decimal(_as_dense(q[qs:qe]), _as_dense(k[ks:ke]), _as_dense(v[ks:ke]),
+                                 causal, None, 0.8)
+            np.testing.assert_allclose(o[qs:qe], ref[0].transpose(1, 0, 2), rtol=0, atol=1e-12)
+
+
+def pin_jagged_torch_sdpa(impl):
+    """Per sequence, PyTorch's float64 SDPA (top-left causal, GQA); no keys gives zeros."""
+    import torch
+    import torch.nn.functional as F
+    q, k, v, qo, ko = _jagged_case(63, [4, 7, 1, 3], [6, 7, 2, 0], H=4, Hkv=1, d=8)
+    for causal in (False, True):
+        o = impl.attention_jagged(q, k, v, qo, ko, causal=causal, scale=0.4)
+        for b in range(4):
+            qs, qe, ks, ke = qo[b], qo[b + 1], ko[b], ko[b + 1]
+            if ke == ks:
+                np.testing.assert_array_equal(o[qs:qe], 0.0)
+                continue
+            tq, tk, tv = (torch.from_numpy(_as_dense(x)) for x in (q[qs:qe], k[ks:ke], v[ks:ke]))
+            ref = F.scaled_dot_product_attention(tq, tk, tv, is_causal=causal, scale=0.4,
+                                                 enable_gqa=True).numpy()[0].transpose(1, 0, 2)
+            np.testing.assert_allclose(o[qs:qe], ref, rtol=0, atol=1e-13)
+
+
+def pin_jagged_equal_lengths_is_dense(impl):
+    """Sequences of one common length are the dense batch in another layout."""
+    B, L, H, Hkv, d = 3, 5, 4, 2, 6
+    q, k, v, qo, ko = _jagged_case(66, [L] * B, [L] * B, H=H, Hkv=Hkv, d=d)
+    for causal in (False, True):
+        o = impl.attention_jagged(q, k, v, qo, ko, causal=causal)
+        dense = impl.attention(*(x.reshape(B, L, -1, d).transpose(0, 2, 1, 3) for x in (q, k, v)),
+                               causal=causal)
+        np.testing.assert_allclose(o, dense.transpose(0, 2, 1, 3).reshape(B * L, H, d),
+                                   rtol=0, atol=1e-14)
+
+
+def pin_jagged_sequence_permutation(impl):
+    """Reordering the packed sequences reorders the output the same way."""
+    lq, lk = [2, 5, 3], [4, 1, 6]
+    q, k, v, qo, ko = _jagged_case(69, lq, lk)
+    o = impl.attention_jagged(q, k, v, qo, ko, causal=True)
+    perm = [2, 0, 1]
+    cat = lambda x, off: np.concatenate([x[off[b]:off[b + 1]] for b in perm])
+    qo2 = np.concatenate([[0], np.cumsum([lq[b] for b in perm])])
+    ko2 = np.concatenate([[0], np.cumsum([lk[b] for b in perm])])
+    o2 = impl.attention_jagged(cat(q, qo), cat(k, ko), cat(v, ko), qo2, ko2, causal=True)
+    np.testing.assert_array_equal(o2, cat(o, qo))
+
+
+def pin_jagged_rows_subset(impl):
+    """attention_jagged_rows returns exactly the matching rows of attention_jagged."""
+    q, k, v, qo, ko = _jagged_case(72, [4, 6], [5, 3])
+    for causal in (False, True):
+        full = impl.attention_jagged(q, k, v, qo, ko, causal=causal)
+        for b, rows in ((0, [3, 0]), (1, [5, 2, 1])):
+            for h in (0, 3):
+                part = impl.attention_jagged_rows(q, k, v, qo, ko, b, h, rows, causal=causal)
+                np.testing.assert_array_equal(part, full[qo[b] + np.array(rows), h])
+
+
 ALL_PINS = [v for n, v in sorted(globals().items()) if n.startswith("pin_")]

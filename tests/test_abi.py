@@ -27,13 +27,14 @@ def lib():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == ["attn_fwd", "attn_fwd_bcast", "attn_strerror", "attn_version"]
+    assert declared_functions() == ["attn_fwd", "attn_fwd_bcast", "attn_fwd_jagged",
+                                    "attn_strerror", "attn_version"]
 
 
 def test_library_exports_every_declared_symbol(lib):
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert lib.attn_version() == 100
+    assert lib.attn_version() == 101
 
 
 def test_strerror_covers_every_status(lib):
@@ -103,3 +104,26 @@ def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
     monkeypatch.setattr(b, "_lib", None)
     with pytest.raises(RuntimeError, match="no fallback"):
         b.load_library(str(tmp_path / "missing.so"))
+
+
+def jagged(lib, qo=FAKE, ko=FAKE, B=2, H=2, Hkv=1, max_Lq=16, max_Lk=16, d=64, scale=0.0,
+           dtype=taa.ATTN_BF16):
+    return lib.attn_fwd_jagged(FAKE, FAKE, FAKE, FAKE, qo, ko, B, H, Hkv, max_Lq, max_Lk, d, 0,
+                               scale, dtype, None)
+
+
+@pytest.mark.parametrize("kwargs,status", [
+    (dict(qo=None), taa.ATTN_EINVAL),
+    (dict(ko=None), taa.ATTN_EINVAL),
+    (dict(d=96), taa.ATTN_EUNSUPPORTED),
+    (dict(H=3, Hkv=2), taa.ATTN_EINVAL),
+    (dict(B=-1), taa.ATTN_EINVAL),
+    (dict(max_Lk=-1), taa.ATTN_EINVAL),
+    (dict(scale=float("nan")), taa.ATTN_EINVAL),
+    # packed K/V rows are Hkv*d apart: 32-bit buffer offsets bound max_Lk * Hkv
+    (dict(max_Lk=(1 << 20), Hkv=8, H=8, d=128), taa.ATTN_EINVAL),
+    (dict(B=0, qo=None, ko=None), taa.ATTN_OK),
+    (dict(max_Lq=0, qo=None, ko=None), taa.ATTN_OK),
+])
+def test_attn_fwd_jagged_argument_checks(lib, kwargs, status):
+    assert jagged(lib, **kwargs) == status

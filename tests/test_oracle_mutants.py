@@ -31,6 +31,13 @@ MUTANTS = {
     "bcast_no_nan": ("o[n] = np.nan", "o[n] = 0.0"),
     "masked_row_not_zero": ("where=z > 0)", "where=z >= 0)"),
     "exp_base_2": ("np.exp(s - m)", "np.exp2(s - m)"),
+    "jagged_kv_uses_q_offsets": ("ks, lk = _seq_bounds(kv_offsets, b)",
+                                 "ks, lk = _seq_bounds(q_offsets, b)"),
+    "jagged_length_short": ("return start, max(int(offsets[b + 1]) - start, 0)",
+                            "return start, max(int(offsets[b + 1]) - start - 1, 0)"),
+    "jagged_global_causal": ("rows = np.arange(lq)\n", "rows = np.arange(qs, qs + lq)\n"),
+    "jagged_heads_interleaved": ("o[qs:qs + lq, h], _ = _head_rows(q[qs:qs + lq, h], k[ks:ks + lk, g]",
+                                 "o[qs:qs + lq, h], _ = _head_rows(q[qs:qs + lq, h], k[ks:ks + lk, h % Hkv]"),
 }
 
 

@@ -40,6 +40,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.attn_fwd_bcast.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32,
                                    vp, f32, i32, vp]
     lib.attn_fwd_bcast.restype = i32
+    lib.attn_fwd_jagged.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
+                                    f32, i32, vp]
+    lib.attn_fwd_jagged.restype = i32
     lib.attn_strerror.argtypes = [i32]
     lib.attn_strerror.restype = ctypes.c_char_p
     lib.attn_version.argtypes = []
@@ -143,4 +146,39 @@ def attn_fwd_bcast(q, k, v, cand2user, o=None, *, causal=False, kv_len=None, sca
     _check(lib.attn_fwd_bcast(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(cand2user), B_c, B_u, H,
                               k.shape[1], Lq, k.shape[2], d, int(bool(causal)), _ptr(kv_len),
                               float(scale), _dtype_code(q), _stream(stream)))
+    return o
+
+
+def attn_fwd_jagged(q, k, v, q_offsets, kv_offsets, max_lq, max_lk, o=None, *, causal=False,
+                    scale=0.0, stream=None):
+    """Jagged attention: sequence b's queries q[q_offsets[b]:q_offsets[b+1]] attend over
+    k/v[kv_offsets[b]:kv_offsets[b+1]] only.
+
+    q [total_q,H,d], k/v [total_kv,Hkv,d] (bf16 or fp32, contiguous, on the device);
+    q_offsets / kv_offsets: int32 [B+1] device tensors; max_lq / max_lk: host ints
+    bounding the sequence lengths. Returns o [total_q,H,d].
+    """
+    import torch
+    lib = load_library()
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not t.is_cuda or not t.is_contiguous() or t.dim() != 3:
+            raise ValueError(f"{name} must be a contiguous 3-D device tensor [tokens, heads, d]")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k and v must share one dtype")
+    if k.shape != v.shape or q.shape[2] != k.shape[2]:
+        raise ValueError("k and v must match, and share d with q")
+    for name, t in (("q_offsets", q_offsets), ("kv_offsets", kv_offsets)):
+        if t.dtype != torch.int32 or not t.is_cuda or not t.is_contiguous() or t.dim() != 1:
+            raise ValueError(f"{name} must be a contiguous 1-D int32 device tensor")
+    if q_offsets.numel() != kv_offsets.numel() or q_offsets.numel() < 1:
+        raise ValueError("q_offsets and kv_offsets must both hold B+1 entries")
+    if o is None:
+        o = torch.empty_like(q)
+    elif o.shape != q.shape or o.dtype != q.dtype or not o.is_contiguous() or not o.is_cuda:
+        raise ValueError("o must be a contiguous device tensor shaped and typed like q")
+    B = q_offsets.numel() - 1
+    _, H, d = q.shape
+    _check(lib.attn_fwd_jagged(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(q_offsets),
+                               _ptr(kv_offsets), B, H, k.shape[1], int(max_lq), int(max_lk), d,
+                               int(bool(causal)), float(scale), _dtype_code(q), _stream(stream)))
     return o

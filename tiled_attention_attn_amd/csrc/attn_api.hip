@@ -24,7 +24,8 @@ bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15u) == 0; }
 int check_and_launch(const void* q, const void* k, const void* v, void* o,
                      const int32_t* cand2user, int NB, int NKV, int H, int Hkv, int Lq, int Lk,
                      int d, int causal, const int32_t* kv_len, float scale, int dtype,
-                     void* stream) {
+                     void* stream, const int32_t* q_offsets = nullptr,
+                     const int32_t* kv_offsets = nullptr) {
   if (dtype != ATTN_F32 && dtype != ATTN_BF16) return ATTN_EUNSUPPORTED;
   if (d != 64 && d != 128) return ATTN_EUNSUPPORTED;
   if (NB < 0 || NKV < 0 || H < 0 || Lq < 0 || Lk < 0 || Hkv < 1) return ATTN_EINVAL;
@@ -46,6 +47,8 @@ int check_and_launch(const void* q, const void* k, const void* v, void* o,
   p.o = o;
   p.kv_len = kv_len;
   p.cand2user = cand2user;
+  p.q_offsets = q_offsets;
+  p.kv_offsets = kv_offsets;
   p.NB = NB;
   p.NKV = NKV;
   p.H = H;
@@ -90,6 +93,16 @@ int attn_fwd_bcast(const void* q, const void* k, const void* v, void* o,
                           scale, dtype, stream);
 }
 
+int attn_fwd_jagged(const void* q, const void* k, const void* v, void* o,
+                    const int32_t* q_offsets, const int32_t* kv_offsets, int B, int H, int Hkv,
+                    int max_Lq, int max_Lk, int d, int causal, float scale, int dtype,
+                    void* stream) {
+  if (B > 0 && H > 0 && max_Lq > 0 && (q_offsets == nullptr || kv_offsets == nullptr))
+    return ATTN_EINVAL;
+  return check_and_launch(q, k, v, o, nullptr, B, B, H, Hkv, max_Lq, max_Lk, d, causal, nullptr,
+                          scale, dtype, stream, q_offsets, kv_offsets);
+}
+
 const char* attn_strerror(int status) {
   switch (status) {
     case ATTN_OK: return "ok";
@@ -100,6 +113,6 @@ const char* attn_strerror(int status) {
   }
 }
 
-int attn_version(void) { return 100; }
+int attn_version(void) { return 101; }
 
 }  // extern "C"

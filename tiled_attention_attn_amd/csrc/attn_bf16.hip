@@ -101,6 +101,7 @@ __device__ __forceinline__ int xcd_remap(int w, int T, int chunk) {
 struct WaveTask {
   int batch;   // query-side batch entry
   int row0;    // first query row of the wave
+  int lq;      // query rows of the wave's sequence
   int kvb;     // K/V batch entry (user for the broadcast variant)
   bool valid;  // rows exist
   bool bad;    // kvb out of range: output NaN
@@ -144,7 +145,7 @@ __device__ __forceinline__ void wait_vm() { __builtin_amdgcn_s_waitcnt(0x0F70); 
 // W = 4: one 4-wave workgroup per SIMD pair (two workgroups per CU), the
 // software-pipelined loop; W = 8: one 8-wave workgroup per CU, the ping-pong
 // loop (waves w and w+4 on one SIMD).
-template <int D, bool CAUSAL, int W>
+template <int D, bool CAUSAL, int W, bool JAGGED>
 __global__ __launch_bounds__(W * 64, W == 4 ? 2 : 1) void attn_fwd_bf16_kernel(const Params p) {
   using TL = Tile<D, W>;
   constexpr int kWaves = W;
@@ -192,6 +193,18 @@ __global__ __launch_bounds__(W * 64, W == 4 ? 2 : 1) void attn_fwd_bf16_kernel(c
   }
   const int g = h / HPG;
 
+  // Row addressing. Dense: rows of one (batch, head) are contiguous, D
+  // elements apart. Jagged (a separate instantiation, so the dense kernels
+  // keep compile-time strides): tokens are packed [total, heads, D], so rows
+  // of one head are heads*D elements apart and sequence b starts at token
+  // offsets[b]; lengths come from the offsets, clamped to [0, Lq] / [0, Lk].
+  constexpr bool jagged = JAGGED;
+  const int q_rs = jagged ? p.H * D : D;
+  const int kv_rs = jagged ? p.Hkv * D : D;
+  auto seq_len = [&](const int32_t* off, int b, int cap) __attribute__((always_inline)) -> int {
+    return min(max(off[b + 1] - off[b], 0), cap);
+  };
+
   // Every thread can derive the task of any wave (needed for shared loop bounds).
   auto task_of = [&](int w) __attribute__((always_inline)) -> WaveTask {
     WaveTask t;
@@ -202,7 +215,9 @@ __global__ __launch_bounds__(W * 64, W == 4 ? 2 : 1) void attn_fwd_bf16_kernel(c
       t.batch = bgrp * p.G + w / p.P;
       t.row0 = (w % p.P) * kRowsPerWave;
     }
-    t.valid = t.batch < p.NB && t.row0 < p.Lq;
+    t.lq = p.Lq;
+    if (jagged && t.batch < p.NB) t.lq = seq_len(p.q_offsets, t.batch, p.Lq);
+    t.valid = t.batch < p.NB && t.row0 < t.lq;
     t.kvb = t.batch;
     t.bad = false;
     if (t.valid && p.cand2user != nullptr) {
@@ -213,15 +228,17 @@ __global__ __launch_bounds__(W * 64, W == 4 ? 2 : 1) void attn_fwd_bf16_kernel(c
   };
 
   const WaveTask me = task_of(wave);
-  const size_t q_head = ((size_t)me.batch * p.H + h) * (size_t)p.Lq;  // row index base
-  const __bf16* __restrict__ qg = (const __bf16*)p.q;
-  __bf16* __restrict__ og = (__bf16*)p.o;
+  // element offset of row 0 of this wave's (sequence, head)
+  size_t q_base = ((size_t)me.batch * p.H + h) * (size_t)p.Lq * D;
+  if (jagged) q_base = me.valid ? (size_t)p.q_offsets[me.batch] * q_rs + (size_t)h * D : 0;
+  const __bf16* __restrict__ qg = (const __bf16*)p.q + q_base;
+  __bf16* __restrict__ og = (__bf16*)p.o + q_base;
 
   // Candidates with an out-of-range user index get NaN rows.
   if (me.valid && me.bad) {
     const int row = me.row0 + col;
-    if (row < p.Lq) {
-      __bf16* orow = og + (q_head + row) * D;
+    if (row < me.lq) {
+      __bf16* orow = og + (size_t)row * q_rs;
       const __bf16 nanv = __builtin_bit_cast(__bf16, (unsigned short)0x7FC0);
       for (int d = half * (D / 2); d < (half + 1) * (D / 2); ++d) orow[d] = nanv;
     }
@@ -238,13 +255,13 @@ __global__ __launch_bounds__(W * 64, W == 4 ? 2 : 1) void attn_fwd_bf16_kernel(c
   for (int j = 0; j < TL::KPER; ++j) {
     const int q = (wave + j * kWaves) * 64 + lane;
     const int r = q / KPITCH, cc = q % KPITCH;
-    koff[j] = (uint32_t)(r * (D * 2) + (cc < NC ? cc : 0) * 16);
+    koff[j] = (uint32_t)(r * (kv_rs * 2) + (cc < NC ? cc : 0) * 16);
   }
 #pragma unroll
   for (int j = 0; j < TL::VPER; ++j) {
     const int q = (wave + j * kWaves) * 64 + lane;
     const int r = q / VPITCH, cc = q % VPITCH;
-    voff[j] = (uint32_t)(r * (D * 2) + (cc < NC ? cc : 0) * 16);
+    voff[j] = (uint32_t)(r * (kv_rs * 2) + (cc < NC ? cc : 0) * 16);
   }
 
   // One pass per distinct K/V batch among the waves (normally exactly one).
@@ -259,13 +276,13 @@ __global__ __launch_bounds__(W * 64, W == 4 ? 2 : 1) void attn_fwd_bf16_kernel(c
     if (seen) continue;
     const int kvb = lt.kvb;
 
-    int nvalid = p.Lk;
+    int nvalid = jagged ? seq_len(p.kv_offsets, kvb, p.Lk) : p.Lk;
     if (p.kv_len != nullptr) nvalid = min(max(p.kv_len[kvb], 0), p.Lk);
 
     // keys a wave needs (causal rows r allow keys <= r)
     auto keys_needed = [&](const WaveTask& t) __attribute__((always_inline)) -> int {
       int n = nvalid;
-      if (CAUSAL) n = min(n, min(t.row0 + kRowsPerWave, p.Lq));
+      if (CAUSAL) n = min(n, min(t.row0 + kRowsPerWave, t.lq));
       return n;
     };
     int ntiles = 0;
@@ -277,8 +294,8 @@ __global__ __launch_bounds__(W * 64, W == 4 ? 2 : 1) void attn_fwd_bf16_kernel(c
     if (ntiles == 0) {
       if (active) {
         const int row = me.row0 + col;  // no valid key: output rows are 0
-        if (row < p.Lq) {
-          __bf16* orow = og + (q_head + row) * D;
+        if (row < me.lq) {
+          __bf16* orow = og + (size_t)row * q_rs;
           for (int d = half * (D / 2); d < (half + 1) * (D / 2); ++d) orow[d] = (__bf16)0.f;
         }
       }
@@ -290,14 +307,19 @@ __global__ __launch_bounds__(W * 64, W == 4 ? 2 : 1) void attn_fwd_bf16_kernel(c
     if (CAUSAL) full_keys = min(full_keys, me.row0 + 1);
     const int my_full = active ? min(full_keys / BN, my_total) : 0;
 
-    const size_t kv_head = ((size_t)kvb * p.Hkv + g) * (size_t)p.Lk;
-    const char* __restrict__ kg = (const char*)p.k + kv_head * (D * 2);
-    const char* __restrict__ vg = (const char*)p.v + kv_head * (D * 2);
+    size_t kv_base = ((size_t)kvb * p.Hkv + g) * (size_t)p.Lk * D;   // elements
+    if (jagged) kv_base = (size_t)p.kv_offsets[kvb] * kv_rs + (size_t)g * D;
+    const char* __restrict__ kg = (const char*)p.k + kv_base * 2;
+    const char* __restrict__ vg = (const char*)p.v + kv_base * 2;
 
     // Direct-to-LDS buffer loads of tile t. The buffer descriptor spans this
     // (batch, head)'s Lk rows, so chunks of rows past the end read as zero
     // (those keys are masked or never read); the tile offset is a scalar.
-    const uint32_t kv_bytes = (uint32_t)p.Lk * (D * 2);
+    // (jagged: the range ends with the last row of this head, so later
+    // rows, which belong to other heads or sequences, read as zero too)
+    const uint32_t kv_bytes =
+        jagged ? (nvalid > 0 ? (uint32_t)(nvalid - 1) * (kv_rs * 2) + D * 2 : 0u)
+               : (uint32_t)p.Lk * (D * 2);
     const __amdgpu_buffer_rsrc_t krsrc =
         __builtin_amdgcn_make_buffer_rsrc((void*)kg, (short)0, (int)kv_bytes, kBufferWord3);
     const __amdgpu_buffer_rsrc_t vrsrc =
@@ -305,7 +327,7 @@ __global__ __launch_bounds__(W * 64, W == 4 ? 2 : 1) void attn_fwd_bf16_kernel(c
     auto load_tile = [&](__amdgpu_buffer_rsrc_t rsrc, u32x4* dst, int t, const uint32_t* off,
                          auto per_c, auto nloads_c) __attribute__((always_inline)) {
       constexpr int PER = decltype(per_c)::value, NLOADS = decltype(nloads_c)::value;
-      const uint32_t tile_off = (uint32_t)t * (BN * D * 2);
+      const uint32_t tile_off = (uint32_t)t * (BN * kv_rs * 2);
 #pragma unroll
       for (int j = 0; j < PER; ++j) {
         const int n = wave + j * kWaves;
@@ -327,8 +349,8 @@ __global__ __launch_bounds__(W * 64, W == 4 ? 2 : 1) void attn_fwd_bf16_kernel(c
 #pragma unroll
     for (int qb = 0; qb < kQB; ++qb) {
       const int row = me.row0 + 32 * qb + col;
-      const bool ok = active && row < p.Lq;
-      const __bf16* qrow = qg + (q_head + (ok ? row : 0)) * D;
+      const bool ok = active && row < me.lq;
+      const __bf16* qrow = qg + (size_t)(ok ? row : 0) * q_rs;
 #pragma unroll
       for (int s = 0; s < QS; ++s) {
         u32x4 x = {0u, 0u, 0u, 0u};
@@ -709,8 +731,8 @@ __global__ __launch_bounds__(W * 64, W == 4 ? 2 : 1) void attn_fwd_bf16_kernel(c
         const float l = halves_sum(l_run[qb]);
         const float inv = (l > 0.f) ? 1.f / l : 0.f;
         const int row = me.row0 + 32 * qb + col;
-        if (row < p.Lq) {
-          __bf16* orow = og + (q_head + row) * D;
+        if (row < me.lq) {
+          __bf16* orow = og + (size_t)row * q_rs;
 #pragma unroll
           for (int b = 0; b < DB; ++b)
 #pragma unroll
@@ -729,8 +751,13 @@ __global__ __launch_bounds__(W * 64, W == 4 ? 2 : 1) void attn_fwd_bf16_kernel(c
 // Host-side launcher (one instance per head dim, causal flag and wave count).
 hipError_t launch_bf16(const Params& p, int D, bool causal, hipStream_t stream) {
   dim3 grid(p.T), block(p.waves * 64);
-#define ATTN_LAUNCH(DD, CC, WW) \
-  hipLaunchKernelGGL((attn_fwd_bf16_kernel<DD, CC, WW>), grid, block, 0, stream, p)
+#define ATTN_LAUNCH(DD, CC, WW)                                                              \
+  do {                                                                                       \
+    if (p.q_offsets != nullptr)                                                              \
+      hipLaunchKernelGGL((attn_fwd_bf16_kernel<DD, CC, WW, true>), grid, block, 0, stream, p); \
+    else                                                                                     \
+      hipLaunchKernelGGL((attn_fwd_bf16_kernel<DD, CC, WW, false>), grid, block, 0, stream, p); \
+  } while (0)
   if (p.waves == 8) {
     if (D == 128) {
       if (causal) ATTN_LAUNCH(128, true, 8); else ATTN_LAUNCH(128, false, 8);
@@ -770,7 +797,8 @@ static int waves_override() {
 bool plan_bf16(Params& p, int D) {
   // K/V of one (batch, head) are addressed through 32-bit buffer offsets;
   // the last tile may run up to 64 rows past Lk.
-  if (((int64_t)p.Lk + 64) * D * 2 > 0x7fffffff) return false;
+  const int64_t kv_row_bytes = (int64_t)(p.q_offsets != nullptr ? p.Hkv : 1) * D * 2;
+  if (((int64_t)p.Lk + 64) * kv_row_bytes > 0x7fffffff) return false;
   int W = (D == 128 && p.Lk >= kPingPongMinKeys) ? 8 : 4;
   if (waves_override() != 0) W = waves_override();
   p.waves = W;

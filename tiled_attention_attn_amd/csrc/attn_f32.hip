@@ -6,6 +6,7 @@
 // fp32 end to end so the result stays within 1e-4 of the exact value. This
 // path serves small fp32 problems: one thread per query row, K/V tiles of 32
 // keys staged in LDS and read as broadcasts, VALU FMAs for both products.
+// It handles the dense, broadcast and jagged layouts.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -28,11 +29,19 @@ __global__ __launch_bounds__(kF32Rows) void attn_fwd_f32_kernel(const Params p) 
   const int b = bh / p.H;
   const int g = h / (p.H / p.Hkv);
   const int row = mt * kF32Rows + tid;
-  const bool row_ok = row < p.Lq;
+  // Dense rows of one (batch, head) are D elements apart; jagged tokens are
+  // packed [total, heads, D] with sequence b starting at offsets[b].
+  const bool jagged = p.q_offsets != nullptr;
+  const int q_rs = jagged ? p.H * D : D;
+  const int kv_rs = jagged ? p.Hkv * D : D;
+  const int lq = jagged ? min(max(p.q_offsets[b + 1] - p.q_offsets[b], 0), p.Lq) : p.Lq;
+  const bool row_ok = row < lq;
 
   const float* __restrict__ qg = (const float*)p.q;
   float* __restrict__ og = (float*)p.o;
-  const size_t qoff = (((size_t)b * p.H + h) * p.Lq + (row_ok ? row : 0)) * D;
+  const size_t qbase = jagged ? (size_t)p.q_offsets[b] * q_rs + (size_t)h * D
+                              : ((size_t)b * p.H + h) * p.Lq * D;
+  const size_t qoff = qbase + (size_t)(row_ok ? row : 0) * q_rs;
 
   int kvb = b;
   if (p.cand2user != nullptr) {
@@ -43,10 +52,12 @@ __global__ __launch_bounds__(kF32Rows) void attn_fwd_f32_kernel(const Params p) 
       return;
     }
   }
-  int nvalid = p.Lk;
+  int nvalid = jagged ? min(max(p.kv_offsets[b + 1] - p.kv_offsets[b], 0), p.Lk) : p.Lk;
   if (p.kv_len != nullptr) nvalid = min(max(p.kv_len[kvb], 0), p.Lk);
+  // keys that may be read: a jagged sequence must not read its neighbours
+  const int kread = jagged ? nvalid : p.Lk;
   int nkeys = nvalid;
-  if (CAUSAL) nkeys = min(nkeys, min(mt * kF32Rows + kF32Rows, p.Lq));
+  if (CAUSAL) nkeys = min(nkeys, min(mt * kF32Rows + kF32Rows, lq));
   const int ntiles = (nkeys + kF32Keys - 1) / kF32Keys;
 
   float q[D], o[D];
@@ -54,8 +65,10 @@ __global__ __launch_bounds__(kF32Rows) void attn_fwd_f32_kernel(const Params p) 
     q[d] = row_ok ? qg[qoff + d] : 0.f;
     o[d] = 0.f;
   }
-  const float* __restrict__ kg = (const float*)p.k + ((size_t)kvb * p.Hkv + g) * p.Lk * D;
-  const float* __restrict__ vg = (const float*)p.v + ((size_t)kvb * p.Hkv + g) * p.Lk * D;
+  const size_t kvbase = jagged ? (size_t)p.kv_offsets[b] * kv_rs + (size_t)g * D
+                               : ((size_t)kvb * p.Hkv + g) * p.Lk * D;
+  const float* __restrict__ kg = (const float*)p.k + kvbase;
+  const float* __restrict__ vg = (const float*)p.v + kvbase;
   float m_run = -INFINITY, l_run = 0.f;
   const float c = p.c;
 
@@ -64,8 +77,8 @@ __global__ __launch_bounds__(kF32Rows) void attn_fwd_f32_kernel(const Params p) 
     for (int e = tid; e < kF32Keys * D; e += kF32Rows) {
       const int j = e / D, d = e % D;
       const int key = t * kF32Keys + j;
-      ks[j][d] = key < p.Lk ? kg[(size_t)key * D + d] : 0.f;
-      vs[j][d] = key < p.Lk ? vg[(size_t)key * D + d] : 0.f;
+      ks[j][d] = key < kread ? kg[(size_t)key * kv_rs + d] : 0.f;
+      vs[j][d] = key < kread ? vg[(size_t)key * kv_rs + d] : 0.f;
     }
     __syncthreads();
     float s[kF32Keys];

@@ -6,14 +6,20 @@ namespace attn {
 
 // One attention problem as the kernels see it. Dense problems have
 // cand2user == nullptr and NKV == NB; the broadcast problem indexes the K/V
-// batch of query batch entry b as cand2user[b].
+// batch of query batch entry b as cand2user[b]. Jagged problems (q_offsets
+// != nullptr) pack the sequences of a batch token by token: Q/O are
+// [total_q, H, D] and K/V [total_kv, Hkv, D]; sequence b holds rows
+// q_offsets[b] .. q_offsets[b+1]-1 (K/V likewise), and Lq / Lk are the
+// largest lengths (the grid is sized on them).
 struct Params {
-  const void* q;             // [NB, H, Lq, D]
-  const void* k;             // [NKV, Hkv, Lk, D]
-  const void* v;             // [NKV, Hkv, Lk, D]
-  void* o;                   // [NB, H, Lq, D]
+  const void* q;             // [NB, H, Lq, D]    (jagged: [total_q, H, D])
+  const void* k;             // [NKV, Hkv, Lk, D] (jagged: [total_kv, Hkv, D])
+  const void* v;             // [NKV, Hkv, Lk, D] (jagged: [total_kv, Hkv, D])
+  void* o;                   // [NB, H, Lq, D]    (jagged: [total_q, H, D])
   const int32_t* kv_len;     // [NKV] or nullptr
   const int32_t* cand2user;  // [NB] or nullptr
+  const int32_t* q_offsets;  // [NB + 1] or nullptr (dense layout)
+  const int32_t* kv_offsets; // [NB + 1], set iff q_offsets is
   int NB, NKV, H, Hkv, Lq, Lk;
   float c;                   // scale * log2(e): softmax runs in base 2
   // Work decomposition (filled by the host dispatcher).
