@@ -33,10 +33,12 @@
  * enqueued on `stream` (a hipStream_t; NULL = the default stream) and the
  * call returns without synchronising. o must not alias q, k or v.
  *
- * Schedules. bf16 problems with d = 128 and Lk >= 8192 run an 8-wave
+ * Schedules. bf16 problems with d = 128 and Lk >= 4096 run an 8-wave
  * workgroup schedule, others a 4-wave one; both compute the same result to
  * within rounding. The environment variable ATTN_BF16_WAVES=4 or 8, read once
- * per process, forces one of them.
+ * per process, forces one of them. Causal problems order their row blocks
+ * longest-first across the K/V heads that share an XCD; ATTN_CHUNK_KV_MIB
+ * (default 4, read once) bounds the K/V bytes of those heads.
  *
  * Errors. The return value is an attn_status. All argument checks run before
  * any HIP call. Device-resident values cannot be checked without a sync, so:

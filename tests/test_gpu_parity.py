@@ -67,12 +67,17 @@ DENSE_CASES = [
     (3, 2, 2, 1, 50, 64, "bf16", False, None),          # single query row
     (1, 1, 1, 513, 1025, 128, "bf16", False, None),
     (1, 1, 1, 700, 1500, 64, "bf16", True, (1000, 1500)),
-    # d=128 with Lk >= 8192 runs the 8-wave schedule
+    # d=128 with Lk >= 4096 runs the 8-wave schedule
     (1, 2, 2, 300, 8200, 128, "bf16", False, None),
     (1, 4, 2, 257, 8193, 128, "bf16", True, None),
     (1, 2, 1, 100, 9000, 128, "bf16", False, (5000, 9000)),
     (1, 1, 1, 8262, 8262, 128, "bf16", True, None),
     (3, 2, 2, 64, 8250, 128, "bf16", False, None),
+    (1, 2, 2, 4096, 4096, 128, "bf16", True, None),
+    (2, 3, 1, 1000, 4100, 128, "bf16", True, (3000, 4100)),
+    # causal with many heads per XCD chunk: row blocks ordered across heads
+    (3, 6, 2, 700, 700, 128, "bf16", True, None),
+    (5, 4, 4, 260, 260, 64, "bf16", True, None),
 ]
 
 

@@ -11,7 +11,7 @@
 namespace attn {
 hipError_t launch_bf16(const Params& p, int D, bool causal, hipStream_t stream);
 hipError_t launch_f32(const Params& p, int D, bool causal, hipStream_t stream);
-bool plan_bf16(Params& p, int D);
+bool plan_bf16(Params& p, int D, bool causal);
 }  // namespace attn
 
 namespace {
@@ -61,7 +61,7 @@ int check_and_launch(const void* q, const void* k, const void* v, void* o,
   const bool is_causal = causal != 0;
   hipError_t err;
   if (dtype == ATTN_BF16) {
-    if (!attn::plan_bf16(p, d)) return ATTN_EINVAL;
+    if (!attn::plan_bf16(p, d, is_causal)) return ATTN_EINVAL;
     err = attn::launch_bf16(p, d, is_causal, (hipStream_t)stream);
   } else {
     const int64_t T = (int64_t)NB * H * ((Lq + kF32Rows - 1) / kF32Rows);

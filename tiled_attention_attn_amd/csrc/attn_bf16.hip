@@ -41,6 +41,7 @@
 #include <stdint.h>
 #include <stdlib.h>
 
+#include <algorithm>
 #include <type_traits>
 
 #include "attn_params.h"
@@ -172,13 +173,20 @@ __global__ __launch_bounds__(W * 64, W == 4 ? 2 : 1) void attn_fwd_bf16_kernel(c
   const int HPG = p.H / p.Hkv;
   int bgrp, h, mt;
   if (p.cand2user == nullptr) {
-    // dense: ((b * Hkv + g) * nMT + mt') * HPG + hq; causal runs heavy tiles first
-    int hq = L % HPG;
-    int r = L / HPG;
-    int mtr = r % p.nMT;
-    r /= p.nMT;
-    int g = r % p.Hkv;
-    bgrp = r / p.Hkv;
+    // dense: chunks of p.units (batch group, K/V head) units, ordered inside as
+    // (mt' * units + unit) * HPG + hq, so a causal chunk runs the heaviest row
+    // block of every unit first (longest-first over the XCD's share); the
+    // last chunk may hold fewer units.
+    const int per_chunk = p.units * p.nMT * HPG;
+    const int sup = L / per_chunk;
+    const int nu = min(p.units, p.NG * p.Hkv - sup * p.units);
+    const int r0 = L - sup * per_chunk;
+    const int hq = r0 % HPG;
+    const int r = r0 / HPG;
+    const int unit = sup * p.units + r % nu;
+    const int mtr = r / nu;
+    const int g = unit % p.Hkv;
+    bgrp = unit / p.Hkv;
     h = g * HPG + hq;
     mt = CAUSAL ? (p.nMT - 1 - mtr) : mtr;
   } else {
@@ -777,7 +785,7 @@ hipError_t launch_bf16(const Params& p, int D, bool causal, hipStream_t stream) 
 
 // Long d=128 key sequences run the 8-wave ping-pong schedule; shorter ones
 // (and d=64, whose softmax outweighs its MFMA work) the 4-wave schedule.
-constexpr int kPingPongMinKeys = 8192;
+constexpr int kPingPongMinKeys = 4096;
 
 // Work decomposition for the bf16 kernel: query rows are split into wave
 // blocks of kRowsPerWave; a workgroup takes `waves` consecutive blocks of one
@@ -794,7 +802,18 @@ static int waves_override() {
   return v;
 }
 
-bool plan_bf16(Params& p, int D) {
+// K/V bytes the units of one causal chunk may span (ATTN_CHUNK_KV_MIB
+// overrides, for tuning).
+int64_t chunk_kv_bytes() {
+  static const int64_t v = [] {
+    const char* e = getenv("ATTN_CHUNK_KV_MIB");
+    const long m = (e != nullptr) ? strtol(e, nullptr, 10) : 0;
+    return (int64_t)(m > 0 ? m : 4) << 20;   // one XCD's L2 (measured best of 1..16 MiB)
+  }();
+  return v;
+}
+
+bool plan_bf16(Params& p, int D, bool causal) {
   // K/V of one (batch, head) are addressed through 32-bit buffer offsets;
   // the last tile may run up to 64 rows past Lk.
   const int64_t kv_row_bytes = (int64_t)(p.q_offsets != nullptr ? p.Hkv : 1) * D * 2;
@@ -822,7 +841,18 @@ bool plan_bf16(Params& p, int D) {
   // Keep all tiles that read one K/V head on one XCD (its L2), so each K/V
   // head streams from memory into a single L2. Broadcast tiles of one head
   // are ordered by candidate group; runs of 16 groups usually share a user.
-  p.chunk = (p.cand2user == nullptr) ? p.nMT * (p.H / p.Hkv) : 16;
+  // Causal dense problems whose K/V heads are too few tiles to fill an XCD
+  // share several heads per chunk, ordered longest-first inside it: up to an
+  // XCD's share of the units, as long as their K/V (read concurrently) stay
+  // within kChunkKVBytes, so that K/V re-reads keep hitting the caches.
+  p.units = 1;
+  if (causal && p.cand2user == nullptr) {
+    const int64_t share = (p.NG * (int64_t)p.Hkv + 7) / 8;
+    const int64_t kv_unit = (int64_t)p.Lk * D * 2 * 2;   // K and V of one unit (at most)
+    const int64_t fit = kv_unit > 0 ? chunk_kv_bytes() / kv_unit : share;
+    p.units = (int)std::max<int64_t>(1, std::min(share, fit));
+  }
+  p.chunk = (p.cand2user == nullptr) ? p.units * p.nMT * (p.H / p.Hkv) : 16;
   return true;
 }
 

@@ -29,6 +29,8 @@ struct Params {
   int NG;     // batch groups = ceil(NB / G)
   int T;      // total workgroups
   int chunk;  // logical tiles kept together on one XCD (0 = no remap)
+  int units;  // dense: (batch group, K/V head) units per chunk; causal tiles of a
+              // chunk run row block by row block across its units (heaviest first)
   int waves;  // waves per workgroup of the bf16 kernel (4 or 8)
 };
 
