@@ -539,23 +539,24 @@ __global__ __launch_bounds__(W * 64, W == 4 ? 2 : 1) void attn_fwd_bf16_kernel(c
           }
         return (ps4[0] + ps4[1]) + (ps4[2] + ps4[3]);
       };
-      // Fast path (8-wave schedule, which has the registers to keep the raw
-      // scores beside P): keep the current reference. Every probability is
-      // at most its lane's partial sum, so if no lane's sum exceeds 2^kTau
-      // the tile is done without forming the row max and O needs no rescale.
-      // A -inf reference (first tile of a pass) gives inf or NaN sums and
-      // falls through, as does a row whose scores grew.
-      if constexpr (W == 8) {
+      // Fast path (wherever the registers allow keeping the raw scores beside
+      // P: the 8-wave schedule, and d = 64): keep the current reference. Every
+      // probability is at most its lane's partial sum, so if no lane's sum
+      // exceeds 2^kTau the tile is done without forming the row max and O
+      // needs no rescale. A -inf reference (first tile of a pass) gives inf
+      // or NaN sums and falls through, as does a row whose scores grew.
+      constexpr bool kFast = W == 8 || D == 64;
+      if constexpr (kFast) {
         const float rs = exps(m_run[qb] * c);
         if (__ballot(!(rs <= kSumLimit)) == 0) {
           l_run[qb] += rs;
           return 1.f;
         }
       }
-      // Row max (max chains, then one exchange between the lane halves). The
-      // 8-wave schedule gets here only when the fast path failed and moves
-      // the reference to the max; the 4-wave one moves it when some row's max
-      // grew by more than 2^kTau.
+      // Row max (max chains, then one exchange between the lane halves). With
+      // the fast path this runs only when it failed and moves the reference
+      // to the max; otherwise the reference moves when some row's max grew by
+      // more than 2^kTau.
       float pm[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) pm[j] = vmax(sacc[0][2 * j], sacc[0][2 * j + 1]);
@@ -569,7 +570,7 @@ __global__ __launch_bounds__(W * 64, W == 4 ? 2 : 1) void attn_fwd_bf16_kernel(c
       const float m_old = m_run[qb];
       const float m_new = vmax(m_old, mx);
       bool move = true;
-      if constexpr (W != 8) move = __ballot((m_new - m_old) * c > kTau) != 0;  // NaN: false
+      if constexpr (!kFast) move = __ballot((m_new - m_old) * c > kTau) != 0;  // NaN: false
       const float m_use = move ? m_new : m_old;
       const float alpha = (m_old == m_use || m_use == -INFINITY)
                               ? 1.f : __builtin_amdgcn_exp2f((m_old - m_use) * c);
