@@ -33,6 +33,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         raise RuntimeError(
             f"{path} is missing: build it with `python -m tiled_attention_attn_amd.build` "
             "(hipcc, gfx950). There is no fallback implementation.")
+    # torch ships its own HIP runtime under the same soname as the system one
+    # this library links; whichever loads first serves the process. Loading
+    # torch first keeps torch on its own runtime and this library on the same
+    # one (loaded the other way round, kernel launches failed).
+    import torch  # noqa: F401
     lib = ctypes.CDLL(path)
     vp, i32, f32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
     lib.attn_fwd.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, vp, f32, i32, vp]

@@ -382,81 +382,11 @@ __global__ __launch_bounds__(W * 64, W == 4 ? 2 : 1) void attn_fwd_bf16_kernel(c
     }
     bf16x8 pprev[kQB][PS];          // probabilities of the previous tile (PV operand)
 
-    // S^T(t) = K(t) . Q^T for both blocks; each K operand feeds two MFMAs and
-    // the next step's operands are read ahead.
-    auto qk = [&](f32x16 (&sacc)[kQB][KB], const u32x4* kb) __attribute__((always_inline)) {
-      const u32x4* kl = kb + col * KPITCH + half;
-      // all K operands are named up front; the scheduling groups below decide
-      // how far ahead of its MFMA each read is issued
-      bf16x8 a[QS][KB];
-#pragma unroll
-      for (int kbk = 0; kbk < KB; ++kbk)
-#pragma unroll
-        for (int qb = 0; qb < kQB; ++qb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) sacc[qb][kbk][i] = 0.f;
-#pragma unroll
-      for (int s = 0; s < QS; ++s)
-#pragma unroll
-        for (int kbk = 0; kbk < KB; ++kbk)
-          a[s][kbk] = __builtin_bit_cast(bf16x8, kl[kbk * 32 * KPITCH + 2 * s]);
-#pragma unroll
-      for (int s = 0; s < QS; ++s) {
-#pragma unroll
-        for (int kbk = 0; kbk < KB; ++kbk)
-#pragma unroll
-          for (int qb = 0; qb < kQB; ++qb)
-            sacc[qb][kbk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[s][kbk], qreg[qb][s],
-                                                                    sacc[qb][kbk], 0, 0, 0);
-      }
-      // Keep PF K operand reads in flight ahead of the MFMAs.
-      constexpr int R = QS * KB, PF0 = W == 8 ? 2 : 4, PF = R < PF0 ? R : PF0;
-      __builtin_amdgcn_sched_group_barrier(kSchedDSRead, PF, 0);
-#pragma unroll
-      for (int i = 0; i < R - PF; ++i) {
-        __builtin_amdgcn_sched_group_barrier(kSchedMFMA, kQB, 0);
-        __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 1, 0);
-      }
-      __builtin_amdgcn_sched_group_barrier(kSchedMFMA, kQB * PF, 0);
-    };
-    // O^T += V^T . P^T; V^T operands through the transposing LDS read:
-    // source role il addresses V[row][dcol .. dcol+3], result lane il then
-    // holds V[key0 + s][dbase + il] for s = 0..3. Next step read ahead.
+    // V^T operands come through the transposing LDS read: source role il
+    // addresses V[row][dcol .. dcol+3], result lane il then holds
+    // V[key0 + s][dbase + il] for s = 0..3.
     const int vlane = (half * 4 + (il >> 2)) * (VPITCH * 16) + ((grp & 1) * 16 + 4 * (il & 3)) * 2;
-    auto pv = [&](const u32x4* vb32) __attribute__((always_inline)) {
-      const LDS_AS char* vb = (const LDS_AS char*)vb32 + vlane;
-      auto vread = [&](int ps, int b) -> bf16x8 {
-        const int o1 = (ps * 16) * (VPITCH * 16) + b * 64;
-        const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)(vb + o1));
-        const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-            (LDS_AS bf16x4*)(vb + o1 + 8 * (VPITCH * 16)));
-        return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-      };
-      constexpr int STEPS = PS * DB;
-      constexpr int AHEAD = 2;                // steps of V reads kept in flight
-      bf16x8 a[AHEAD];
-#pragma unroll
-      for (int i = 0; i < AHEAD - 1; ++i) a[i] = vread(i / DB, i % DB);
-#pragma unroll
-      for (int step = 0; step < STEPS; ++step) {
-        const int ps = step / DB, b = step % DB;
-        const int nxt = step + AHEAD - 1;
-        if (nxt < STEPS) a[nxt % AHEAD] = vread(nxt / DB, nxt % DB);
-#pragma unroll
-        for (int qb = 0; qb < kQB; ++qb)
-          oacc[qb][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[step % AHEAD], pprev[qb][ps],
-                                                                oacc[qb][b], 0, 0, 0);
-      }
-      // Keep AHEAD steps (2 transposing reads each) in flight ahead of the MFMAs.
-      __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 2 * AHEAD, 0);
-#pragma unroll
-      for (int i = 0; i < STEPS - AHEAD; ++i) {
-        __builtin_amdgcn_sched_group_barrier(kSchedMFMA, kQB, 0);
-        __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 2, 0);
-      }
-      __builtin_amdgcn_sched_group_barrier(kSchedMFMA, AHEAD * kQB, 0);
-    };
-    // Both products of one half-step in a single instruction stream: first
+    // Both products of one step in a single instruction stream: first
     // O += P(t-1) V(t-1), then S(t) = K(t) Q^T, so P(t-1) is dead before S(t)
     // is born. Operand reads run two MFMAs ahead through the whole stream
     // (a V^T operand is two reads, a K operand one), so the matrix pipe does
@@ -539,24 +469,20 @@ __global__ __launch_bounds__(W * 64, W == 4 ? 2 : 1) void attn_fwd_bf16_kernel(c
           }
         return (ps4[0] + ps4[1]) + (ps4[2] + ps4[3]);
       };
-      // Fast path (wherever the registers allow keeping the raw scores beside
-      // P: the 8-wave schedule, and d = 64): keep the current reference. Every
-      // probability is at most its lane's partial sum, so if no lane's sum
-      // exceeds 2^kTau the tile is done without forming the row max and O
-      // needs no rescale. A -inf reference (first tile of a pass) gives inf
-      // or NaN sums and falls through, as does a row whose scores grew.
-      constexpr bool kFast = W == 8 || D == 64;
-      if constexpr (kFast) {
+      // Fast path: keep the current reference. Every probability is at most
+      // its lane's partial sum, so if no lane's sum exceeds 2^kTau the tile
+      // is done without forming the row max and O needs no rescale. A -inf
+      // reference (first tile of a pass) gives inf or NaN sums and falls
+      // through, as does a row whose scores grew.
+      {
         const float rs = exps(m_run[qb] * c);
         if (__ballot(!(rs <= kSumLimit)) == 0) {
           l_run[qb] += rs;
           return 1.f;
         }
       }
-      // Row max (max chains, then one exchange between the lane halves). With
-      // the fast path this runs only when it failed and moves the reference
-      // to the max; otherwise the reference moves when some row's max grew by
-      // more than 2^kTau.
+      // Exact path: row max (max chains, then one exchange between the lane
+      // halves); the reference moves to it.
       float pm[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) pm[j] = vmax(sacc[0][2 * j], sacc[0][2 * j + 1]);
@@ -568,10 +494,7 @@ __global__ __launch_bounds__(W * 64, W == 4 ? 2 : 1) void attn_fwd_bf16_kernel(c
                       vmax(vmax(pm[4], pm[5]), vmax(pm[6], pm[7])));
       mx = halves_max(mx);
       const float m_old = m_run[qb];
-      const float m_new = vmax(m_old, mx);
-      bool move = true;
-      if constexpr (!kFast) move = __ballot((m_new - m_old) * c > kTau) != 0;  // NaN: false
-      const float m_use = move ? m_new : m_old;
+      const float m_use = vmax(m_old, mx);
       const float alpha = (m_old == m_use || m_use == -INFINITY)
                               ? 1.f : __builtin_amdgcn_exp2f((m_old - m_use) * c);
       m_run[qb] = m_use;
@@ -679,9 +602,13 @@ __global__ __launch_bounds__(W * 64, W == 4 ? 2 : 1) void attn_fwd_bf16_kernel(c
 
     } else {
     // ---- software-pipelined tile loop ----------------------------------------
-    // Iteration t reads K(t) and V(t-1) while K(t+1) and V(t) stream into the
-    // other buffers; the loop is unrolled by two so every access names one
-    // fixed LDS buffer.
+    // Iteration t runs the MFMA stream O += P(t-1) V(t-1), S(t) = K(t) Q^T,
+    // then the softmax of S(t), while K(t+1) and V(t) stream into the other
+    // buffers; the two workgroups on a SIMD pair overlap each other's MFMA
+    // and softmax work. As in the 8-wave loop, P starts zeroed with V(0) in
+    // the buffer the empty first PV reads, and the score tile after the last
+    // is computed and never read. The loop is unrolled by two so every access
+    // names one fixed LDS buffer.
     f32x16 sacc[kQB][KB];
     auto iteration = [&](auto parity, int t) {
       constexpr int PAR = decltype(parity)::value;
@@ -692,18 +619,10 @@ __global__ __launch_bounds__(W * 64, W == 4 ? 2 : 1) void attn_fwd_bf16_kernel(c
       if (t + 1 < ntiles) load_k(knext, t + 1);
       if (t < ntiles) load_v(vcur, t);
       if (active) {
-        const bool do_pv = t >= 1 && t <= my_total;
         const bool do_sm = t < my_total;
-        // Raise this wave's issue priority while it feeds the MFMA pipe, so
-        // the other wave on the SIMD fills the gaps with its softmax VALU.
-        if (do_sm) {
+        if (t <= my_total) {
           __builtin_amdgcn_s_setprio(1);
-          qk(sacc, kcur);
-          __builtin_amdgcn_s_setprio(0);
-        }
-        if (do_pv) {
-          __builtin_amdgcn_s_setprio(1);
-          pv(vprev);
+          pvqk(sacc, kcur, vprev);
           __builtin_amdgcn_s_setprio(0);
         }
         if (do_sm) {
@@ -721,7 +640,10 @@ __global__ __launch_bounds__(W * 64, W == 4 ? 2 : 1) void attn_fwd_bf16_kernel(c
       wait_vm();
       __syncthreads();
     };
+#pragma unroll
+    for (int ps = 0; ps < PS; ++ps) pprev[0][ps] = bf16x8{};
     load_k(kbuf0, 0);
+    load_v(vbuf1, 0);
     wait_vm();
     __syncthreads();
     int t = 0;
