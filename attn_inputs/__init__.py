@@ -69,6 +69,7 @@ class AttnInputs:
                kv_len [B_u] or None.
     Jagged:    q [total_q,H,d], k/v [total_kv,Hkv,d], q_offsets and
                kv_offsets int32 [B+1].
+    Block-sparse: dense q/k/v plus block_mask uint8 [1 or H, nQB, nKB] and blk.
     """
     q: np.ndarray
     k: np.ndarray
@@ -79,6 +80,8 @@ class AttnInputs:
     cand2user: np.ndarray | None = None
     q_offsets: np.ndarray | None = None
     kv_offsets: np.ndarray | None = None
+    block_mask: np.ndarray | None = None
+    blk: int = 0
     scale: float | None = None
     meta: dict = field(default_factory=dict)
 
@@ -156,9 +159,39 @@ def make_jagged(B, H, Hkv, d, *, len_range=None, lengths=None, kv_lengths=None, 
                                 max_Lk=int(kv_lengths.max(initial=0))))
 
 
+def block_pattern(nqb: int, nkb: int, window: int, n_global: int) -> np.ndarray:
+    """Fixed block pattern [1, nqb, nkb]: query block qb keeps key blocks
+    qb-window+1 .. qb (a local band) and the first n_global key blocks."""
+    qb = np.arange(nqb)[:, None]
+    kb = np.arange(nkb)[None, :]
+    keep = ((kb <= qb) & (kb > qb - window)) | (kb < n_global)
+    return keep.astype(np.uint8)[None]
+
+
+def make_block_sparse(B, H, Hkv, Lq, Lk, d, blk, *, dtype="bf16", causal=False, seed=0,
+                      window=None, n_global=0, density=None, mask_heads=1,
+                      kv_len_range=None, scale=None) -> AttnInputs:
+    """Block-sparse problem: a dense problem plus a block mask, either the fixed
+    local-window + global pattern (window given) or iid blocks kept with
+    probability `density` drawn on the integer stream."""
+    w = make_dense(B, H, Hkv, Lq, Lk, d, dtype=dtype, causal=causal, seed=seed,
+                   kv_len_range=kv_len_range, scale=scale)
+    nqb, nkb = -(-Lq // blk), -(-Lk // blk)
+    if window is not None:
+        mask = np.repeat(block_pattern(nqb, nkb, window, n_global), mask_heads, axis=0)
+    else:
+        r = _gen(seed, STREAM_INT + 1).random((mask_heads, nqb, nkb))
+        mask = (r < density).astype(np.uint8)
+    w.block_mask, w.blk = mask, blk
+    w.meta = dict(kind="block_sparse", B=B, H=H, Hkv=Hkv, Lq=Lq, Lk=Lk, d=d, blk=blk,
+                  mask_heads=mask_heads, window=window, n_global=n_global, density=density)
+    return w
+
+
 # The workloads the method is measured on: tiny fp32 parity case, dense causal,
-# in-kernel broadcast, kv_len-masked, long-sequence GQA causal, and jagged
-# causal self-attention over sequences of uniformly drawn lengths.
+# in-kernel broadcast, kv_len-masked, long-sequence GQA causal, jagged causal
+# self-attention over sequences of uniformly drawn lengths, and fixed-block
+# sparse causal attention (a local band of 8 blocks plus 1 global block).
 WORKLOADS = {
     "fp32_tiny": dict(kind="dense", B=1, H=1, Hkv=1, Lq=128, Lk=128, d=64, dtype="f32",
                       causal=False),
@@ -172,6 +205,9 @@ WORKLOADS = {
                               dtype="bf16", causal=True),
     "jagged_causal_B32": dict(kind="jagged", B=32, H=16, Hkv=16, d=128, len_range=(256, 4096),
                               dtype="bf16", causal=True),
+    "block_sparse_L16384": dict(kind="block_sparse", B=1, H=16, Hkv=16, Lq=16384, Lk=16384,
+                                d=128, blk=256, window=8, n_global=1, dtype="bf16",
+                                causal=True),
 }
 
 
@@ -183,5 +219,8 @@ def make_workload(name: str, seed: int = 0) -> AttnInputs:
                           w.pop("d"), seed=seed, **w)
     if kind == "jagged":
         return make_jagged(w.pop("B"), w.pop("H"), w.pop("Hkv"), w.pop("d"), seed=seed, **w)
+    if kind == "block_sparse":
+        return make_block_sparse(w.pop("B"), w.pop("H"), w.pop("Hkv"), w.pop("Lq"), w.pop("Lk"),
+                                 w.pop("d"), w.pop("blk"), seed=seed, **w)
     return make_bcast(w.pop("B_c"), w.pop("B_u"), w.pop("H"), w.pop("Hkv"), w.pop("Lq"),
                       w.pop("Lk"), w.pop("d"), seed=seed, **w)

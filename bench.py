@@ -52,6 +52,8 @@ def pairs(w: ai.AttnInputs) -> int:
         return total * H
     NB, H, Lq, _ = w.q.shape
     Lk = w.k.shape[2]
+    if w.block_mask is not None:
+        return _block_sparse_pairs(w)
     kv_b = w.kv_len if w.cand2user is None or w.kv_len is None else w.kv_len[w.cand2user]
     total = 0
     for b in range(NB):
@@ -64,6 +66,26 @@ def pairs(w: ai.AttnInputs) -> int:
     return total * H
 
 
+def _block_sparse_pairs(w: ai.AttnInputs) -> int:
+    """Allowed (query, key) pairs under the block mask, causal and kv_len, all heads."""
+    NB, H, Lq, _ = w.q.shape
+    Lk, blk, bm = w.k.shape[2], w.blk, w.block_mask
+    total = 0
+    for b in range(NB):
+        n = Lk if w.kv_len is None else int(min(max(w.kv_len[b], 0), Lk))
+        for hm in range(bm.shape[0]):
+            heads = H if bm.shape[0] == 1 else 1
+            for qb in range(bm.shape[1]):
+                i = np.arange(qb * blk, min((qb + 1) * blk, Lq))
+                for kb in np.nonzero(bm[hm, qb])[0]:
+                    lo, hi = kb * blk, min((kb + 1) * blk, n)
+                    if hi <= lo:
+                        continue
+                    top = np.minimum(i + 1, hi) if w.causal else np.full(len(i), hi)
+                    total += heads * int(np.maximum(top - lo, 0).sum())
+    return total
+
+
 def algorithmic_flops(w) -> int:
     return 4 * w.q.shape[-1] * pairs(w)
 
@@ -74,6 +96,11 @@ def algorithmic_bytes(w) -> int:
     if w.q_offsets is not None:   # jagged: every packed K/V token is read once
         return 2 * w.q.size * esz + 2 * w.k.size * esz + 4 * (w.q_offsets.size + w.kv_offsets.size)
     NKV, Hkv, Lk, d = w.k.shape
+    if w.block_mask is not None:   # K/V blocks that some query block reads, plus the mask
+        nkb = w.block_mask.shape[2]
+        used = w.block_mask.any(axis=(0, 1))
+        rows = sum(min((kb + 1) * w.blk, Lk) - kb * w.blk for kb in range(nkb) if used[kb])
+        return 2 * w.q.size * esz + 2 * NKV * Hkv * rows * d * esz + w.block_mask.size
     kv_rows = 0
     for u in range(NKV):
         kv_rows += Lk if w.kv_len is None else int(min(max(w.kv_len[u], 0), Lk))
@@ -106,11 +133,15 @@ class Runner:
         self.c2u = None if w.cand2user is None else torch.from_numpy(w.cand2user).cuda()
         self.qo = None if w.q_offsets is None else torch.from_numpy(w.q_offsets).cuda()
         self.ko = None if w.kv_offsets is None else torch.from_numpy(w.kv_offsets).cuda()
+        self.bm = None if w.block_mask is None else torch.from_numpy(w.block_mask).cuda()
         import tiled_attention_attn_amd as taa
         self.taa = taa
 
     def __call__(self):
-        if self.qo is not None:
+        if self.bm is not None:
+            self.taa.attn_fwd_block_sparse(self.q, self.k, self.v, self.bm, self.w.blk, self.o,
+                                           causal=self.w.causal, kv_len=self.kv)
+        elif self.qo is not None:
             self.taa.attn_fwd_jagged(self.q, self.k, self.v, self.qo, self.ko,
                                      self.w.meta["max_Lq"], self.w.meta["max_Lk"], self.o,
                                      causal=self.w.causal)
@@ -154,10 +185,14 @@ def sampled_error(run: Runner, seed: int = 1, nrows: int = 4) -> float:
         u = b if w.cand2user is None else int(w.cand2user[b])
         g = h // (H // w.k.shape[1])
         kvl = None if w.kv_len is None else w.kv_len[u:u + 1]
-        ref = oracle.attention_rows(ai.to_f64(w.q[b:b + 1, h:h + 1], w.dtype),
-                                    ai.to_f64(w.k[u:u + 1, g:g + 1], w.dtype),
-                                    ai.to_f64(w.v[u:u + 1, g:g + 1], w.dtype), 0, 0, rows,
-                                    causal=w.causal, kv_len=kvl)
+        qf, kf, vf = (ai.to_f64(x, w.dtype) for x in
+                      (w.q[b:b + 1, h:h + 1], w.k[u:u + 1, g:g + 1], w.v[u:u + 1, g:g + 1]))
+        if w.block_mask is not None:
+            bm = w.block_mask[0:1] if w.block_mask.shape[0] == 1 else w.block_mask[h:h + 1]
+            ref = oracle.attention_block_sparse_rows(qf, kf, vf, bm, w.blk, 0, 0, rows,
+                                                     causal=w.causal, kv_len=kvl)
+        else:
+            ref = oracle.attention_rows(qf, kf, vf, 0, 0, rows, causal=w.causal, kv_len=kvl)
         worst = max(worst, float(np.abs(got - ref).max()))
     return worst
 

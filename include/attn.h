@@ -123,10 +123,34 @@ int attn_fwd_jagged(const void* q, const void* k, const void* v, void* o,
                     int B, int H, int Hkv, int max_Lq, int max_Lk, int d,
                     int causal, float scale, int dtype, void* stream);
 
+/*
+ * Fixed-block sparse attention forward: queries and keys are cut into blocks
+ * of blk rows, and query block qb attends only to the key blocks kb with
+ * block_mask[hm, qb, kb] != 0. The pages give this operation only as an
+ * article title ("Meta 造了个 Triton 扩展 TLX..." page, link list, "TLX Block
+ * Attention: ... Fixed-Block Sparse Self-Attention"); the reading here is the
+ * plain one: a boolean block mask on top of the dense path's masks.
+ *   q, k, v, o, B, H, Hkv, Lq, Lk, d, causal, kv_len, scale, dtype, stream
+ *              as attn_fwd (dense layout)
+ *   block_mask [mask_heads, ceil(Lq/blk), ceil(Lk/blk)] uint8 in device
+ *              memory; nonzero = the block pair is attended
+ *   mask_heads 1 (one mask for all heads and batch entries) or H (one per head)
+ *   blk        block size, a positive multiple of 128 (a workgroup's query
+ *              rows never straddle a block); ceil(Lk/blk) <= 1024
+ * A key block left out is never loaded; rows whose blocks leave no valid key
+ * are written as 0. Errors: ATTN_EINVAL also for a bad blk / mask_heads, a
+ * NULL block_mask, or more than 1024 key blocks; otherwise as attn_fwd.
+ */
+int attn_fwd_block_sparse(const void* q, const void* k, const void* v, void* o,
+                          const uint8_t* block_mask, int mask_heads, int blk,
+                          int B, int H, int Hkv, int Lq, int Lk, int d,
+                          int causal, const int32_t* kv_len, float scale,
+                          int dtype, void* stream);
+
 /* Static, human-readable text for a status code (never NULL). */
 const char* attn_strerror(int status);
 
-/* ABI version: major * 100 + minor (101: attn_fwd_jagged added). */
+/* ABI version: major * 100 + minor (101: attn_fwd_jagged; 102: attn_fwd_block_sparse). */
 int attn_version(void);
 
 #ifdef __cplusplus

@@ -33,6 +33,13 @@ q_offsets[b+1]-1 and key tokens kv_offsets[b] .. kv_offsets[b+1]-1, and is
 the definition above applied to its own slices (causal top-left in local
 indices; no keys gives zero rows).
 
+Fixed-block sparse attention: the same page lists an article on a
+fixed-block sparse self-attention kernel, again title only. The plain
+reading: a boolean block mask [Hm, ceil(Lq/blk), ceil(Lk/blk)] (Hm = 1 shared
+by all heads, or one per head) removes the key blocks a query block does not
+attend to; key j is allowed for query i only where mask[h, i // blk,
+j // blk] is set, on top of the causal and kv_len masks.
+
 Readings where the pages are silent (each is also listed with the design
 notes): scale defaults to 1/sqrt(d); the mask is additive -inf; causal is
 top-left (key j allowed iff j <= i); kv_len is one value per K/V batch entry,
@@ -53,7 +60,8 @@ import math
 import numpy as np
 
 __all__ = ["attention", "attention_rows", "attention_bcast", "attention_jagged",
-           "attention_jagged_rows", "probabilities"]
+           "attention_jagged_rows", "attention_block_sparse", "attention_block_sparse_rows",
+           "probabilities"]
 
 
 def _default_scale(d: int, scale) -> float:
@@ -63,8 +71,12 @@ def _default_scale(d: int, scale) -> float:
     return float(scale)
 
 
-def _allowed(rows: np.ndarray, Lk: int, causal: bool, kv_len_b) -> np.ndarray:
-    """Boolean [len(rows), Lk]: which (query i, key j) pairs are not masked."""
+def _allowed(rows: np.ndarray, Lk: int, causal: bool, kv_len_b, block=None) -> np.ndarray:
+    """Boolean [len(rows), Lk]: which (query i, key j) pairs are not masked.
+
+    block = (mask [nQB, nKB], blk) additionally allows (i, j) only where
+    mask[i // blk, j // blk] is set.
+    """
     j = np.arange(Lk)[None, :]
     i = np.asarray(rows)[:, None]
     ok = np.ones((len(rows), Lk), dtype=bool)
@@ -73,6 +85,9 @@ def _allowed(rows: np.ndarray, Lk: int, causal: bool, kv_len_b) -> np.ndarray:
         ok &= j < n
     if causal:
         ok &= j <= i
+    if block is not None:
+        bm, blk = block
+        ok &= np.asarray(bm, dtype=bool)[i // blk, j // blk]
     return ok
 
 
@@ -88,9 +103,9 @@ def _softmax_rows(s: np.ndarray, ok: np.ndarray) -> np.ndarray:
     return np.divide(e, z, out=np.zeros_like(e), where=z > 0)
 
 
-def _head_rows(q_bh, k_bg, v_bg, rows, causal, kv_len_b, scale):
+def _head_rows(q_bh, k_bg, v_bg, rows, causal, kv_len_b, scale, block=None):
     s = scale * (q_bh[rows] @ k_bg.T)          # [R, Lk] scores
-    p = _softmax_rows(s, _allowed(rows, k_bg.shape[0], causal, kv_len_b))
+    p = _softmax_rows(s, _allowed(rows, k_bg.shape[0], causal, kv_len_b, block))
     return p @ v_bg, p
 
 
@@ -210,4 +225,43 @@ def attention_jagged_rows(q, k, v, q_offsets, kv_offsets, b, h, rows, *, causal=
     out, _ = _head_rows(q_bh, np.asarray(k[ks:ks + lk, g], np.float64),
                         np.asarray(v[ks:ks + lk, g], np.float64), rows, causal, None,
                         _default_scale(d, scale))
+    return out
+
+
+def _block_for_head(block_mask, blk, h):
+    bm = np.asarray(block_mask)
+    return (bm[0] if bm.shape[0] == 1 else bm[h]), int(blk)
+
+
+def attention_block_sparse(q, k, v, block_mask, blk, *, causal=False, kv_len=None, scale=None):
+    """Fixed-block sparse attention, float64: dense attention with key j allowed for
+    query i only where block_mask[h, i // blk, j // blk] is set.
+
+    q [B,H,Lq,d]; k, v [B,Hkv,Lk,d]; block_mask [1 or H, ceil(Lq/blk), ceil(Lk/blk)].
+    """
+    q, k, v = (np.asarray(x, np.float64) for x in (q, k, v))
+    B, H, Lq, d = q.shape
+    Hkv, Lk = k.shape[1], k.shape[2]
+    group = H // Hkv
+    sc = _default_scale(d, scale)
+    o = np.zeros((B, H, Lq, d))
+    rows = np.arange(Lq)
+    for b in range(B):
+        kvl = None if kv_len is None else kv_len[b]
+        for h in range(H):
+            g = h // group
+            o[b, h], _ = _head_rows(q[b, h], k[b, g], v[b, g], rows, causal, kvl, sc,
+                                    _block_for_head(block_mask, blk, h))
+    return o
+
+
+def attention_block_sparse_rows(q, k, v, block_mask, blk, b, h, rows, *, causal=False,
+                                kv_len=None, scale=None):
+    """Rows o[b, h, rows, :] of the block-sparse output (sampled checks at full size)."""
+    H, Hkv = q.shape[1], k.shape[1]
+    g = h // (H // Hkv)
+    kvl = None if kv_len is None else kv_len[b]
+    out, _ = _head_rows(np.asarray(q[b, h], np.float64), np.asarray(k[b, g], np.float64),
+                        np.asarray(v[b, g], np.float64), np.asarray(rows), causal, kvl,
+                        _default_scale(q.shape[3], scale), _block_for_head(block_mask, blk, h))
     return out

@@ -383,4 +383,104 @@ def pin_jagged_rows_subset(impl):
                 np.testing.assert_array_equal(part, full[qo[b] + np.array(rows), h])
 
 
+# --- fixed-block sparse -----------------------------------------------------------------
+
+def _block_mask(shape, seed, density=0.6):
+    m = (_rng(seed).random(shape) < density).astype(np.uint8)
+    return m
+
+
+def pin_block_sparse_all_ones_is_dense(impl):
+    """A mask with every block set is dense attention, bit for bit."""
+    q, k, v = _rand((2, 4, 9, 5), 80), _rand((2, 2, 11, 5), 81), _rand((2, 2, 11, 5), 82)
+    for causal in (False, True):
+        for kv in (None, np.array([11, 6])):
+            o = impl.attention_block_sparse(q, k, v, np.ones((1, 3, 3), np.uint8), 4,
+                                            causal=causal, kv_len=kv)
+            np.testing.assert_array_equal(o, impl.attention(q, k, v, causal=causal, kv_len=kv))
+
+
+def _brute_block(q, k, v, bm, blk, causal, scale):
+    """40-digit direct evaluation with the block condition written out."""
+    getcontext().prec = 40
+    B, H, Lq, d = q.shape
+    Hkv, Lk = k.shape[1], k.shape[2]
+    o = np.zeros(q.shape)
+    sc = Decimal(repr(scale))
+    for b in range(B):
+        for h in range(H):
+            g = (h * Hkv) // H
+            m = bm[0] if bm.shape[0] == 1 else bm[h]
+            for i in range(Lq):
+                ws, num = [], [Decimal(0)] * d
+                for j in range(Lk):
+                    if (causal and j > i) or not m[i // blk][j // blk]:
+                        continue
+                    s = sum(Decimal(repr(float(q[b, h, i, t]))) * Decimal(repr(float(k[b, g, j, t])))
+                            for t in range(d))
+                    w = (sc * s).exp()
+                    ws.append(w)
+                    for t in range(d):
+                        num[t] += w * Decimal(repr(float(v[b, g, j, t])))
+                z = sum(ws, Decimal(0))
+                if z > 0:
+                    o[b, h, i] = [float(x / z) for x in num]
+    return o
+
+
+def pin_block_sparse_brute_force(impl):
+    """Per-head masks (one query block with no key block at all), ragged edges: brute force."""
+    q, k, v = _rand((1, 2, 7, 3), 83), _rand((1, 1, 6, 3), 84), _rand((1, 1, 6, 3), 85)
+    bm = np.array([[[1, 0, 1], [0, 0, 0], [1, 1, 0], [0, 1, 1]],
+                   [[0, 1, 0], [1, 1, 1], [0, 0, 1], [1, 0, 0]]], np.uint8)
+    for causal in (False, True):
+        o = impl.attention_block_sparse(q, k, v, bm, 2, causal=causal, scale=0.9)
+        np.testing.assert_allclose(o, _brute_block(q, k, v, bm, 2, causal, 0.9), rtol=0,
+                                   atol=1e-12)
+
+
+def pin_block_sparse_is_gathered_keys(impl):
+    """Without causal masking, a query block attends exactly to the keys of its set blocks:
+    dense attention over those keys, gathered."""
+    blk = 3
+    q, k, v = _rand((1, 2, 9, 4), 86), _rand((1, 2, 12, 4), 87), _rand((1, 2, 12, 4), 88)
+    bm = np.array([[[1, 0, 0, 1], [0, 1, 1, 0], [1, 1, 1, 1]]], np.uint8)
+    o = impl.attention_block_sparse(q, k, v, bm, blk)
+    for qb in range(3):
+        keys = np.concatenate([np.arange(kb * blk, (kb + 1) * blk) for kb in range(4)
+                               if bm[0, qb, kb]])
+        ref = impl.attention(q[:, :, qb * blk:(qb + 1) * blk], k[:, :, keys], v[:, :, keys])
+        np.testing.assert_allclose(o[:, :, qb * blk:(qb + 1) * blk], ref, rtol=0, atol=1e-14)
+
+
+def pin_block_sparse_torch_sdpa(impl):
+    """PyTorch's float64 SDPA with the block mask expanded to a boolean element mask."""
+    import torch
+    import torch.nn.functional as F
+    blk, Lq, Lk = 4, 10, 14
+    q, k, v = _rand((2, 4, Lq, 8), 89), _rand((2, 2, Lk, 8), 90), _rand((2, 2, Lk, 8), 91)
+    bm = _block_mask((4, 3, 4), 92)
+    bm[:, :, 0] = 1          # every query block keeps a block (SDPA gives NaN rows otherwise)
+    for causal in (False, True):
+        allow = np.kron(bm, np.ones((blk, blk), np.uint8))[:, :Lq, :Lk].astype(bool)
+        if causal:
+            allow &= np.tril(np.ones((Lq, Lk), bool))[None]
+        ref = F.scaled_dot_product_attention(*(torch.from_numpy(x) for x in (q, k, v)),
+                                             attn_mask=torch.from_numpy(allow)[None], scale=0.35,
+                                             enable_gqa=True).numpy()
+        o = impl.attention_block_sparse(q, k, v, bm, blk, causal=causal, scale=0.35)
+        np.testing.assert_allclose(o, ref, rtol=0, atol=1e-13)
+
+
+def pin_block_sparse_shared_mask(impl):
+    """One mask for all heads equals that mask repeated per head; rows subsets agree."""
+    q, k, v = _rand((2, 3, 8, 4), 93), _rand((2, 3, 8, 4), 94), _rand((2, 3, 8, 4), 95)
+    bm = _block_mask((1, 4, 4), 96)
+    o1 = impl.attention_block_sparse(q, k, v, bm, 2, causal=True)
+    o2 = impl.attention_block_sparse(q, k, v, np.repeat(bm, 3, axis=0), 2, causal=True)
+    np.testing.assert_array_equal(o1, o2)
+    part = impl.attention_block_sparse_rows(q, k, v, bm, 2, 1, 2, [5, 0, 3], causal=True)
+    np.testing.assert_array_equal(part, o1[1, 2, [5, 0, 3]])
+
+
 ALL_PINS = [v for n, v in sorted(globals().items()) if n.startswith("pin_")]

@@ -27,14 +27,14 @@ def lib():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == ["attn_fwd", "attn_fwd_bcast", "attn_fwd_jagged",
-                                    "attn_strerror", "attn_version"]
+    assert declared_functions() == ["attn_fwd", "attn_fwd_bcast", "attn_fwd_block_sparse",
+                                    "attn_fwd_jagged", "attn_strerror", "attn_version"]
 
 
 def test_library_exports_every_declared_symbol(lib):
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert lib.attn_version() == 101
+    assert lib.attn_version() == 102
 
 
 def test_strerror_covers_every_status(lib):
@@ -127,3 +127,25 @@ def jagged(lib, qo=FAKE, ko=FAKE, B=2, H=2, Hkv=1, max_Lq=16, max_Lk=16, d=64, s
 ])
 def test_attn_fwd_jagged_argument_checks(lib, kwargs, status):
     assert jagged(lib, **kwargs) == status
+
+
+def sparse(lib, mask=FAKE, mask_heads=1, blk=128, B=1, H=2, Hkv=1, Lq=256, Lk=256, d=128,
+           dtype=taa.ATTN_BF16):
+    return lib.attn_fwd_block_sparse(FAKE, FAKE, FAKE, FAKE, mask, mask_heads, blk, B, H, Hkv, Lq,
+                                     Lk, d, 0, None, 0.0, dtype, None)
+
+
+@pytest.mark.parametrize("kwargs,status", [
+    (dict(blk=64), taa.ATTN_EINVAL),            # not a multiple of 128
+    (dict(blk=0), taa.ATTN_EINVAL),
+    (dict(blk=200), taa.ATTN_EINVAL),
+    (dict(mask_heads=3, H=4), taa.ATTN_EINVAL),
+    (dict(mask=None), taa.ATTN_EINVAL),
+    (dict(Lk=128 * 1024 + 1), taa.ATTN_EINVAL),   # 1025 key blocks
+    (dict(d=96), taa.ATTN_EUNSUPPORTED),
+    (dict(H=3, Hkv=2, mask_heads=3), taa.ATTN_EINVAL),
+    (dict(B=0, mask=None), taa.ATTN_OK),
+    (dict(Lq=0, mask=None), taa.ATTN_OK),
+])
+def test_attn_fwd_block_sparse_argument_checks(lib, kwargs, status):
+    assert sparse(lib, **kwargs) == status

@@ -36,6 +36,14 @@ MUTANTS = {
     "jagged_length_short": ("return start, max(int(offsets[b + 1]) - start, 0)",
                             "return start, max(int(offsets[b + 1]) - start - 1, 0)"),
     "jagged_global_causal": ("rows = np.arange(lq)\n", "rows = np.arange(qs, qs + lq)\n"),
+    "block_mask_transposed": ("ok &= np.asarray(bm, dtype=bool)[i // blk, j // blk]",
+                              "ok &= np.asarray(bm, dtype=bool).T[i // blk, j // blk]"),
+    "block_mask_ignored": ("ok &= np.asarray(bm, dtype=bool)[i // blk, j // blk]",
+                           "ok &= np.asarray(bm, dtype=bool).any()"),
+    "block_mask_first_head": ("return (bm[0] if bm.shape[0] == 1 else bm[h]), int(blk)",
+                              "return bm[0], int(blk)"),
+    "block_index_by_key_only": ("ok &= np.asarray(bm, dtype=bool)[i // blk, j // blk]",
+                                "ok &= np.asarray(bm, dtype=bool)[0 * i, j // blk]"),
     "jagged_heads_interleaved": ("o[qs:qs + lq, h], _ = _head_rows(q[qs:qs + lq, h], k[ks:ks + lk, g]",
                                  "o[qs:qs + lq, h], _ = _head_rows(q[qs:qs + lq, h], k[ks:ks + lk, h % Hkv]"),
 }

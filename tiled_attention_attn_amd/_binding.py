@@ -48,6 +48,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.attn_fwd_jagged.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
                                     f32, i32, vp]
     lib.attn_fwd_jagged.restype = i32
+    lib.attn_fwd_block_sparse.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
+                                          i32, i32, vp, f32, i32, vp]
+    lib.attn_fwd_block_sparse.restype = i32
     lib.attn_strerror.argtypes = [i32]
     lib.attn_strerror.restype = ctypes.c_char_p
     lib.attn_version.argtypes = []
@@ -186,4 +189,36 @@ def attn_fwd_jagged(q, k, v, q_offsets, kv_offsets, max_lq, max_lk, o=None, *, c
     _check(lib.attn_fwd_jagged(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(q_offsets),
                                _ptr(kv_offsets), B, H, k.shape[1], int(max_lq), int(max_lk), d,
                                int(bool(causal)), float(scale), _dtype_code(q), _stream(stream)))
+    return o
+
+
+def attn_fwd_block_sparse(q, k, v, block_mask, blk, o=None, *, causal=False, kv_len=None,
+                          scale=0.0, stream=None):
+    """Fixed-block sparse attention: query block qb attends to key block kb only where
+    block_mask[h or 0, qb, kb] is nonzero.
+
+    q [B,H,Lq,d], k/v [B,Hkv,Lk,d] as attn_fwd; block_mask: uint8 (or bool) device tensor
+    [1 or H, ceil(Lq/blk), ceil(Lk/blk)]; blk a multiple of 128. Returns o.
+    """
+    import torch
+    lib = load_library()
+    o = _prep(q, k, v, o, {"kv_len": kv_len})
+    B, H, Lq, d = q.shape
+    Lk = k.shape[2]
+    if k.shape[0] != B:
+        raise ValueError("k/v batch must equal q batch")
+    if block_mask.dtype == torch.bool:
+        block_mask = block_mask.to(torch.uint8)
+    if (block_mask.dtype != torch.uint8 or not block_mask.is_cuda or not block_mask.is_contiguous()
+            or block_mask.dim() != 3):
+        raise ValueError("block_mask must be a contiguous 3-D uint8 device tensor")
+    nqb, nkb = -(-Lq // blk), -(-Lk // blk)
+    if block_mask.shape[0] not in (1, H) or tuple(block_mask.shape[1:]) != (nqb, nkb):
+        raise ValueError(f"block_mask must be [1 or {H}, {nqb}, {nkb}] for blk={blk}")
+    if kv_len is not None and kv_len.numel() != B:
+        raise ValueError("kv_len must have one entry per batch element")
+    _check(lib.attn_fwd_block_sparse(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(block_mask),
+                                     block_mask.shape[0], int(blk), B, H, k.shape[1], Lq, Lk, d,
+                                     int(bool(causal)), _ptr(kv_len), float(scale),
+                                     _dtype_code(q), _stream(stream)))
     return o

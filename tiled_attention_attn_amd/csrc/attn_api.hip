@@ -25,7 +25,8 @@ int check_and_launch(const void* q, const void* k, const void* v, void* o,
                      const int32_t* cand2user, int NB, int NKV, int H, int Hkv, int Lq, int Lk,
                      int d, int causal, const int32_t* kv_len, float scale, int dtype,
                      void* stream, const int32_t* q_offsets = nullptr,
-                     const int32_t* kv_offsets = nullptr) {
+                     const int32_t* kv_offsets = nullptr, const uint8_t* block_mask = nullptr,
+                     int blk = 0, int mask_heads = 0) {
   if (dtype != ATTN_F32 && dtype != ATTN_BF16) return ATTN_EUNSUPPORTED;
   if (d != 64 && d != 128) return ATTN_EUNSUPPORTED;
   if (NB < 0 || NKV < 0 || H < 0 || Lq < 0 || Lk < 0 || Hkv < 1) return ATTN_EINVAL;
@@ -49,6 +50,13 @@ int check_and_launch(const void* q, const void* k, const void* v, void* o,
   p.cand2user = cand2user;
   p.q_offsets = q_offsets;
   p.kv_offsets = kv_offsets;
+  p.block_mask = block_mask;
+  if (block_mask != nullptr) {
+    p.blk = blk;
+    p.nQB = (Lq + blk - 1) / blk;
+    p.nKB = (Lk + blk - 1) / blk;
+    p.mask_heads = mask_heads;
+  }
   p.NB = NB;
   p.NKV = NKV;
   p.H = H;
@@ -93,6 +101,22 @@ int attn_fwd_bcast(const void* q, const void* k, const void* v, void* o,
                           scale, dtype, stream);
 }
 
+int attn_fwd_block_sparse(const void* q, const void* k, const void* v, void* o,
+                          const uint8_t* block_mask, int mask_heads, int blk, int B, int H,
+                          int Hkv, int Lq, int Lk, int d, int causal, const int32_t* kv_len,
+                          float scale, int dtype, void* stream) {
+  if (blk <= 0 || blk % 128 != 0) return ATTN_EINVAL;
+  if (mask_heads != 1 && mask_heads != H) return ATTN_EINVAL;
+  if ((int64_t)B * H * Lq == 0) {   // nothing to compute; the other checks still apply
+    return check_and_launch(q, k, v, o, nullptr, B, B, H, Hkv, Lq, Lk, d, causal, kv_len, scale,
+                            dtype, stream);
+  }
+  if (block_mask == nullptr) return ATTN_EINVAL;
+  if (((int64_t)Lk + blk - 1) / blk > 1024) return ATTN_EINVAL;   // key blocks one list holds
+  return check_and_launch(q, k, v, o, nullptr, B, B, H, Hkv, Lq, Lk, d, causal, kv_len, scale,
+                          dtype, stream, nullptr, nullptr, block_mask, blk, mask_heads);
+}
+
 int attn_fwd_jagged(const void* q, const void* k, const void* v, void* o,
                     const int32_t* q_offsets, const int32_t* kv_offsets, int B, int H, int Hkv,
                     int max_Lq, int max_Lk, int d, int causal, float scale, int dtype,
@@ -113,6 +137,6 @@ const char* attn_strerror(int status) {
   }
 }
 
-int attn_version(void) { return 101; }
+int attn_version(void) { return 102; }
 
 }  // extern "C"

@@ -146,7 +146,12 @@ __device__ __forceinline__ void wait_vm() { __builtin_amdgcn_s_waitcnt(0x0F70); 
 // W = 4: one 4-wave workgroup per SIMD pair (two workgroups per CU), the
 // software-pipelined loop; W = 8: one 8-wave workgroup per CU, the ping-pong
 // loop (waves w and w+4 on one SIMD).
-template <int D, bool CAUSAL, int W, bool JAGGED>
+// Tensor layouts of the kernel instantiations.
+constexpr int kDense = 0, kJagged = 1, kSparse = 2;
+// Most key blocks a block-sparse query block may list (LDS list size).
+constexpr int kMaxKeyBlocks = 1024;
+
+template <int D, bool CAUSAL, int W, int LAYOUT>
 __global__ __launch_bounds__(W * 64, W == 4 ? 2 : 1) void attn_fwd_bf16_kernel(const Params p) {
   using TL = Tile<D, W>;
   constexpr int kWaves = W;
@@ -206,7 +211,10 @@ __global__ __launch_bounds__(W * 64, W == 4 ? 2 : 1) void attn_fwd_bf16_kernel(c
   // keep compile-time strides): tokens are packed [total, heads, D], so rows
   // of one head are heads*D elements apart and sequence b starts at token
   // offsets[b]; lengths come from the offsets, clamped to [0, Lq] / [0, Lk].
-  constexpr bool jagged = JAGGED;
+  constexpr bool jagged = LAYOUT == kJagged;
+  constexpr bool sparse = LAYOUT == kSparse;
+  // block-sparse: active key blocks of the workgroup's query block, then the count
+  __shared__ int klist[sparse ? kMaxKeyBlocks + 1 : 1];
   const int q_rs = jagged ? p.H * D : D;
   const int kv_rs = jagged ? p.Hkv * D : D;
   auto seq_len = [&](const int32_t* off, int b, int cap) __attribute__((always_inline)) -> int {
@@ -293,10 +301,64 @@ __global__ __launch_bounds__(W * 64, W == 4 ? 2 : 1) void attn_fwd_bf16_kernel(c
       if (CAUSAL) n = min(n, min(t.row0 + kRowsPerWave, t.lq));
       return n;
     };
+    // The key tiles of the pass, in order. Dense and jagged: 0, 1, 2, ...
+    // Block-sparse: the tiles of the key blocks set in the mask row of the
+    // workgroup's query block (every wave of a workgroup lies in one query
+    // block: blk is a multiple of the workgroup's rows), compacted by wave 0.
+    int nact = 0;
+    int tpb = 1;   // tiles per key block
+    if constexpr (sparse) {
+      tpb = p.blk / BN;
+      const int qblk = min(task_of(0).row0 / p.blk, p.nQB - 1);
+      const int hm = p.mask_heads == 1 ? 0 : h;
+      if (wave == 0) {
+        const uint8_t* mrow = p.block_mask + ((size_t)hm * p.nQB + qblk) * p.nKB;
+        int cnt = 0;
+        for (int base = 0; base < p.nKB; base += 64) {
+          const int kb = base + lane;
+          const bool on = kb < p.nKB && mrow[kb] != 0;
+          const uint64_t bal = __ballot(on);
+          const int before = __builtin_amdgcn_mbcnt_hi(
+              (uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+          if (on) klist[cnt + before] = kb;
+          cnt += __builtin_popcountll(bal);
+        }
+        if (lane == 0) klist[kMaxKeyBlocks] = cnt;
+      }
+      __syncthreads();
+      nact = __builtin_amdgcn_readfirstlane(klist[kMaxKeyBlocks]);
+    }
+    auto tile_of = [&](int s) __attribute__((always_inline)) -> int {
+      if constexpr (sparse)
+        return __builtin_amdgcn_readfirstlane(klist[s / tpb]) * tpb + s % tpb;
+      else
+        return s;
+    };
+    // tiles of the sequence with some key below `keys`, and with every key below it
+    auto tiles_touching = [&](int keys) __attribute__((always_inline)) -> int {
+      if constexpr (!sparse) {
+        return (keys + BN - 1) / BN;
+      } else {
+        int n = 0;
+        for (int i = 0; i < nact; ++i)
+          n += min(max((keys - klist[i] * p.blk + BN - 1) / BN, 0), tpb);
+        return n;
+      }
+    };
+    auto tiles_inside = [&](int keys) __attribute__((always_inline)) -> int {
+      if constexpr (!sparse) {
+        return keys / BN;
+      } else {
+        int n = 0;
+        for (int i = 0; i < nact; ++i) n += min(max((keys - klist[i] * p.blk) / BN, 0), tpb);
+        return n;
+      }
+    };
+
     int ntiles = 0;
     for (int w = 0; w < kWaves; ++w) {
       const WaveTask t = task_of(w);
-      if (t.valid && !t.bad && t.kvb == kvb) ntiles = max(ntiles, (keys_needed(t) + BN - 1) / BN);
+      if (t.valid && !t.bad && t.kvb == kvb) ntiles = max(ntiles, tiles_touching(keys_needed(t)));
     }
     const bool active = me.valid && !me.bad && me.kvb == kvb;
     if (ntiles == 0) {
@@ -309,11 +371,12 @@ __global__ __launch_bounds__(W * 64, W == 4 ? 2 : 1) void attn_fwd_bf16_kernel(c
       }
       continue;
     }
-    const int my_total = active ? (keys_needed(me) + BN - 1) / BN : 0;
-    // tiles whose every key is valid for every row of this wave (no mask needed)
+    const int my_total = active ? tiles_touching(keys_needed(me)) : 0;
+    // tiles whose every key is valid for every row of this wave (no mask
+    // needed); with tiles in increasing key order they come first
     int full_keys = nvalid;
     if (CAUSAL) full_keys = min(full_keys, me.row0 + 1);
-    const int my_full = active ? min(full_keys / BN, my_total) : 0;
+    const int my_full = active ? min(tiles_inside(full_keys), my_total) : 0;
 
     size_t kv_base = ((size_t)kvb * p.Hkv + g) * (size_t)p.Lk * D;   // elements
     if (jagged) kv_base = (size_t)p.kv_offsets[kvb] * kv_rs + (size_t)g * D;
@@ -440,9 +503,9 @@ __global__ __launch_bounds__(W * 64, W == 4 ? 2 : 1) void attn_fwd_bf16_kernel(c
     };
     // Online softmax of block qb for tile t (base 2, scale folded into c);
     // produces the next PV operand and returns the rescale factor of O.
-    auto softmax = [&](f32x16 (&sacc)[KB], int qb, int t, bool masked, bf16x8 (&pout)[PS]) __attribute__((always_inline)) -> float {
+    auto softmax = [&](f32x16 (&sacc)[KB], int qb, int tile, bool masked, bf16x8 (&pout)[PS]) __attribute__((always_inline)) -> float {
       if (masked) {
-        const int key0 = t * BN;
+        const int key0 = tile * BN;
         const int qrow = me.row0 + 32 * qb + col;
 #pragma unroll
         for (int kbk = 0; kbk < KB; ++kbk)
@@ -544,7 +607,7 @@ __global__ __launch_bounds__(W * 64, W == 4 ? 2 : 1) void attn_fwd_bf16_kernel(c
 #pragma unroll
         for (int qb = 0; qb < kQB; ++qb) {
           bf16x8 pnew[PS];
-          const float alpha = softmax(sacc[qb], qb, t, masked, pnew);
+          const float alpha = softmax(sacc[qb], qb, tile_of(t), masked, pnew);
           rescale(qb, alpha);
 #pragma unroll
           for (int ps = 0; ps < PS; ++ps) pprev[qb][ps] = pnew[ps];
@@ -567,9 +630,9 @@ __global__ __launch_bounds__(W * 64, W == 4 ? 2 : 1) void attn_fwd_bf16_kernel(c
       u32x4* vc = SP ? vbuf1 : vbuf0;           // V(s)
       const int s2 = h >> 1;
       if (EVEN) {
-        if (s2 + 1 < ntiles) load_k(kn, s2 + 1);
+        if (s2 + 1 < ntiles) load_k(kn, tile_of(s2 + 1));
       } else {
-        if (s2 < ntiles) load_v(vc, s2);
+        if (s2 < ntiles) load_v(vc, tile_of(s2));
       }
       if (active) {
         if (EVEN == (G == 0)) mfma_phase(s2, kc, vp);
@@ -593,8 +656,8 @@ __global__ __launch_bounds__(W * 64, W == 4 ? 2 : 1) void attn_fwd_bf16_kernel(c
     // that it multiplies the zeroed P by finite values.
 #pragma unroll
     for (int ps = 0; ps < PS; ++ps) pprev[0][ps] = bf16x8{};
-    load_k(kbuf0, 0);
-    load_v(vbuf1, 0);
+    load_k(kbuf0, tile_of(0));
+    load_v(vbuf1, tile_of(0));
     wait_vm();
     __syncthreads();
     if (grp_id == 0) run_group(std::integral_constant<int, 0>{});
@@ -616,8 +679,8 @@ __global__ __launch_bounds__(W * 64, W == 4 ? 2 : 1) void attn_fwd_bf16_kernel(c
       u32x4* knext = PAR ? kbuf0 : kbuf1;
       u32x4* vprev = PAR ? vbuf0 : vbuf1;
       u32x4* vcur = PAR ? vbuf1 : vbuf0;
-      if (t + 1 < ntiles) load_k(knext, t + 1);
-      if (t < ntiles) load_v(vcur, t);
+      if (t + 1 < ntiles) load_k(knext, tile_of(t + 1));
+      if (t < ntiles) load_v(vcur, tile_of(t));
       if (active) {
         const bool do_sm = t < my_total;
         if (t <= my_total) {
@@ -630,7 +693,7 @@ __global__ __launch_bounds__(W * 64, W == 4 ? 2 : 1) void attn_fwd_bf16_kernel(c
 #pragma unroll
           for (int qb = 0; qb < kQB; ++qb) {
             bf16x8 pnew[PS];
-            const float alpha = softmax(sacc[qb], qb, t, masked, pnew);
+            const float alpha = softmax(sacc[qb], qb, tile_of(t), masked, pnew);
             rescale(qb, alpha);
 #pragma unroll
             for (int ps = 0; ps < PS; ++ps) pprev[qb][ps] = pnew[ps];
@@ -642,8 +705,8 @@ __global__ __launch_bounds__(W * 64, W == 4 ? 2 : 1) void attn_fwd_bf16_kernel(c
     };
 #pragma unroll
     for (int ps = 0; ps < PS; ++ps) pprev[0][ps] = bf16x8{};
-    load_k(kbuf0, 0);
-    load_v(vbuf1, 0);
+    load_k(kbuf0, tile_of(0));
+    load_v(vbuf1, tile_of(0));
     wait_vm();
     __syncthreads();
     int t = 0;
@@ -682,12 +745,14 @@ __global__ __launch_bounds__(W * 64, W == 4 ? 2 : 1) void attn_fwd_bf16_kernel(c
 // Host-side launcher (one instance per head dim, causal flag and wave count).
 hipError_t launch_bf16(const Params& p, int D, bool causal, hipStream_t stream) {
   dim3 grid(p.T), block(p.waves * 64);
-#define ATTN_LAUNCH(DD, CC, WW)                                                              \
-  do {                                                                                       \
-    if (p.q_offsets != nullptr)                                                              \
-      hipLaunchKernelGGL((attn_fwd_bf16_kernel<DD, CC, WW, true>), grid, block, 0, stream, p); \
-    else                                                                                     \
-      hipLaunchKernelGGL((attn_fwd_bf16_kernel<DD, CC, WW, false>), grid, block, 0, stream, p); \
+#define ATTN_LAUNCH(DD, CC, WW)                                                                 \
+  do {                                                                                          \
+    if (p.q_offsets != nullptr)                                                                 \
+      hipLaunchKernelGGL((attn_fwd_bf16_kernel<DD, CC, WW, kJagged>), grid, block, 0, stream, p); \
+    else if (p.block_mask != nullptr)                                                           \
+      hipLaunchKernelGGL((attn_fwd_bf16_kernel<DD, CC, WW, kSparse>), grid, block, 0, stream, p); \
+    else                                                                                        \
+      hipLaunchKernelGGL((attn_fwd_bf16_kernel<DD, CC, WW, kDense>), grid, block, 0, stream, p);  \
   } while (0)
   if (p.waves == 8) {
     if (D == 128) {
@@ -743,6 +808,11 @@ bool plan_bf16(Params& p, int D, bool causal) {
   if (((int64_t)p.Lk + 64) * kv_row_bytes > 0x7fffffff) return false;
   int W = (D == 128 && p.Lk >= kPingPongMinKeys) ? 8 : 4;
   if (waves_override() != 0) W = waves_override();
+  // block-sparse: a workgroup's rows must lie in one query block
+  if (p.block_mask != nullptr) {
+    if (p.blk % (W * kRowsPerWave) != 0) W = 4;
+    if (p.blk % (W * kRowsPerWave) != 0 || p.nKB > kMaxKeyBlocks) return false;
+  }
   p.waves = W;
   const int64_t nrb = ((int64_t)p.Lq + kRowsPerWave - 1) / kRowsPerWave;
   if (nrb >= W) {

@@ -6,7 +6,7 @@
 // fp32 end to end so the result stays within 1e-4 of the exact value. This
 // path serves small fp32 problems: one thread per query row, K/V tiles of 32
 // keys staged in LDS and read as broadcasts, VALU FMAs for both products.
-// It handles the dense, broadcast and jagged layouts.
+// It handles the dense, broadcast, jagged and block-sparse layouts.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -72,7 +72,15 @@ __global__ __launch_bounds__(kF32Rows) void attn_fwd_f32_kernel(const Params p) 
   float m_run = -INFINITY, l_run = 0.f;
   const float c = p.c;
 
+  // block-sparse: the workgroup's 64 rows lie in one query block (blk is a
+  // multiple of 128); skip the key tiles of blocks its mask row leaves out
+  const uint8_t* mrow = nullptr;
+  if (p.block_mask != nullptr) {
+    const int qblk = min(mt * kF32Rows / p.blk, p.nQB - 1);
+    mrow = p.block_mask + ((size_t)(p.mask_heads == 1 ? 0 : h) * p.nQB + qblk) * p.nKB;
+  }
   for (int t = 0; t < ntiles; ++t) {
+    if (mrow != nullptr && mrow[(t * kF32Keys) / p.blk] == 0) continue;   // uniform
     __syncthreads();
     for (int e = tid; e < kF32Keys * D; e += kF32Rows) {
       const int j = e / D, d = e % D;

@@ -20,6 +20,8 @@ struct Params {
   const int32_t* cand2user;  // [NB] or nullptr
   const int32_t* q_offsets;  // [NB + 1] or nullptr (dense layout)
   const int32_t* kv_offsets; // [NB + 1], set iff q_offsets is
+  const uint8_t* block_mask; // [mask_heads, nQB, nKB] or nullptr (no block sparsity)
+  int blk, nQB, nKB, mask_heads;  // block size (keys = queries), mask extents
   int NB, NKV, H, Hkv, Lq, Lk;
   float c;                   // scale * log2(e): softmax runs in base 2
   // Work decomposition (filled by the host dispatcher).
