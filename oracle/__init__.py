@@ -40,6 +40,15 @@ by all heads, or one per head) removes the key blocks a query block does not
 attend to; key j is allowed for query i only where mask[h, i // blk,
 j // blk] is set, on top of the causal and kv_len masks.
 
+In-kernel broadcast linear layer: the same "How We Built TLX" section names
+a linear-compression kernel sped up by splitting the matrix product and
+fusing the broadcast, and gives no formula. The plain reading: one linear
+layer over the concatenated features [x_user[cand2user[c]], x_cand[c]] with
+weight w [N, K_u + K_c] (user columns first) and an optional bias; the
+oracle computes it on the replicated features, the way it would be computed
+without the optimisation. ikbo_user_partial is the user half of that
+product plus the bias (the quantity computed once per user).
+
 Readings where the pages are silent (each is also listed with the design
 notes): scale defaults to 1/sqrt(d); the mask is additive -inf; causal is
 top-left (key j allowed iff j <= i); kv_len is one value per K/V batch entry,
@@ -61,7 +70,7 @@ import numpy as np
 
 __all__ = ["attention", "attention_rows", "attention_bcast", "attention_jagged",
            "attention_jagged_rows", "attention_block_sparse", "attention_block_sparse_rows",
-           "probabilities"]
+           "probabilities", "ikbo_linear", "ikbo_user_partial"]
 
 
 def _default_scale(d: int, scale) -> float:
@@ -265,3 +274,38 @@ def attention_block_sparse_rows(q, k, v, block_mask, blk, b, h, rows, *, causal=
                         np.asarray(v[b, g], np.float64), np.asarray(rows), causal, kvl,
                         _default_scale(q.shape[3], scale), _block_for_head(block_mask, blk, h))
     return out
+
+
+def ikbo_linear(x_user, x_cand, w, cand2user, bias=None):
+    """In-kernel-broadcast linear layer, float64, written as the replicated product.
+
+    x_user [B_u, K_u]; x_cand [B_c, K_c]; w [N, K_u + K_c], the weight of one
+    linear layer over the concatenated features [user | candidate]; bias [N]
+    or None; cand2user [B_c]. Returns y [B_c, N]:
+        y[c] = concat(x_user[cand2user[c]], x_cand[c]) @ w.T + bias
+    with NaN rows for candidates whose user index is outside [0, B_u).
+    """
+    xu, xc, w = (np.asarray(x, np.float64) for x in (x_user, x_cand, w))
+    c2u = np.asarray(cand2user, np.int64)
+    B_u, K_u = xu.shape
+    B_c, K_c = xc.shape
+    assert w.shape[1] == K_u + K_c and c2u.shape == (B_c,)
+    bad = (c2u < 0) | (c2u >= B_u)
+    u = np.where(bad, 0, c2u)
+    rep = xu[u] if B_u > 0 else np.zeros((B_c, K_u))
+    feats = np.concatenate([rep, xc], axis=1)
+    y = feats @ w.T
+    if bias is not None:
+        y = y + np.asarray(bias, np.float64)[None, :]
+    y[bad] = np.nan
+    return y
+
+
+def ikbo_user_partial(x_user, w, bias=None):
+    """The user half of the layer, once per user: z = x_user @ w[:, :K_u].T + bias."""
+    xu, w = np.asarray(x_user, np.float64), np.asarray(w, np.float64)
+    K_u = xu.shape[1]
+    z = xu @ w[:, :K_u].T
+    if bias is not None:
+        z = z + np.asarray(bias, np.float64)[None, :]
+    return z

@@ -483,4 +483,100 @@ def pin_block_sparse_shared_mask(impl):
     np.testing.assert_array_equal(part, o1[1, 2, [5, 0, 3]])
 
 
+# --- in-kernel broadcast linear layer -------------------------------------------
+
+def _ikbo_case(seed, B_u=3, B_c=7, K_u=5, K_c=4, N=6):
+    rng = _rng(seed)
+    xu = rng.standard_normal((B_u, K_u))
+    xc = rng.standard_normal((B_c, K_c))
+    w = rng.standard_normal((N, K_u + K_c))
+    b = rng.standard_normal(N)
+    c2u = rng.integers(0, B_u, B_c)
+    return xu, xc, w, b, c2u
+
+
+def pin_ikbo_brute_force(impl):
+    """Loops over (candidate, output) on the explicitly concatenated feature vector,
+    summed exactly (math.fsum), with and without a bias."""
+    xu, xc, w, b, c2u = _ikbo_case(61)
+    for bias in (b, None):
+        y = impl.ikbo_linear(xu, xc, w, c2u, bias)
+        for c in range(xc.shape[0]):
+            f = list(xu[c2u[c]]) + list(xc[c])
+            for n in range(w.shape[0]):
+                want = math.fsum([f[t] * w[n, t] for t in range(len(f))] +
+                                 ([bias[n]] if bias is not None else []))
+                assert abs(y[c, n] - want) <= 1e-12, (c, n, y[c, n], want)
+
+
+def pin_ikbo_torch_linear(impl):
+    """torch.nn.functional.linear (float64) on the replicated, concatenated features."""
+    import torch
+    xu, xc, w, b, c2u = _ikbo_case(62, B_u=4, B_c=11, K_u=9, K_c=3, N=5)
+    feats = torch.cat([torch.from_numpy(xu)[torch.from_numpy(c2u)], torch.from_numpy(xc)], 1)
+    want = torch.nn.functional.linear(feats, torch.from_numpy(w), torch.from_numpy(b)).numpy()
+    np.testing.assert_allclose(impl.ikbo_linear(xu, xc, w, c2u, b), want, rtol=0, atol=1e-12)
+
+
+def pin_ikbo_permutation_weight(impl):
+    """A 0/1 weight that picks feature perm[n] for output n: y[:, n] = feats[:, perm[n]],
+    where the features are the user's (first K_u) and then the candidate's."""
+    xu, xc, _, _, c2u = _ikbo_case(63, K_u=4, K_c=3)
+    K = xu.shape[1] + xc.shape[1]
+    perm = _rng(64).permutation(K)
+    w = np.zeros((K, K))
+    w[np.arange(K), perm] = 1.0
+    y = impl.ikbo_linear(xu, xc, w, c2u)
+    for c in range(xc.shape[0]):
+        for n in range(K):
+            t = perm[n]
+            want = xu[c2u[c], t] if t < xu.shape[1] else xc[c, t - xu.shape[1]]
+            assert y[c, n] == want
+
+
+def pin_ikbo_same_user_rows(impl):
+    """Candidates with no features of their own (x_cand = 0) get their user's row of
+    the user partial; equal candidate features of one user give equal rows."""
+    xu, _, w, b, c2u = _ikbo_case(65, B_c=9)
+    xc = np.zeros((9, 4))
+    y = impl.ikbo_linear(xu, xc, w, c2u, b)
+    z = impl.ikbo_user_partial(xu, w, b)
+    np.testing.assert_allclose(y, z[c2u], rtol=0, atol=1e-12)
+    xc = np.tile(_rand((1, 4), 66), (9, 1))
+    y = impl.ikbo_linear(xu, xc, w, np.zeros(9, np.int64), b)
+    assert np.all(y == y[0])
+
+
+def pin_ikbo_user_partial_brute_force(impl):
+    """z[u, n] = sum over the first K_u weight columns only, plus the bias."""
+    xu, _, w, b, _ = _ikbo_case(67, K_u=3, K_c=5)
+    z = impl.ikbo_user_partial(xu, w, b)
+    for u in range(xu.shape[0]):
+        for n in range(w.shape[0]):
+            want = math.fsum([xu[u, t] * w[n, t] for t in range(3)] + [b[n]])
+            assert abs(z[u, n] - want) <= 1e-12
+
+
+def pin_ikbo_out_of_range_user_is_nan(impl):
+    """cand2user outside [0, B_u): that row is NaN, every other row is finite and
+    unchanged."""
+    xu, xc, w, b, c2u = _ikbo_case(68)
+    bad = c2u.copy()
+    bad[[1, 4]] = [-1, xu.shape[0]]
+    y = impl.ikbo_linear(xu, xc, w, bad, b)
+    y0 = impl.ikbo_linear(xu, xc, w, c2u, b)
+    assert np.all(np.isnan(y[[1, 4]]))
+    keep = [c for c in range(len(c2u)) if c not in (1, 4)]
+    assert np.array_equal(y[keep], y0[keep])
+
+
+def pin_ikbo_candidate_permutation(impl):
+    """Permuting candidates (their features and map together) permutes the rows."""
+    xu, xc, w, b, c2u = _ikbo_case(69, B_c=10)
+    perm = _rng(70).permutation(10)
+    y = impl.ikbo_linear(xu, xc, w, c2u, b)
+    yp = impl.ikbo_linear(xu, xc[perm], w, c2u[perm], b)
+    np.testing.assert_allclose(yp, y[perm], rtol=0, atol=1e-13)
+
+
 ALL_PINS = [v for n, v in sorted(globals().items()) if n.startswith("pin_")]

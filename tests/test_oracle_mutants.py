@@ -44,6 +44,15 @@ MUTANTS = {
                               "return bm[0], int(blk)"),
     "block_index_by_key_only": ("ok &= np.asarray(bm, dtype=bool)[i // blk, j // blk]",
                                 "ok &= np.asarray(bm, dtype=bool)[0 * i, j // blk]"),
+    "ikbo_concat_swapped": ("feats = np.concatenate([rep, xc], axis=1)",
+                            "feats = np.concatenate([xc, rep], axis=1)"),
+    "ikbo_ignores_map": ("bad = (c2u < 0) | (c2u >= B_u)",
+                         "c2u = np.arange(B_c) % max(B_u, 1); bad = (c2u < 0) | (c2u >= B_u)"),
+    "ikbo_weight_transposed": ("y = feats @ w.T", "y = feats @ w.reshape(w.shape[1], -1)"),
+    "ikbo_bias_dropped": ("        y = y + np.asarray(bias, np.float64)[None, :]\n",
+                          "        pass\n"),
+    "ikbo_no_nan": ("y[bad] = np.nan", "y[bad] = 0.0"),
+    "ikbo_user_partial_wrong_columns": ("z = xu @ w[:, :K_u].T", "z = xu @ w[:, -K_u:].T"),
     "jagged_heads_interleaved": ("o[qs:qs + lq, h], _ = _head_rows(q[qs:qs + lq, h], k[ks:ks + lk, g]",
                                  "o[qs:qs + lq, h], _ = _head_rows(q[qs:qs + lq, h], k[ks:ks + lk, h % Hkv]"),
 }
