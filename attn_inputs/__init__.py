@@ -10,7 +10,8 @@ any machine with the same numpy. Normal samples are float32 N(0, 1); bf16
 tensors are those samples rounded to nearest-even and held as raw uint16 bit
 patterns.
 
-Stream ids: Q=0, K=1, V=2, integers (kv_len) = 3.
+Stream ids: Q=0, K=1, V=2, integers (kv_len) = 3, block masks = 4; the
+linear layer's x_user=10, x_cand=11, w=12, bias=13, cand2user order=14.
 """
 from __future__ import annotations
 
@@ -20,6 +21,7 @@ import hashlib
 import numpy as np
 
 STREAM_Q, STREAM_K, STREAM_V, STREAM_INT = 0, 1, 2, 3
+STREAM_XU, STREAM_XC, STREAM_W, STREAM_BIAS, STREAM_MAP = 10, 11, 12, 13, 14
 
 
 def _gen(seed: int, stream: int) -> np.random.Generator:
@@ -224,3 +226,56 @@ def make_workload(name: str, seed: int = 0) -> AttnInputs:
                                  w.pop("d"), w.pop("blk"), seed=seed, **w)
     return make_bcast(w.pop("B_c"), w.pop("B_u"), w.pop("H"), w.pop("Hkv"), w.pop("Lq"),
                       w.pop("Lk"), w.pop("d"), seed=seed, **w)
+
+
+@dataclass
+class LinearInputs:
+    """One in-kernel broadcast linear problem; x_user [B_u,K_u], x_cand [B_c,K_c] and
+    w [N,K_u+K_c] are bf16 bits (uint16), bias float32 [N] or None, cand2user int32 [B_c]."""
+    x_user: np.ndarray
+    x_cand: np.ndarray
+    w: np.ndarray
+    bias: np.ndarray | None
+    cand2user: np.ndarray
+    out_dtype: str = "bf16"
+    meta: dict = field(default_factory=dict)
+
+    def f64(self):
+        return (to_f64(self.x_user, "bf16"), to_f64(self.x_cand, "bf16"), to_f64(self.w, "bf16"),
+                None if self.bias is None else self.bias.astype(np.float64))
+
+
+def make_linear(B_u, B_c, K_u, K_c, N, *, bias=True, out_dtype="bf16", shuffle=False,
+                cand2user=None, seed=0) -> LinearInputs:
+    """Features iid N(0,1); weight N(0,1)/sqrt(K_u+K_c) (outputs of unit scale); bias
+    0.1 N(0,1). cand2user defaults to contiguous groups of B_c // B_u candidates per
+    user (the order in which one request's candidates arrive); shuffle=True permutes
+    it on its own stream."""
+    K = K_u + K_c
+    x_user = f32_to_bf16_bits(normal_f32((B_u, K_u), seed, STREAM_XU))
+    x_cand = f32_to_bf16_bits(normal_f32((B_c, K_c), seed, STREAM_XC))
+    w = f32_to_bf16_bits(normal_f32((N, K), seed, STREAM_W) * np.float32(1.0 / np.sqrt(max(K, 1))))
+    b = normal_f32((N,), seed, STREAM_BIAS) * np.float32(0.1) if bias else None
+    if cand2user is None:
+        per = max(1, B_c // max(B_u, 1))
+        cand2user = np.minimum(np.arange(B_c) // per, max(B_u - 1, 0))
+        if shuffle:
+            cand2user = _gen(seed, STREAM_MAP).permutation(cand2user)
+    cand2user = np.asarray(cand2user, dtype=np.int32)
+    return LinearInputs(x_user, x_cand, w, b, cand2user, out_dtype,
+                        meta=dict(kind="ikbo_linear", B_u=B_u, B_c=B_c, K_u=K_u, K_c=K_c, N=N,
+                                  bias=bool(bias), out_dtype=out_dtype))
+
+
+# The linear layer's workload: 2048 users with 32 candidates each, user
+# features of 2048 and candidate features of 1024 compressed to 1024 outputs.
+LINEAR_WORKLOADS = {
+    "ikbo_linear_Bc65536": dict(B_u=2048, B_c=65536, K_u=2048, K_c=1024, N=1024, bias=True,
+                                out_dtype="bf16"),
+}
+
+
+def make_linear_workload(name: str, seed: int = 0) -> LinearInputs:
+    w = dict(LINEAR_WORKLOADS[name])
+    return make_linear(w.pop("B_u"), w.pop("B_c"), w.pop("K_u"), w.pop("K_c"), w.pop("N"),
+                       seed=seed, **w)

@@ -1,5 +1,6 @@
 /*
- * attn.h - C ABI of the MI355X (gfx950) fused tiled attention forward pass.
+ * attn.h - C ABI of the MI355X (gfx950) fused tiled attention forward pass
+ * and the in-kernel broadcast linear layer.
  *
  * Operation. For every batch entry b, query head h and query row i,
  *     O[b,h,i,:] = sum_j softmax_j( scale * <Q[b,h,i,:], K[b,g,j,:]> + mask[i,j] ) * V[b,g,j,:]
@@ -147,10 +148,44 @@ int attn_fwd_block_sparse(const void* q, const void* k, const void* v, void* o,
                           int causal, const int32_t* kv_len, float scale,
                           int dtype, void* stream);
 
+/*
+ * In-kernel broadcast linear layer: one linear layer over the concatenated
+ * features [x_user[cand2user[c]], x_cand[c]] of every candidate c, computed
+ * without replicating the user features. "How We Built TLX" (Chinese
+ * translation, "Case study 2: in-kernel broadcast optimisation for RecSys")
+ * names this linear-compression kernel and the three steps that sped it up
+ * (splitting the matrix product, aligning memory, fusing the broadcast) but
+ * gives no formula; the reading here is the plain one:
+ *     y[c] = x_cand[c] w_cand^T + z[cand2user[c]],
+ *     z[u] = x_user[u] w_user^T + bias            (once per user)
+ * with w = [w_user | w_cand] split by columns.
+ *   x_user    [B_u, K_u] bf16         user features
+ *   x_cand    [B_c, K_c] bf16         candidate features
+ *   w         [N, K_u + K_c] bf16     weight, user columns first (the
+ *                                     nn.Linear layout: one row per output)
+ *   bias      [N] fp32 or NULL
+ *   cand2user [B_c] int32, values in [0, B_u) (others give NaN rows)
+ *   y         [B_c, N] of y_dtype (ATTN_BF16: rounded to nearest-even from
+ *             the fp32 sum; ATTN_F32), written
+ *   z         [B_u, N] fp32, written with the user half plus the bias; the
+ *             caller owns it (it is also a result) and it must not alias y
+ * Products are exact in fp32 and accumulate in fp32. All pointers are device
+ * pointers, 16-byte aligned. K_u and K_c are multiples of 8, N a multiple of
+ * 4, K_u + K_c <= 2^20 and N * (K_u + K_c) * 2 < 2^31; either K may be 0 (that
+ * half contributes nothing). B_c > 0 needs B_u >= 1. Two kernels are enqueued
+ * on `stream` (z, then y); the call does not synchronise. Errors: ATTN_EINVAL
+ * for a bad size, a NULL or misaligned pointer that the sizes make used;
+ * ATTN_EUNSUPPORTED for another y_dtype; ATTN_ELAUNCH.
+ */
+int ikbo_linear(const void* x_user, const void* x_cand, const void* w, const float* bias,
+                const int32_t* cand2user, void* y, float* z,
+                int B_u, int B_c, int K_u, int K_c, int N, int y_dtype, void* stream);
+
 /* Static, human-readable text for a status code (never NULL). */
 const char* attn_strerror(int status);
 
-/* ABI version: major * 100 + minor (101: attn_fwd_jagged; 102: attn_fwd_block_sparse). */
+/* ABI version: major * 100 + minor (101: attn_fwd_jagged; 102: attn_fwd_block_sparse;
+ * 103: ikbo_linear). */
 int attn_version(void);
 
 #ifdef __cplusplus

@@ -15,7 +15,7 @@ HEADER = os.path.join(ROOT, "include", "attn.h")
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(attn_\w+)\s*\(", text, flags=re.M)))
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**((?:attn|ikbo)_\w+)\s*\(", text, flags=re.M)))
 
 
 @pytest.fixture(scope="module")
@@ -28,13 +28,14 @@ def lib():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == ["attn_fwd", "attn_fwd_bcast", "attn_fwd_block_sparse",
-                                    "attn_fwd_jagged", "attn_strerror", "attn_version"]
+                                    "attn_fwd_jagged", "attn_strerror", "attn_version",
+                                    "ikbo_linear"]
 
 
 def test_library_exports_every_declared_symbol(lib):
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert lib.attn_version() == 102
+    assert lib.attn_version() == 103
 
 
 def test_strerror_covers_every_status(lib):
@@ -149,3 +150,30 @@ def sparse(lib, mask=FAKE, mask_heads=1, blk=128, B=1, H=2, Hkv=1, Lq=256, Lk=25
 ])
 def test_attn_fwd_block_sparse_argument_checks(lib, kwargs, status):
     assert sparse(lib, **kwargs) == status
+
+
+def ikbo(lib, xu=FAKE, xc=FAKE, w=FAKE, bias=None, c2u=FAKE, y=FAKE, z=FAKE, B_u=4, B_c=64,
+         K_u=128, K_c=64, N=256, y_dtype=taa.ATTN_BF16):
+    return lib.ikbo_linear(xu, xc, w, bias, c2u, y, z, B_u, B_c, K_u, K_c, N, y_dtype, None)
+
+
+@pytest.mark.parametrize("kwargs,status", [
+    (dict(y_dtype=7), taa.ATTN_EUNSUPPORTED),
+    (dict(K_u=100), taa.ATTN_EINVAL),            # rows not 16-byte multiples
+    (dict(K_c=12), taa.ATTN_EINVAL),
+    (dict(N=6), taa.ATTN_EINVAL),                # not a multiple of 4
+    (dict(B_c=-1), taa.ATTN_EINVAL),
+    (dict(B_u=0), taa.ATTN_EINVAL),              # candidates need users
+    (dict(z=None), taa.ATTN_EINVAL),
+    (dict(c2u=None), taa.ATTN_EINVAL),
+    (dict(y=None), taa.ATTN_EINVAL),
+    (dict(xu=ctypes.c_void_p(0x1008)), taa.ATTN_EINVAL),   # misaligned
+    (dict(bias=ctypes.c_void_p(0x1004)), taa.ATTN_EINVAL),
+    (dict(K_u=1 << 20, K_c=8), taa.ATTN_EINVAL),           # K above 2^20
+    (dict(K_u=65536, K_c=0, N=16384), taa.ATTN_EINVAL),    # weight past 2^31 bytes
+    (dict(N=0), taa.ATTN_OK),
+    (dict(B_u=0, B_c=0), taa.ATTN_OK),
+    (dict(B_c=0, z=None), taa.ATTN_EINVAL),      # z is written whenever there are users
+])
+def test_ikbo_linear_argument_checks(lib, kwargs, status):
+    assert ikbo(lib, **kwargs) == status

@@ -1,0 +1,137 @@
+"""The in-kernel broadcast linear layer on the GPU against the float64 oracle,
+element by element, through the C ABI.
+
+Error bound, from the arithmetic: products of bf16 values are exact in fp32;
+summing K of them in fp32 (in any order, rounding at each addition) errs by at
+most (K + 2) * 2^-24 * S per element, with S = sum |x_t w_t| + |bias|; the
+bound below doubles that in case the hardware rounds toward zero. A bf16
+output adds the final rounding, at most 2^-8 of the value.
+"""
+import numpy as np
+import pytest
+
+import attn_inputs as ai
+import oracle
+from gpu_util import from_dev, i32_dev, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    import tiled_attention_attn_amd as taa
+    taa.load_library()
+    return taa
+
+
+def bound(xu, xc, w, c2u, bias, ref, out_dtype):
+    """Per-element error bound of the fp32 accumulation (+ bf16 rounding)."""
+    K_u = xu.shape[1]
+    u = np.clip(c2u, 0, max(xu.shape[0] - 1, 0))
+    s = np.abs(xc) @ np.abs(w[:, K_u:]).T
+    if K_u:
+        s = s + (np.abs(xu) @ np.abs(w[:, :K_u]).T)[u]
+    if bias is not None:
+        s = s + np.abs(bias)[None, :]
+    tol = (w.shape[1] + 2) * 2.0 ** -23 * s
+    if out_dtype == "bf16":
+        tol = tol + 2.0 ** -8 * np.abs(ref)
+    return tol + 1e-30
+
+
+def run(taa, w, c2u=None):
+    import torch
+    xu, xc, wt = (to_dev(x, "bf16") for x in (w.x_user, w.x_cand, w.w))
+    bias = None if w.bias is None else torch.from_numpy(w.bias).cuda()
+    out = torch.bfloat16 if w.out_dtype == "bf16" else torch.float32
+    y, z = taa.ikbo_linear(xu, xc, wt, i32_dev(w.cand2user if c2u is None else c2u), bias,
+                           out_dtype=out)
+    torch.cuda.synchronize()
+    return from_dev(y), from_dev(z)
+
+
+def check(w, y, z, c2u=None):
+    c2u = w.cand2user if c2u is None else c2u
+    xu, xc, wt, b = w.f64()
+    ref = oracle.ikbo_linear(xu, xc, wt, c2u, b)
+    ok = ~np.isnan(ref).any(axis=1)
+    tol = bound(xu, xc, wt, c2u, b, ref, w.out_dtype)
+    err = np.abs(y - ref)
+    assert np.all(np.isnan(y[~ok])), "out-of-range users must give NaN rows"
+    assert np.all(err[ok] <= tol[ok]), float(np.max(err[ok] / tol[ok]))
+    zref = oracle.ikbo_user_partial(xu, wt, b)
+    ztol = bound(xu, np.zeros((xu.shape[0], 0)), wt[:, :xu.shape[1]],
+                 np.arange(xu.shape[0]), b, zref, "f32")
+    assert np.all(np.abs(z - zref) <= ztol)
+
+
+LINEAR_CASES = [
+    # (B_u, B_c, K_u, K_c, N, bias, out dtype, shuffled map)
+    (4, 128, 128, 64, 128, True, "bf16", False),     # whole tiles
+    (5, 300, 200, 72, 260, True, "bf16", True),      # ragged rows, columns and K tails
+    (3, 77, 8, 8, 4, False, "f32", True),            # tiny
+    (7, 513, 0, 136, 132, True, "f32", True),        # no user features
+    (9, 257, 264, 0, 100, True, "bf16", False),      # no candidate features
+    (64, 2048, 1024, 512, 512, True, "bf16", False),
+    (33, 1000, 136, 1032, 388, False, "f32", True),
+    (6, 0, 64, 64, 128, True, "bf16", False),        # users only: z is still written
+]
+
+
+@pytest.mark.parametrize("case", LINEAR_CASES,
+                         ids=lambda c: f"Bu{c[0]}-Bc{c[1]}-Ku{c[2]}-Kc{c[3]}-N{c[4]}-{c[6]}")
+def test_ikbo_linear_matches_oracle(lib, case):
+    B_u, B_c, K_u, K_c, N, bias, out, shuffle = case
+    w = ai.make_linear(B_u, B_c, K_u, K_c, N, bias=bias, out_dtype=out, shuffle=shuffle, seed=41)
+    y, z = run(lib, w)
+    check(w, y, z)
+
+
+def test_out_of_range_users_give_nan_rows(lib):
+    w = ai.make_linear(4, 200, 64, 64, 128, seed=43)
+    c2u = w.cand2user.copy()
+    c2u[[0, 7, 199]] = [-1, 4, 1 << 30]
+    y, z = run(lib, w, c2u)
+    check(w, y, z, c2u)
+
+
+def test_no_candidate_features_is_the_gathered_user_rows(lib):
+    """K_c = 0: y[c] is z[cand2user[c]] rounded to bf16, bit for bit."""
+    import torch
+    w = ai.make_linear(8, 300, 136, 0, 260, shuffle=True, seed=45)
+    y, z = run(lib, w)
+    want = torch.from_numpy(z[w.cand2user]).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(y, want)
+
+
+def test_repeatable(lib):
+    w = ai.make_linear(16, 700, 256, 192, 384, shuffle=True, seed=47)
+    y1, z1 = run(lib, w)
+    y2, z2 = run(lib, w)
+    assert np.array_equal(y1, y2) and np.array_equal(z1, z2)
+
+
+def test_ikbo_linear_full_size_workload_sampled(lib):
+    """The full workload, in the launch configuration the bench times; sampled rows
+    against the oracle on those candidates."""
+    import torch
+    w = ai.make_linear_workload("ikbo_linear_Bc65536", seed=0)
+    xu, xc, wt = (to_dev(x, "bf16") for x in (w.x_user, w.x_cand, w.w))
+    y, z = lib.ikbo_linear(xu, xc, wt, i32_dev(w.cand2user), torch.from_numpy(w.bias).cuda())
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(13)
+    B_c = w.x_cand.shape[0]
+    rows = np.unique(np.concatenate([[0, 127, 128, B_c - 1], rng.integers(0, B_c, 60)]))
+    got = y[torch.from_numpy(rows).cuda()].to(torch.float64).cpu().numpy()
+    xuf, _, wf, b = w.f64()
+    xcf = ai.to_f64(w.x_cand[rows], "bf16")
+    ref = oracle.ikbo_linear(xuf, xcf, wf, w.cand2user[rows], b)
+    tol = bound(xuf, xcf, wf, w.cand2user[rows], b, ref, "bf16")
+    assert np.all(np.abs(got - ref) <= tol)
+    users = np.unique(np.concatenate([[0, w.x_user.shape[0] - 1], rng.integers(0, 2048, 8)]))
+    zgot = z[torch.from_numpy(users).cuda()].to(torch.float64).cpu().numpy()
+    zref = oracle.ikbo_user_partial(xuf[users], wf, b)
+    assert np.max(np.abs(zgot - zref)) <= 1e-3

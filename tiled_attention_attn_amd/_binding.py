@@ -51,6 +51,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.attn_fwd_block_sparse.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
                                           i32, i32, vp, f32, i32, vp]
     lib.attn_fwd_block_sparse.restype = i32
+    lib.ikbo_linear.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp]
+    lib.ikbo_linear.restype = i32
     lib.attn_strerror.argtypes = [i32]
     lib.attn_strerror.restype = ctypes.c_char_p
     lib.attn_version.argtypes = []
@@ -222,3 +224,46 @@ def attn_fwd_block_sparse(q, k, v, block_mask, blk, o=None, *, causal=False, kv_
                                      int(bool(causal)), _ptr(kv_len), float(scale),
                                      _dtype_code(q), _stream(stream)))
     return o
+
+
+def ikbo_linear(x_user, x_cand, w, cand2user, bias=None, y=None, z=None, *, out_dtype=None,
+                stream=None):
+    """In-kernel broadcast linear layer; returns (y, z).
+
+    y[c] = concat(x_user[cand2user[c]], x_cand[c]) @ w.T + bias, computed as
+    x_cand @ w[:, K_u:].T plus row cand2user[c] of z = x_user @ w[:, :K_u].T + bias.
+    x_user [B_u,K_u], x_cand [B_c,K_c], w [N,K_u+K_c]: contiguous bf16 device tensors;
+    cand2user int32 [B_c]; bias fp32 [N] or None; y [B_c,N] bf16 (default) or fp32;
+    z fp32 [B_u,N] (allocated when None).
+    """
+    import torch
+    lib = load_library()
+    for name, t in (("x_user", x_user), ("x_cand", x_cand), ("w", w)):
+        if (not t.is_cuda or not t.is_contiguous() or t.dim() != 2
+                or t.dtype != torch.bfloat16):
+            raise ValueError(f"{name} must be a contiguous 2-D bfloat16 device tensor")
+    B_u, K_u = x_user.shape
+    B_c, K_c = x_cand.shape
+    N = w.shape[0]
+    if w.shape[1] != K_u + K_c:
+        raise ValueError(f"w must be [N, {K_u + K_c}] (user columns, then candidate columns)")
+    if (cand2user.dtype != torch.int32 or not cand2user.is_cuda or not cand2user.is_contiguous()
+            or cand2user.numel() != B_c):
+        raise ValueError("cand2user must be a contiguous int32 device tensor with B_c entries")
+    if bias is not None and (bias.dtype != torch.float32 or not bias.is_cuda
+                             or not bias.is_contiguous() or bias.numel() != N):
+        raise ValueError("bias must be a contiguous float32 device tensor with N entries")
+    if y is None:
+        y = torch.empty((B_c, N), dtype=out_dtype or torch.bfloat16, device=x_cand.device)
+    elif (tuple(y.shape) != (B_c, N) or not y.is_cuda or not y.is_contiguous()
+          or y.dtype not in (torch.bfloat16, torch.float32)):
+        raise ValueError("y must be a contiguous [B_c, N] bfloat16 or float32 device tensor")
+    if z is None:
+        z = torch.empty((B_u, N), dtype=torch.float32, device=x_user.device)
+    elif (tuple(z.shape) != (B_u, N) or z.dtype != torch.float32 or not z.is_cuda
+          or not z.is_contiguous()):
+        raise ValueError("z must be a contiguous [B_u, N] float32 device tensor")
+    _check(lib.ikbo_linear(_ptr(x_user), _ptr(x_cand), _ptr(w), _ptr(bias), _ptr(cand2user),
+                           _ptr(y), _ptr(z), B_u, B_c, K_u, K_c, N, _dtype_code(y),
+                           _stream(stream)))
+    return y, z

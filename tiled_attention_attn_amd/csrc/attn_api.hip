@@ -7,8 +7,10 @@
 
 #include "../../include/attn.h"
 #include "attn_params.h"
+#include "gemm_params.h"
 
 namespace attn {
+hipError_t launch_ikbo_gemm(GemmParams p, bool gather, bool out_f32, hipStream_t stream);
 hipError_t launch_bf16(const Params& p, int D, bool causal, hipStream_t stream);
 hipError_t launch_f32(const Params& p, int D, bool causal, hipStream_t stream);
 bool plan_bf16(Params& p, int D, bool causal);
@@ -127,6 +129,56 @@ int attn_fwd_jagged(const void* q, const void* k, const void* v, void* o,
                           scale, dtype, stream, q_offsets, kv_offsets);
 }
 
+int ikbo_linear(const void* x_user, const void* x_cand, const void* w, const float* bias,
+                const int32_t* cand2user, void* y, float* z, int B_u, int B_c, int K_u, int K_c,
+                int N, int y_dtype, void* stream) {
+  if (y_dtype != ATTN_F32 && y_dtype != ATTN_BF16) return ATTN_EUNSUPPORTED;
+  if (B_u < 0 || B_c < 0 || K_u < 0 || K_c < 0 || N < 0) return ATTN_EINVAL;
+  if (K_u % 8 != 0 || K_c % 8 != 0 || N % 4 != 0) return ATTN_EINVAL;
+  const int64_t K = (int64_t)K_u + K_c;
+  if (K > ((int64_t)1 << 20)) return ATTN_EINVAL;
+  if (B_c > 0 && N > 0 && B_u < 1) return ATTN_EINVAL;
+  if (N == 0 || (B_u == 0 && B_c == 0)) return ATTN_OK;
+  // Weight rows are addressed with 32-bit offsets; activations are split by rows.
+  if ((int64_t)(N - 1) * K * 2 + K * 2 > 0x7fffffff) return ATTN_EINVAL;
+  if ((int64_t)B_c * N > ((int64_t)1 << 46) || (int64_t)B_u * N > ((int64_t)1 << 46))
+    return ATTN_EINVAL;
+  auto need = [](const void* ptr, bool used) { return !used || (ptr != nullptr && aligned16(ptr)); };
+  if (!need(z, B_u > 0) || !need(x_user, B_u > 0 && K_u > 0) || !need(w, K > 0) ||
+      !need(x_cand, B_c > 0 && K_c > 0) || !need(y, B_c > 0) || !need(cand2user, B_c > 0) ||
+      !aligned16(bias))
+    return ATTN_EINVAL;
+
+  attn::GemmParams p{};
+  p.N = N;
+  p.ldb = (int)K;
+  hipError_t err = hipSuccess;
+  if (B_u > 0) {   // z = x_user w_user^T + bias
+    p.a = x_user;
+    p.b = w;
+    p.c = z;
+    p.bias = bias;
+    p.M = B_u;
+    p.K = K_u;
+    p.lda = K_u;
+    err = attn::launch_ikbo_gemm(p, false, true, (hipStream_t)stream);
+  }
+  if (err == hipSuccess && B_c > 0) {   // y = x_cand w_cand^T + z[cand2user]
+    p.a = x_cand;
+    p.b = (const char*)w + (size_t)K_u * 2;
+    p.c = y;
+    p.bias = nullptr;
+    p.z = z;
+    p.zrow = cand2user;
+    p.Mz = B_u;
+    p.M = B_c;
+    p.K = K_c;
+    p.lda = K_c;
+    err = attn::launch_ikbo_gemm(p, true, y_dtype == ATTN_F32, (hipStream_t)stream);
+  }
+  return err == hipSuccess ? ATTN_OK : ATTN_ELAUNCH;
+}
+
 const char* attn_strerror(int status) {
   switch (status) {
     case ATTN_OK: return "ok";
@@ -137,6 +189,6 @@ const char* attn_strerror(int status) {
   }
 }
 
-int attn_version(void) { return 102; }
+int attn_version(void) { return 103; }
 
 }  // extern "C"

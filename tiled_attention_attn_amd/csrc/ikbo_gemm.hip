@@ -1,0 +1,335 @@
+// In-kernel broadcast (IKBO) linear layer for gfx950: bf16 MFMA GEMM with
+// fp32 accumulation and a gathered-row epilogue.
+//
+// Method: "How We Built TLX" (Chinese translation, "Case study 2: in-kernel
+// broadcast optimisation for RecSys") speeds up a linear-compression kernel
+// by splitting the matrix product, aligning memory and fusing the broadcast:
+// a user's features are the same for all of its candidates, so the user half
+// of the product is computed once per user and broadcast to the candidates
+// inside the kernel instead of being replicated in memory. For a linear layer
+// with weight W = [W_user | W_cand] over the concatenated features
+// [x_user[cand2user[c]], x_cand[c]], candidate c's output is
+//     Y[c] = x_cand[c] W_cand^T + (x_user W_user^T + bias)[cand2user[c]].
+// Step 1 writes Z = x_user W_user^T + bias (fp32, one row per user); step 2
+// computes x_cand W_cand^T and adds row Z[cand2user[c]] in its epilogue.
+//
+// Both steps run one kernel: C[M, N] = A[M, K] B[N, K]^T (+ bias or Z[zrow]).
+// Operands follow the linear-layer layout (B is [out, in], rows contiguous in
+// K), so both MFMA operands read 16 contiguous bytes per lane from LDS. A
+// workgroup owns a TILE x TILE output tile (256, or 128 when the grid of 256
+// tiles would leave CUs idle), split over its waves as blocks of
+// v_mfma_f32_32x32x16_bf16 computed transposed (C^T = B A^T), so that each
+// lane holds one output row and runs of 4 consecutive columns. The wave tile
+// sets the LDS reads per MFMA (128 x 64 reads 6 fragments per 8 MFMAs). K advances 64 at a time through two LDS stages filled with
+// direct-to-LDS buffer loads; LDS rows are padded by one 16-byte chunk so that
+// operand reads are free of bank conflicts.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stdlib.h>
+
+#include "gemm_params.h"
+
+namespace attn {
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+#define LDS_AS __attribute__((address_space(3)))
+
+constexpr int kBK = 64;                         // K per LDS stage
+constexpr int kRowChunks = kBK / 8;             // 16-byte chunks of one row in a stage
+constexpr int kPitch = kRowChunks + 1;          // LDS row pitch in chunks (one pad)
+// Word 3 of a raw buffer descriptor (gfx9 family): 32-bit data format, no
+// swizzle; with stride 0 an access is in range iff its offset is below
+// num_records, and out-of-range loads return zero.
+constexpr int kBufferWord3 = 0x00020000;
+constexpr uint32_t kOutOfRange = 0x80000000u;   // above every num_records used here
+constexpr int kSchedMFMA = 0x008, kSchedDSRead = 0x100;
+
+// s_waitcnt vmcnt(0): wait for this wave's direct-to-LDS loads.
+__device__ __forceinline__ void wait_vm() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// Workgroups are dispatched round-robin over the 8 XCDs (XCD x runs ids x,
+// x+8, ...). Give each XCD a contiguous range of tiles, so the column tiles
+// of one row block (which share their A rows) run on one XCD's L2.
+__device__ __forceinline__ int xcd_tile(int w, int T) {
+  const int x = w & 7, i = w >> 3, q = T >> 3, r = T & 7;
+  return x * q + (x < r ? x : r) + i;
+}
+
+}  // namespace
+
+// Wave layout of a TILE x TILE workgroup tile: 128 -> 2 x 2 waves of 64 x 64
+// (two workgroups per CU); 256 -> 2 x 4 waves of 128 x 64 (one per CU, two
+// waves per SIMD). Both keep the accumulators in architected VGPRs.
+template <int TILE>
+struct GemmShape {
+  static constexpr int kWavesM = 2, kWavesN = TILE / 64;
+  static constexpr int kWaves = kWavesM * kWavesN;
+  static constexpr int MB = TILE / kWavesM / 32;   // 32 x 32 blocks per wave, rows
+  static constexpr int NB = TILE / kWavesN / 32;   // and columns
+  static constexpr int kPerCU = TILE == 128 ? 2 : 1;
+};
+
+template <int TILE, bool GATHER, bool OUT_F32>
+__global__ __launch_bounds__(TILE == 128 ? 256 : 512, TILE == 128 ? 2 : 1) void
+ikbo_gemm_kernel(const GemmParams p) {
+  using S = GemmShape<TILE>;
+  static_assert(S::kWaves * 64 == (TILE == 128 ? 256 : 512) && S::kPerCU == (TILE == 128 ? 2 : 1),
+                "launch bounds match the wave layout");
+  constexpr int kWaves = S::kWaves, MB = S::MB, NB = S::NB;
+  constexpr int WTM = MB * 32, WTN = NB * 32;     // wave tile
+  constexpr int kChunks = TILE * kPitch;          // chunks per operand stage
+  constexpr int kLoads = kChunks / 64;            // wave-wide loads per operand stage
+  constexpr int kPer = (kLoads + kWaves - 1) / kWaves;
+  static_assert(kChunks % 64 == 0, "an operand stage is whole wave loads");
+  // Separate arrays per stage buffer: the compiler then knows that reads of
+  // one buffer do not wait for direct-to-LDS loads still landing in the other.
+  __shared__ u32x4 abuf0[kChunks];
+  __shared__ u32x4 abuf1[kChunks];
+  __shared__ u32x4 bbuf0[kChunks];
+  __shared__ u32x4 bbuf1[kChunks];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int half = lane >> 5, col = lane & 31;
+  const int wm = wave / S::kWavesN, wn = wave % S::kWavesN;
+  const int tile = xcd_tile(blockIdx.x, p.tiles);
+  const int m0 = (tile / p.tiles_n) * TILE;
+  const int n0 = (tile % p.tiles_n) * TILE;
+
+  // Buffer descriptors start at the tile's first row and end with the last
+  // valid row's K-th element: chunks of rows past M (or N) read as zero.
+  const uint32_t a_row = (uint32_t)p.lda * 2, b_row = (uint32_t)p.ldb * 2;
+  const __amdgpu_buffer_rsrc_t arsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)((const char*)p.a + (size_t)m0 * a_row), (short)0,
+      (int)((uint32_t)(p.M - m0 - 1) * a_row + (uint32_t)p.K * 2), kBufferWord3);
+  const __amdgpu_buffer_rsrc_t brsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)((const char*)p.b + (size_t)n0 * b_row), (short)0,
+      (int)((uint32_t)(p.N - n0 - 1) * b_row + (uint32_t)p.K * 2), kBufferWord3);
+
+  // Wave load n fills LDS chunks 64n .. 64n+63 of a stage; chunk q holds row
+  // q / kPitch, column chunk q % kPitch (the pad chunk repeats column 0).
+  uint32_t aoff[kPer], boff[kPer];
+  int ccol[kPer];
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int q = (wave + j * kWaves) * 64 + lane;
+    const int r = q / kPitch;
+    ccol[j] = q % kPitch < kRowChunks ? q % kPitch : 0;
+    aoff[j] = (uint32_t)r * a_row + (uint32_t)ccol[j] * 16;
+    boff[j] = (uint32_t)r * b_row + (uint32_t)ccol[j] * 16;
+  }
+  // Stage s covers K columns 64s .. 64s+63; chunks past K read as zero.
+  auto load_stage = [&](u32x4* adst, u32x4* bdst, int s) __attribute__((always_inline)) {
+    const uint32_t koff = (uint32_t)s * (kBK * 2);
+    const int lim = (p.K - s * kBK) >> 3;          // valid column chunks in this stage
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int n = wave + j * kWaves;
+      if (j < kPer - 1 || n < kLoads) {
+        // (the offsets are cast to a plain uint32_t: in this template an
+        // array-element argument made the host pass drop the kernel's stub)
+        const bool ok = ccol[j] < lim;
+        const uint32_t ao = ok ? aoff[j] + koff : kOutOfRange;
+        const uint32_t bo = ok ? boff[j] + koff : kOutOfRange;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(arsrc, (void LDS_AS*)(adst + n * 64), 16,
+                                                 (uint32_t)ao, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(brsrc, (void LDS_AS*)(bdst + n * 64), 16,
+                                                 (uint32_t)bo, 0, 0, 0);
+      }
+    }
+  };
+
+  // acc[i][j]: rows m0 + wm*WTM + i*32 .. +31 (one per lane) by columns
+  // n0 + wn*WTN + j*32 .. +31 (in registers).
+  f32x16 acc[MB][NB];
+#pragma unroll
+  for (int i = 0; i < MB; ++i)
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  // Fragments of one k-substep (16 of K): MB of A and NB of B, two slots.
+  bf16x8 av[2][MB], bv[2][NB];
+  auto read = [&](const u32x4* ab, const u32x4* bb, int s, int slot)
+                  __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < MB; ++i)
+      av[slot][i] =
+          __builtin_bit_cast(bf16x8, ab[(wm * WTM + i * 32 + col) * kPitch + 2 * s + half]);
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+      bv[slot][j] =
+          __builtin_bit_cast(bf16x8, bb[(wn * WTN + j * 32 + col) * kPitch + 2 * s + half]);
+  };
+  auto mfma = [&](int slot) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < MB; ++i)
+#pragma unroll
+      for (int j = 0; j < NB; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bv[slot][j], av[slot][i], acc[i][j],
+                                                            0, 0, 0);
+  };
+  // Reads of the next substep interleaved with the MFMAs of this one.
+  auto interleave = [&]() __attribute__((always_inline)) {
+    constexpr int R = MB + NB, Q = MB * NB / R, E = MB * NB % R;
+#pragma unroll
+    for (int r = 0; r < E; ++r) {
+      __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedMFMA, Q + 1, 0);
+    }
+#pragma unroll
+    for (int r = E; r < R; ++r) {
+      __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedMFMA, Q, 0);
+    }
+  };
+  // One stage from buffer (ab, bb) whose substep 0 is already in slot 0:
+  // substeps 0..2 here; substep 3's MFMAs are left to after the barrier.
+  auto stage = [&](const u32x4* ab, const u32x4* bb) __attribute__((always_inline)) {
+    read(ab, bb, 1, 1);
+    mfma(0);
+    interleave();
+    read(ab, bb, 2, 0);
+    mfma(1);
+    interleave();
+    read(ab, bb, 3, 1);
+    mfma(0);
+    interleave();
+  };
+
+  const int nst = (p.K + kBK - 1) / kBK;
+  if (nst > 0) {
+    load_stage(abuf0, bbuf0, 0);
+    wait_vm();
+    __syncthreads();
+    if (nst > 1) load_stage(abuf1, bbuf1, 1);
+    read(abuf0, bbuf0, 0, 0);
+  }
+  // At the barrier that ends stage t every wave has finished reading buffer
+  // t % 2 (the barrier waits for LDS reads) and stage t + 1 has landed; the
+  // loads of stage t + 2 then go into buffer t % 2, and substep 3 of stage t
+  // runs while substep 0 of stage t + 1 is read (past the last stage that
+  // read is of unused data). Stages go in pairs so that every LDS access
+  // names one buffer; an odd last stage runs after the loop.
+  auto step = [&](u32x4* ab, u32x4* bb, u32x4* nab, u32x4* nbb, int t)
+                  __attribute__((always_inline)) {
+    stage(ab, bb);
+    __builtin_amdgcn_sched_barrier(0);   // keep substep 3's MFMAs after the barrier
+    wait_vm();
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+    if (t + 2 < nst) load_stage(ab, bb, t + 2);
+    read(nab, nbb, 0, 0);
+    mfma(1);
+  };
+  int t = 0;
+  for (; t + 1 < nst; t += 2) {
+    step(abuf0, bbuf0, abuf1, bbuf1, t);
+    step(abuf1, bbuf1, abuf0, bbuf0, t + 1);
+  }
+  if (t < nst) {
+    stage(abuf0, bbuf0);
+    mfma(1);
+  }
+
+  // Epilogue. Register 4g + e of acc[i][j] is column j*32 + 8g + 4*half + e
+  // of the wave's block (the MFMA output row index), for lane row col. N is a
+  // multiple of 4, so each run of 4 columns is wholly inside or outside.
+#pragma unroll
+  for (int i = 0; i < MB; ++i) {
+    const int m = m0 + wm * WTM + i * 32 + col;
+    if (m >= p.M) continue;
+    const float* zsrc = nullptr;
+    bool zbad = false;
+    if constexpr (GATHER) {
+      const int zr = p.zrow[m];
+      zbad = zr < 0 || zr >= p.Mz;
+      zsrc = p.z + (size_t)(zbad ? 0 : zr) * p.N;
+    } else {
+      zsrc = p.bias;
+    }
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int n = n0 + wn * WTN + j * 32 + 8 * g + 4 * half;
+        if (n >= p.N) continue;
+        f32x4 v = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
+                   acc[i][j][4 * g + 3]};
+        if (zsrc != nullptr) v += *(const f32x4*)(zsrc + n);
+        if (zbad) v = __builtin_nanf("");
+        if constexpr (OUT_F32) {
+          *(f32x4*)((float*)p.c + (size_t)m * p.N + n) = v;
+        } else {
+          const bf16x4 h = {(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
+          *(bf16x4*)((__bf16*)p.c + (size_t)m * p.N + n) = h;
+        }
+      }
+  }
+}
+
+template <int TILE>
+hipError_t launch_tile(const GemmParams& q, bool gather, bool out_f32, hipStream_t stream) {
+  const dim3 grid((unsigned)q.tiles), block(GemmShape<TILE>::kWaves * 64);
+  if (gather) {
+    if (out_f32) hipLaunchKernelGGL((ikbo_gemm_kernel<TILE, true, true>), grid, block, 0, stream, q);
+    else hipLaunchKernelGGL((ikbo_gemm_kernel<TILE, true, false>), grid, block, 0, stream, q);
+  } else {
+    if (out_f32) hipLaunchKernelGGL((ikbo_gemm_kernel<TILE, false, true>), grid, block, 0, stream, q);
+    else hipLaunchKernelGGL((ikbo_gemm_kernel<TILE, false, false>), grid, block, 0, stream, q);
+  }
+  return hipGetLastError();
+}
+
+namespace {
+
+// Tile edge: 256 when that still gives every CU a workgroup, else 128
+// (ATTN_GEMM_TILE=128|256, read once, forces one).
+int pick_tile(int M, int N) {
+  static const int forced = [] {
+    const char* e = getenv("ATTN_GEMM_TILE");
+    return e ? atoi(e) : 0;
+  }();
+  if (forced == 128 || forced == 256) return forced;
+  const int64_t t256 = (int64_t)((M + 255) / 256) * ((N + 255) / 256);
+  return t256 >= 256 ? 256 : 128;
+}
+
+}  // namespace
+
+// Launch one GEMM. A rows beyond what 32-bit buffer offsets reach are handled
+// by splitting M into chunks with their own base pointers.
+hipError_t launch_ikbo_gemm(GemmParams p, bool gather, bool out_f32, hipStream_t stream) {
+  if (p.M <= 0 || p.N <= 0) return hipSuccess;
+  const int tile = pick_tile(p.M, p.N);
+  const int64_t row = (int64_t)p.lda * 2;
+  int64_t max_rows = ((int64_t)0x7fffffff - (int64_t)p.K * 2) / (row > 0 ? row : 1) + 1;
+  max_rows = max_rows / 256 * 256;
+  if (max_rows < 256) return hipErrorInvalidValue;
+  p.tiles_n = (p.N + tile - 1) / tile;
+  const size_t esz = out_f32 ? 4 : 2;
+  for (int64_t m = 0; m < p.M; m += max_rows) {
+    GemmParams q = p;
+    q.M = (int)(p.M - m < max_rows ? p.M - m : max_rows);
+    q.a = (const char*)p.a + m * row;
+    q.c = (char*)p.c + (size_t)m * p.N * esz;
+    if (gather) q.zrow = p.zrow + m;
+    const int64_t tiles = (int64_t)((q.M + tile - 1) / tile) * q.tiles_n;
+    if (tiles > 0x7fffffff) return hipErrorInvalidValue;
+    q.tiles = (int)tiles;
+    const hipError_t err = tile == 256 ? launch_tile<256>(q, gather, out_f32, stream)
+                                       : launch_tile<128>(q, gather, out_f32, stream);
+    if (err != hipSuccess) return err;
+  }
+  return hipSuccess;
+}
+
+}  // namespace attn
