@@ -9,7 +9,10 @@ starts. Prints ONE JSON line. `value` is algorithmic TFLOP/s (4*d FLOPs per
 unmasked query/key pair) of the headline workload; `roofline` relates the
 kernel's average launch time to the bf16 MFMA peak; `cpu_baseline` times the
 float64 oracle on a bounded sample of the same workload on the host cores;
-`variants` holds the other workloads (the broadcast one also in GB/s).
+`variants` holds the other workloads (the broadcast one also in GB/s) and the
+in-kernel broadcast linear layer (both of its launches per step, 2 FLOPs per
+multiply-add of the decomposed products, with torch's hipBLASLt products and
+gather on the same inputs timed beside it for context).
 """
 from __future__ import annotations
 
@@ -285,6 +288,50 @@ def cpu_baseline(w: ai.AttnInputs, budget_s: float = 15.0) -> dict:
                       f"rows of {w.meta} ({flops:.3e} algorithmic FLOPs in {t_total:.1f} s)"}
 
 
+def linear_variant(name: str, steps: int) -> dict:
+    """Time the in-kernel broadcast linear layer on its workload (both launches: the
+    user half, then the candidate half with the gathered user rows), with sampled
+    rows checked against the float64 oracle."""
+    import oracle
+    import torch
+    import tiled_attention_attn_amd as taa
+    wl = ai.make_linear_workload(name, seed=0)
+    B_u, K_u = wl.x_user.shape
+    B_c, K_c = wl.x_cand.shape
+    N = wl.w.shape[0]
+    xu, xc, w = (to_device(x, "bf16") for x in (wl.x_user, wl.x_cand, wl.w))
+    bias = None if wl.bias is None else torch.from_numpy(wl.bias).cuda()
+    c2u = torch.from_numpy(wl.cand2user).cuda()
+    y = torch.empty((B_c, N), dtype=torch.bfloat16, device="cuda")
+    z = torch.empty((B_u, N), dtype=torch.float32, device="cuda")
+    ms = time_steps(lambda: taa.ikbo_linear(xu, xc, w, c2u, bias, y, z), steps, 3)
+    flops = 2 * (B_u * K_u + B_c * K_c) * N
+    nbytes = (2 * (wl.x_user.size + wl.x_cand.size + wl.w.size) + 4 * N + 4 * B_c
+              + 2 * B_c * N + 2 * 4 * B_u * N)
+    rng = np.random.default_rng(3)
+    rows = np.unique(np.concatenate([[0, B_c - 1], rng.integers(0, B_c, 30)]))
+    got = y[torch.from_numpy(rows).cuda()].double().cpu().numpy()
+    xuf, _, wf, bf = wl.f64()
+    ref = oracle.ikbo_linear(xuf, ai.to_f64(wl.x_cand[rows], "bf16"), wf, wl.cand2user[rows], bf)
+    # The same computation through torch: hipBLASLt products and a torch gather.
+    wu_t, wc_t = w[:, :K_u].t().contiguous(), w[:, K_u:].t().contiguous()
+    c2u_l = c2u.long()
+    bias_t = torch.zeros(N, device="cuda") if bias is None else bias
+    ms_torch = time_steps(
+        lambda: torch.mm(xc, wc_t) + (torch.mm(xu, wu_t).float() + bias_t)[c2u_l].bfloat16(),
+        max(5, steps // 2), 3)
+    tf = flops / (ms * 1e-3) / 1e12
+    return {"ms_per_step": round(ms, 5), "TFLOP/s": round(tf, 3),
+            "frac_of_peak": round(tf / PEAK_TFLOPS["bf16"], 4), "dtype": "bf16",
+            "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1),
+            "algorithmic_flops_per_step": flops, "algorithmic_bytes_per_step": nbytes,
+            "replication_equivalent_TFLOP/s":
+                round(2 * B_c * (K_u + K_c) * N / (ms * 1e-3) / 1e12, 3),
+            "torch_hipblaslt_decomposed_ms": round(ms_torch, 5),
+            "max_abs_err_sampled": float(np.abs(got - ref).max()),
+            "config": dict(wl.meta)}
+
+
 def traffic_for(workload: str, flops_ms: float):
     """HBM bytes per launch measured with rocprofv3 counters, if taken on this kernel source."""
     if not os.path.exists(TRAFFIC_FILE):
@@ -380,6 +427,9 @@ def main():
                 ent["replication_equivalent_GB/s"] = round(rep / (msv * 1e-3) / 1e9, 1)
             variants[name] = ent
             del rv
+            torch.cuda.empty_cache()
+        for name in sorted(ai.LINEAR_WORKLOADS):
+            variants[name] = linear_variant(name, max(5, args.steps // 2))
             torch.cuda.empty_cache()
         out["variants"] = variants
     print(json.dumps(out))

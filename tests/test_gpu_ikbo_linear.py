@@ -78,6 +78,9 @@ LINEAR_CASES = [
     (64, 2048, 1024, 512, 512, True, "bf16", False),
     (33, 1000, 136, 1032, 388, False, "f32", True),
     (6, 0, 64, 64, 128, True, "bf16", False),        # users only: z is still written
+    # grids large enough for the bigger tiles (128 x 128, then 256 x 256), ragged
+    (16, 2100, 136, 264, 2048, True, "bf16", True),
+    (40, 16400, 264, 136, 1028, True, "bf16", True),
 ]
 
 

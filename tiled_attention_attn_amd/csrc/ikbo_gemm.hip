@@ -16,8 +16,8 @@
 // Both steps run one kernel: C[M, N] = A[M, K] B[N, K]^T (+ bias or Z[zrow]).
 // Operands follow the linear-layer layout (B is [out, in], rows contiguous in
 // K), so both MFMA operands read 16 contiguous bytes per lane from LDS. A
-// workgroup owns a TILE x TILE output tile (256, or 128 when the grid of 256
-// tiles would leave CUs idle), split over its waves as blocks of
+// workgroup owns a TM x TN output tile (256 x 256, or a smaller one when that
+// grid would leave CUs idle), split over its waves as blocks of
 // v_mfma_f32_32x32x16_bf16 computed transposed (C^T = B A^T), so that each
 // lane holds one output row and runs of 4 consecutive columns. The wave tile
 // sets the LDS reads per MFMA (128 x 64 reads 6 fragments per 8 MFMAs). K advances 64 at a time through two LDS stages filled with
@@ -64,44 +64,49 @@ __device__ __forceinline__ int xcd_tile(int w, int T) {
 
 }  // namespace
 
-// Wave layout of a TILE x TILE workgroup tile: 128 -> 2 x 2 waves of 64 x 64
-// (two workgroups per CU); 256 -> 2 x 4 waves of 128 x 64 (one per CU, two
-// waves per SIMD). Both keep the accumulators in architected VGPRs.
-template <int TILE>
+// Tile configurations (TM x TN per workgroup, waves as WM x WN):
+//   0: 256 x 256, 2 x 4 waves of 128 x 64, one workgroup per CU;
+//   1: 128 x 128, 2 x 2 waves of 64 x 64, two per CU;
+//   2: 128 x 64,  2 x 2 waves of 64 x 32, two per CU (small grids).
+// All keep the accumulators in architected VGPRs.
+template <int CFG>
 struct GemmShape {
-  static constexpr int kWavesM = 2, kWavesN = TILE / 64;
+  static constexpr int TM = CFG == 0 ? 256 : 128;
+  static constexpr int TN = CFG == 0 ? 256 : CFG == 1 ? 128 : 64;
+  static constexpr int kWavesM = 2, kWavesN = CFG == 0 ? 4 : 2;
   static constexpr int kWaves = kWavesM * kWavesN;
-  static constexpr int MB = TILE / kWavesM / 32;   // 32 x 32 blocks per wave, rows
-  static constexpr int NB = TILE / kWavesN / 32;   // and columns
-  static constexpr int kPerCU = TILE == 128 ? 2 : 1;
+  static constexpr int MB = TM / kWavesM / 32;     // 32 x 32 blocks per wave, rows
+  static constexpr int NB = TN / kWavesN / 32;     // and columns
+  static constexpr int kPerCU = CFG == 0 ? 1 : 2;
 };
 
-template <int TILE, bool GATHER, bool OUT_F32>
-__global__ __launch_bounds__(TILE == 128 ? 256 : 512, TILE == 128 ? 2 : 1) void
+template <int CFG, bool GATHER, bool OUT_F32>
+__global__ __launch_bounds__(CFG == 0 ? 512 : 256, CFG == 0 ? 1 : 2) void
 ikbo_gemm_kernel(const GemmParams p) {
-  using S = GemmShape<TILE>;
-  static_assert(S::kWaves * 64 == (TILE == 128 ? 256 : 512) && S::kPerCU == (TILE == 128 ? 2 : 1),
+  using S = GemmShape<CFG>;
+  static_assert(S::kWaves * 64 == (CFG == 0 ? 512 : 256) && S::kPerCU == (CFG == 0 ? 1 : 2),
                 "launch bounds match the wave layout");
-  constexpr int kWaves = S::kWaves, MB = S::MB, NB = S::NB;
+  constexpr int kWaves = S::kWaves, MB = S::MB, NB = S::NB, TM = S::TM, TN = S::TN;
   constexpr int WTM = MB * 32, WTN = NB * 32;     // wave tile
-  constexpr int kChunks = TILE * kPitch;          // chunks per operand stage
-  constexpr int kLoads = kChunks / 64;            // wave-wide loads per operand stage
-  constexpr int kPer = (kLoads + kWaves - 1) / kWaves;
-  static_assert(kChunks % 64 == 0, "an operand stage is whole wave loads");
+  constexpr int kChunksA = TM * kPitch, kChunksB = TN * kPitch;   // chunks per stage
+  constexpr int kLoadsA = kChunksA / 64, kLoadsB = kChunksB / 64; // wave-wide loads
+  constexpr int kPerA = (kLoadsA + kWaves - 1) / kWaves;
+  constexpr int kPerB = (kLoadsB + kWaves - 1) / kWaves;
+  static_assert(kChunksA % 64 == 0 && kChunksB % 64 == 0, "a stage is whole wave loads");
   // Separate arrays per stage buffer: the compiler then knows that reads of
   // one buffer do not wait for direct-to-LDS loads still landing in the other.
-  __shared__ u32x4 abuf0[kChunks];
-  __shared__ u32x4 abuf1[kChunks];
-  __shared__ u32x4 bbuf0[kChunks];
-  __shared__ u32x4 bbuf1[kChunks];
+  __shared__ u32x4 abuf0[kChunksA];
+  __shared__ u32x4 abuf1[kChunksA];
+  __shared__ u32x4 bbuf0[kChunksB];
+  __shared__ u32x4 bbuf1[kChunksB];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int half = lane >> 5, col = lane & 31;
   const int wm = wave / S::kWavesN, wn = wave % S::kWavesN;
   const int tile = xcd_tile(blockIdx.x, p.tiles);
-  const int m0 = (tile / p.tiles_n) * TILE;
-  const int n0 = (tile % p.tiles_n) * TILE;
+  const int m0 = (tile / p.tiles_n) * TM;
+  const int n0 = (tile % p.tiles_n) * TN;
 
   // Buffer descriptors start at the tile's first row and end with the last
   // valid row's K-th element: chunks of rows past M (or N) read as zero.
@@ -114,47 +119,82 @@ ikbo_gemm_kernel(const GemmParams p) {
       (int)((uint32_t)(p.N - n0 - 1) * b_row + (uint32_t)p.K * 2), kBufferWord3);
 
   // Wave load n fills LDS chunks 64n .. 64n+63 of a stage; chunk q holds row
-  // q / kPitch, column chunk q % kPitch (the pad chunk repeats column 0).
-  uint32_t aoff[kPer], boff[kPer];
-  int ccol[kPer];
+  // q / kPitch, column chunk q % kPitch (chunk kRowChunks is the pad).
+  uint32_t aoff[kPerA], boff[kPerB];
+  int acol[kPerA], bcol[kPerB];
 #pragma unroll
-  for (int j = 0; j < kPer; ++j) {
+  for (int j = 0; j < kPerA; ++j) {
     const int q = (wave + j * kWaves) * 64 + lane;
-    const int r = q / kPitch;
-    ccol[j] = q % kPitch < kRowChunks ? q % kPitch : 0;
-    aoff[j] = (uint32_t)r * a_row + (uint32_t)ccol[j] * 16;
-    boff[j] = (uint32_t)r * b_row + (uint32_t)ccol[j] * 16;
+    acol[j] = q % kPitch;
+    aoff[j] = (uint32_t)(q / kPitch) * a_row + (uint32_t)acol[j] * 16;
   }
-  // Stage s covers K columns 64s .. 64s+63; chunks past K read as zero.
+#pragma unroll
+  for (int j = 0; j < kPerB; ++j) {
+    const int q = (wave + j * kWaves) * 64 + lane;
+    bcol[j] = q % kPitch;
+    boff[j] = (uint32_t)(q / kPitch) * b_row + (uint32_t)bcol[j] * 16;
+  }
+  // Stage s covers K columns 64s .. 64s+63; chunks past K, and the pad
+  // chunk of every row (column chunk kRowChunks), take the out-of-range
+  // offset: they read as zero without a memory request.
+  // (Offsets are passed as plain uint32_t values: in this template an
+  // array-element argument made the host pass drop the kernel's stub.)
   auto load_stage = [&](u32x4* adst, u32x4* bdst, int s) __attribute__((always_inline)) {
     const uint32_t koff = (uint32_t)s * (kBK * 2);
-    const int lim = (p.K - s * kBK) >> 3;          // valid column chunks in this stage
+    const int lim = min((p.K - s * kBK) >> 3, kRowChunks);   // valid column chunks
 #pragma unroll
-    for (int j = 0; j < kPer; ++j) {
+    for (int j = 0; j < kPerA; ++j) {
       const int n = wave + j * kWaves;
-      if (j < kPer - 1 || n < kLoads) {
-        // (the offsets are cast to a plain uint32_t: in this template an
-        // array-element argument made the host pass drop the kernel's stub)
-        const bool ok = ccol[j] < lim;
-        const uint32_t ao = ok ? aoff[j] + koff : kOutOfRange;
-        const uint32_t bo = ok ? boff[j] + koff : kOutOfRange;
+      if (j < kPerA - 1 || n < kLoadsA) {
+        const uint32_t o = acol[j] < lim ? aoff[j] + koff : kOutOfRange;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(arsrc, (void LDS_AS*)(adst + n * 64), 16,
-                                                 (uint32_t)ao, 0, 0, 0);
+                                                 (uint32_t)o, 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < kPerB; ++j) {
+      const int n = wave + j * kWaves;
+      if (j < kPerB - 1 || n < kLoadsB) {
+        const uint32_t o = bcol[j] < lim ? boff[j] + koff : kOutOfRange;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(brsrc, (void LDS_AS*)(bdst + n * 64), 16,
-                                                 (uint32_t)bo, 0, 0, 0);
+                                                 (uint32_t)o, 0, 0, 0);
       }
     }
   };
 
   // acc[i][j]: rows m0 + wm*WTM + i*32 .. +31 (one per lane) by columns
-  // n0 + wn*WTN + j*32 .. +31 (in registers).
+  // n0 + wn*WTN + j*32 .. +31 (in registers): register 4g + e holds column
+  // j*32 + 8g + 4*half + e of the wave's block (the MFMA output row index).
+  // The accumulators start from the row's addend (row zrow[m] of Z, or the
+  // bias), so the products are summed onto it and the epilogue only stores;
+  // these loads are issued before the first stage's and land with them. An
+  // out-of-range zrow starts the row at NaN, which the sum keeps. N is a
+  // multiple of 4: each run of 4 columns is wholly inside or outside.
   f32x16 acc[MB][NB];
 #pragma unroll
-  for (int i = 0; i < MB; ++i)
+  for (int i = 0; i < MB; ++i) {
+    const float* src = nullptr;
+    bool bad = false;
+    if constexpr (GATHER) {
+      const int m = m0 + wm * WTM + i * 32 + col;
+      const int zr = m < p.M ? p.zrow[m] : 0;
+      bad = zr < 0 || zr >= p.Mz;
+      src = p.z + (size_t)(bad ? 0 : zr) * p.N;
+    } else {
+      src = p.bias;
+    }
 #pragma unroll
     for (int j = 0; j < NB; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+      for (int g = 0; g < 4; ++g) {
+        const int n = n0 + wn * WTN + j * 32 + 8 * g + 4 * half;
+        f32x4 v = {0.f, 0.f, 0.f, 0.f};
+        if (src != nullptr && n < p.N) v = *(const f32x4*)(src + n);
+        if (bad) v = __builtin_nanf("");
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[i][j][4 * g + e] = v[e];
+      }
+  }
 
   // Fragments of one k-substep (16 of K): MB of A and NB of B, two slots.
   bf16x8 av[2][MB], bv[2][NB];
@@ -188,7 +228,7 @@ ikbo_gemm_kernel(const GemmParams p) {
 #pragma unroll
     for (int r = E; r < R; ++r) {
       __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(kSchedMFMA, Q, 0);
+      if constexpr (Q > 0) __builtin_amdgcn_sched_group_barrier(kSchedMFMA, Q, 0);
     }
   };
   // One stage from buffer (ab, bb) whose substep 0 is already in slot 0:
@@ -240,32 +280,22 @@ ikbo_gemm_kernel(const GemmParams p) {
     mfma(1);
   }
 
-  // Epilogue. Register 4g + e of acc[i][j] is column j*32 + 8g + 4*half + e
-  // of the wave's block (the MFMA output row index), for lane row col. N is a
-  // multiple of 4, so each run of 4 columns is wholly inside or outside.
+  // Epilogue: store the accumulators (rows past M and column runs past N
+  // are skipped). Staging the tile through LDS for row-contiguous stores
+  // measured slower: every workgroup reaches this point at once and the
+  // stores then run at the HBM write rate either way.
 #pragma unroll
   for (int i = 0; i < MB; ++i) {
     const int m = m0 + wm * WTM + i * 32 + col;
     if (m >= p.M) continue;
-    const float* zsrc = nullptr;
-    bool zbad = false;
-    if constexpr (GATHER) {
-      const int zr = p.zrow[m];
-      zbad = zr < 0 || zr >= p.Mz;
-      zsrc = p.z + (size_t)(zbad ? 0 : zr) * p.N;
-    } else {
-      zsrc = p.bias;
-    }
 #pragma unroll
     for (int j = 0; j < NB; ++j)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int n = n0 + wn * WTN + j * 32 + 8 * g + 4 * half;
         if (n >= p.N) continue;
-        f32x4 v = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
-                   acc[i][j][4 * g + 3]};
-        if (zsrc != nullptr) v += *(const f32x4*)(zsrc + n);
-        if (zbad) v = __builtin_nanf("");
+        const f32x4 v = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
+                         acc[i][j][4 * g + 3]};
         if constexpr (OUT_F32) {
           *(f32x4*)((float*)p.c + (size_t)m * p.N + n) = v;
         } else {
@@ -276,31 +306,37 @@ ikbo_gemm_kernel(const GemmParams p) {
   }
 }
 
-template <int TILE>
-hipError_t launch_tile(const GemmParams& q, bool gather, bool out_f32, hipStream_t stream) {
-  const dim3 grid((unsigned)q.tiles), block(GemmShape<TILE>::kWaves * 64);
+template <int CFG>
+hipError_t launch_cfg(const GemmParams& q, bool gather, bool out_f32, hipStream_t stream) {
+  const dim3 grid((unsigned)q.tiles), block(GemmShape<CFG>::kWaves * 64);
   if (gather) {
-    if (out_f32) hipLaunchKernelGGL((ikbo_gemm_kernel<TILE, true, true>), grid, block, 0, stream, q);
-    else hipLaunchKernelGGL((ikbo_gemm_kernel<TILE, true, false>), grid, block, 0, stream, q);
+    if (out_f32) hipLaunchKernelGGL((ikbo_gemm_kernel<CFG, true, true>), grid, block, 0, stream, q);
+    else hipLaunchKernelGGL((ikbo_gemm_kernel<CFG, true, false>), grid, block, 0, stream, q);
   } else {
-    if (out_f32) hipLaunchKernelGGL((ikbo_gemm_kernel<TILE, false, true>), grid, block, 0, stream, q);
-    else hipLaunchKernelGGL((ikbo_gemm_kernel<TILE, false, false>), grid, block, 0, stream, q);
+    if (out_f32) hipLaunchKernelGGL((ikbo_gemm_kernel<CFG, false, true>), grid, block, 0, stream, q);
+    else hipLaunchKernelGGL((ikbo_gemm_kernel<CFG, false, false>), grid, block, 0, stream, q);
   }
   return hipGetLastError();
 }
 
 namespace {
 
-// Tile edge: 256 when that still gives every CU a workgroup, else 128
-// (ATTN_GEMM_TILE=128|256, read once, forces one).
-int pick_tile(int M, int N) {
+int64_t cfg_tiles(int cfg, int64_t M, int64_t N) {
+  const int tm = cfg == 0 ? 256 : 128, tn = cfg == 0 ? 256 : cfg == 1 ? 128 : 64;
+  return ((M + tm - 1) / tm) * ((N + tn - 1) / tn);
+}
+
+// The largest tile that still gives every CU a workgroup (256 CUs); the
+// environment variable ATTN_GEMM_CFG=0|1|2 (read once) forces one.
+int pick_cfg(int M, int N) {
   static const int forced = [] {
-    const char* e = getenv("ATTN_GEMM_TILE");
-    return e ? atoi(e) : 0;
+    const char* e = getenv("ATTN_GEMM_CFG");
+    return e ? atoi(e) : -1;
   }();
-  if (forced == 128 || forced == 256) return forced;
-  const int64_t t256 = (int64_t)((M + 255) / 256) * ((N + 255) / 256);
-  return t256 >= 256 ? 256 : 128;
+  if (forced >= 0 && forced <= 2) return forced;
+  if (cfg_tiles(0, M, N) >= 256) return 0;
+  if (cfg_tiles(1, M, N) >= 256) return 1;
+  return 2;
 }
 
 }  // namespace
@@ -309,12 +345,13 @@ int pick_tile(int M, int N) {
 // by splitting M into chunks with their own base pointers.
 hipError_t launch_ikbo_gemm(GemmParams p, bool gather, bool out_f32, hipStream_t stream) {
   if (p.M <= 0 || p.N <= 0) return hipSuccess;
-  const int tile = pick_tile(p.M, p.N);
+  const int cfg = pick_cfg(p.M, p.N);
+  const int tm = cfg == 0 ? 256 : 128, tn = cfg == 0 ? 256 : cfg == 1 ? 128 : 64;
   const int64_t row = (int64_t)p.lda * 2;
   int64_t max_rows = ((int64_t)0x7fffffff - (int64_t)p.K * 2) / (row > 0 ? row : 1) + 1;
   max_rows = max_rows / 256 * 256;
   if (max_rows < 256) return hipErrorInvalidValue;
-  p.tiles_n = (p.N + tile - 1) / tile;
+  p.tiles_n = (p.N + tn - 1) / tn;
   const size_t esz = out_f32 ? 4 : 2;
   for (int64_t m = 0; m < p.M; m += max_rows) {
     GemmParams q = p;
@@ -322,11 +359,12 @@ hipError_t launch_ikbo_gemm(GemmParams p, bool gather, bool out_f32, hipStream_t
     q.a = (const char*)p.a + m * row;
     q.c = (char*)p.c + (size_t)m * p.N * esz;
     if (gather) q.zrow = p.zrow + m;
-    const int64_t tiles = (int64_t)((q.M + tile - 1) / tile) * q.tiles_n;
+    const int64_t tiles = (int64_t)((q.M + tm - 1) / tm) * q.tiles_n;
     if (tiles > 0x7fffffff) return hipErrorInvalidValue;
     q.tiles = (int)tiles;
-    const hipError_t err = tile == 256 ? launch_tile<256>(q, gather, out_f32, stream)
-                                       : launch_tile<128>(q, gather, out_f32, stream);
+    const hipError_t err = cfg == 0   ? launch_cfg<0>(q, gather, out_f32, stream)
+                           : cfg == 1 ? launch_cfg<1>(q, gather, out_f32, stream)
+                                      : launch_cfg<2>(q, gather, out_f32, stream);
     if (err != hipSuccess) return err;
   }
   return hipSuccess;
