@@ -35,6 +35,7 @@ HEADLINE = "gqa_causal_L16384"
 PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}   # MI355X dense MFMA / fp32 matrix peaks
 PEAK_HBM_GBS = 8000.0
 KERNEL_SOURCE = os.path.join(ROOT, "tiled_attention_attn_amd", "csrc", "attn_bf16.hip")
+LINEAR_SOURCE = os.path.join(ROOT, "tiled_attention_attn_amd", "csrc", "ikbo_gemm.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
@@ -114,8 +115,8 @@ def algorithmic_bytes(w) -> int:
     return total
 
 
-def kernel_source_hash() -> str:
-    with open(KERNEL_SOURCE, "rb") as f:
+def kernel_source_hash(path: str = KERNEL_SOURCE) -> str:
+    with open(path, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
@@ -288,7 +289,7 @@ def cpu_baseline(w: ai.AttnInputs, budget_s: float = 15.0) -> dict:
                       f"rows of {w.meta} ({flops:.3e} algorithmic FLOPs in {t_total:.1f} s)"}
 
 
-def linear_variant(name: str, steps: int) -> dict:
+def linear_variant(name: str, steps: int, warmup: int = 3) -> dict:
     """Time the in-kernel broadcast linear layer on its workload (both launches: the
     user half, then the candidate half with the gathered user rows), with sampled
     rows checked against the float64 oracle."""
@@ -304,7 +305,7 @@ def linear_variant(name: str, steps: int) -> dict:
     c2u = torch.from_numpy(wl.cand2user).cuda()
     y = torch.empty((B_c, N), dtype=torch.bfloat16, device="cuda")
     z = torch.empty((B_u, N), dtype=torch.float32, device="cuda")
-    ms = time_steps(lambda: taa.ikbo_linear(xu, xc, w, c2u, bias, y, z), steps, 3)
+    ms = time_steps(lambda: taa.ikbo_linear(xu, xc, w, c2u, bias, y, z), steps, warmup)
     flops = 2 * (B_u * K_u + B_c * K_c) * N
     nbytes = (2 * (wl.x_user.size + wl.x_cand.size + wl.w.size) + 4 * N + 4 * B_c
               + 2 * B_c * N + 2 * 4 * B_u * N)
@@ -332,14 +333,72 @@ def linear_variant(name: str, steps: int) -> dict:
             "config": dict(wl.meta)}
 
 
-def traffic_for(workload: str, flops_ms: float):
-    """HBM bytes per launch measured with rocprofv3 counters, if taken on this kernel source."""
+def linear_main(args) -> None:
+    """The linear layer as the measured workload: one JSON line, as for attention."""
+    ent = linear_variant(args.workload, args.steps, warmup=args.warmup)
+    cfg = ent.pop("config")
+    tf = ent["TFLOP/s"]
+    out = {
+        "metric": "in-kernel broadcast linear layer TFLOP/s (bf16, decomposed FLOPs)",
+        "value": tf, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ent["ms_per_step"], "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1), Philox streams)",
+        "config": {"workload": args.workload, **{k: v for k, v in cfg.items() if k != "kind"}},
+        "roofline": {"bound": "mfma", "achieved": tf, "peak": PEAK_TFLOPS["bf16"],
+                     "unit": "TFLOP/s", "frac": round(tf / PEAK_TFLOPS["bf16"], 4),
+                     "traffic": traffic_for(args.workload), "scope": "both launches of one step",
+                     "algorithmic_flops_per_launch": ent["algorithmic_flops_per_step"],
+                     "algorithmic_bytes_per_launch": ent["algorithmic_bytes_per_step"]},
+        "max_abs_err_sampled": ent["max_abs_err_sampled"],
+        "replication_equivalent_TFLOP/s": ent["replication_equivalent_TFLOP/s"],
+        "torch_hipblaslt_decomposed_ms": ent["torch_hipblaslt_decomposed_ms"],
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = linear_cpu_baseline(args.workload)
+    print(json.dumps(out))
+
+
+def linear_cpu_baseline(name: str, budget_s: float = 15.0) -> dict:
+    """The float64 oracle on random batches of candidates (replicated features, as it
+    stands), scaled to the layer's decomposed FLOPs per candidate."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        cores = os.cpu_count() or 1
+    wl = ai.make_linear_workload(name, seed=0)
+    B_u, K_u = wl.x_user.shape
+    B_c, K_c = wl.x_cand.shape
+    N = wl.w.shape[0]
+    xuf, _, wf, bf = wl.f64()
+    per_cand = 2 * (B_u * K_u + B_c * K_c) * N / B_c
+    rng = np.random.default_rng(123)
+    done, t_total = 0, 0.0
+    while t_total < budget_s and done < B_c:
+        rows = np.sort(rng.choice(B_c, size=256, replace=False))
+        xcf = ai.to_f64(wl.x_cand[rows], "bf16")
+        t0 = time.perf_counter()
+        oracle.ikbo_linear(xuf, xcf, wf, wl.cand2user[rows], bf)
+        t_total += time.perf_counter() - t0
+        done += len(rows)
+    return {"value": per_cand * done / t_total / 1e12, "unit": "TFLOP/s", "cores": int(cores),
+            "kind": "oracle",
+            "sample": f"{done} random candidates in batches of 256 ({t_total:.1f} s), scaled to "
+                      f"the layer's {per_cand:.4g} decomposed FLOPs per candidate"}
+
+
+def traffic_for(workload: str):
+    """HBM bytes per launch (per step for the linear layer) measured with rocprofv3
+    counters, if they were taken on the current kernel source."""
     if not os.path.exists(TRAFFIC_FILE):
         return None
     with open(TRAFFIC_FILE) as f:
         rec = json.load(f)
     ent = rec.get(workload)
-    if not ent or ent.get("kernel_source_sha256_16") != kernel_source_hash():
+    src = LINEAR_SOURCE if workload in ai.LINEAR_WORKLOADS else KERNEL_SOURCE
+    if not ent or ent.get("kernel_source_sha256_16") != kernel_source_hash(src):
         return None
     return ent.get("hbm_bytes_per_launch")
 
@@ -349,7 +408,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default=HEADLINE, choices=sorted(ai.WORKLOADS))
+    ap.add_argument("--workload", default=HEADLINE,
+                    choices=sorted(ai.WORKLOADS) + sorted(ai.LINEAR_WORKLOADS))
     ap.add_argument("--no-variants", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -375,6 +435,9 @@ def main():
         print(json.dumps({"copy_calibration_bytes_read": n, "bytes_written": n, "copies": 5}))
         return
 
+    if args.workload in ai.LINEAR_WORKLOADS:
+        linear_main(args)
+        return
     w = ai.make_workload(args.workload, seed=0)
     run = Runner(w)
     ms = time_steps(run, args.steps, args.warmup)
@@ -383,7 +446,7 @@ def main():
     tflops = flops / (ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.dtype]
     err = sampled_error(run)
-    traffic = traffic_for(args.workload, ms)
+    traffic = traffic_for(args.workload)
     out = {
         "metric": METRIC,
         "value": round(tflops, 3),
