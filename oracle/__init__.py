@@ -49,6 +49,13 @@ oracle computes it on the replicated features, the way it would be computed
 without the optimisation. ikbo_user_partial is the user half of that
 product plus the bias (the quantity computed once per user).
 
+Normalisation fused into attention: the TLX pages say normalisation can be
+fused into GEMM and attention kernels, saving a memory round trip, and list an
+article on it by title. The plain reading for this path: RMS normalisation of
+every query and key row over d with a gain vector each (q-norm and k-norm),
+x / sqrt(mean(x^2) + eps) * gamma, before the attention above; values are not
+normalised.
+
 Readings where the pages are silent (each is also listed with the design
 notes): scale defaults to 1/sqrt(d); the mask is additive -inf; causal is
 top-left (key j allowed iff j <= i); kv_len is one value per K/V batch entry,
@@ -70,7 +77,8 @@ import numpy as np
 
 __all__ = ["attention", "attention_rows", "attention_bcast", "attention_jagged",
            "attention_jagged_rows", "attention_block_sparse", "attention_block_sparse_rows",
-           "probabilities", "ikbo_linear", "ikbo_user_partial"]
+           "probabilities", "ikbo_linear", "ikbo_user_partial", "rms_norm",
+           "attention_qknorm", "attention_qknorm_rows"]
 
 
 def _default_scale(d: int, scale) -> float:
@@ -309,3 +317,34 @@ def ikbo_user_partial(x_user, w, bias=None):
     if bias is not None:
         z = z + np.asarray(bias, np.float64)[None, :]
     return z
+
+
+def rms_norm(x, gamma=None, eps=1e-6):
+    """Root-mean-square normalisation over the last axis, float64:
+    x / sqrt(mean(x^2) + eps) * gamma (gamma None: ones)."""
+    x = np.asarray(x, np.float64)
+    r = 1.0 / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps)
+    y = x * r
+    if gamma is not None:
+        y = y * np.asarray(gamma, np.float64)
+    return y
+
+
+def attention_qknorm(q, k, v, gamma_q=None, gamma_k=None, eps=1e-6, *, causal=False,
+                     kv_len=None, scale=None):
+    """Attention on RMS-normalised queries and keys: every row of q and of k is
+    normalised over d (with its own gain vector), v is used as given."""
+    return attention(rms_norm(q, gamma_q, eps), rms_norm(k, gamma_k, eps), v, causal=causal,
+                     kv_len=kv_len, scale=scale)
+
+
+def attention_qknorm_rows(q, k, v, b, h, rows, gamma_q=None, gamma_k=None, eps=1e-6, *,
+                          causal=False, kv_len=None, scale=None):
+    """Rows o[b, h, rows, :] of attention_qknorm (sampled checks at full size)."""
+    H, Hkv = q.shape[1], k.shape[1]
+    g = h // (H // Hkv)
+    qn = rms_norm(q[b:b + 1, h:h + 1], gamma_q, eps)
+    kn = rms_norm(k[b:b + 1, g:g + 1], gamma_k, eps)
+    kvl = None if kv_len is None else np.asarray(kv_len)[b:b + 1]
+    return attention_rows(qn, kn, np.asarray(v[b:b + 1, g:g + 1], np.float64), 0, 0, rows,
+                          causal=causal, kv_len=kvl, scale=scale)

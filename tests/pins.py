@@ -579,4 +579,81 @@ def pin_ikbo_candidate_permutation(impl):
     np.testing.assert_allclose(yp, y[perm], rtol=0, atol=1e-13)
 
 
+# --- normalisation fused into attention ------------------------------------------
+
+def pin_rms_norm_torch(impl):
+    """torch.nn.functional.rms_norm in float64, with and without a gain, two eps."""
+    import torch
+    x = _rand((3, 4, 7, 16), 71)
+    g = 1.0 + 0.3 * _rand((16,), 72)
+    for eps in (1e-6, 0.25):
+        for gamma in (g, None):
+            want = torch.nn.functional.rms_norm(
+                torch.from_numpy(x), (16,), None if gamma is None else torch.from_numpy(gamma),
+                eps).numpy()
+            np.testing.assert_allclose(impl.rms_norm(x, gamma, eps), want, rtol=0, atol=1e-13)
+
+
+def pin_rms_norm_closed_forms(impl):
+    """eps = 0: a constant row c becomes sign(c) * gamma; a one-hot row a e_t becomes
+    sign(a) sqrt(d) e_t * gamma; a zero row stays zero for eps > 0."""
+    d = 8
+    g = np.arange(1, d + 1, dtype=float)
+    for c in (3.0, -0.5):
+        np.testing.assert_allclose(impl.rms_norm(np.full((1, d), c), g, 0.0)[0], np.sign(c) * g,
+                                   rtol=1e-15, atol=0)
+    x = np.zeros((1, d))
+    x[0, 5] = -2.5
+    want = np.zeros(d)
+    want[5] = -math.sqrt(d) * g[5]
+    np.testing.assert_allclose(impl.rms_norm(x, g, 0.0)[0], want, rtol=1e-15, atol=0)
+    assert np.all(impl.rms_norm(np.zeros((2, d)), g, 1e-6) == 0)
+
+
+def pin_qknorm_torch_sdpa(impl):
+    """torch float64 SDPA (GQA, causal, kv_len mask) on rows normalised by torch's
+    rms_norm with the query gain on q and the key gain on k; v as given."""
+    import torch
+    F = torch.nn.functional
+    B, H, Hkv, Lq, Lk, d = 2, 4, 2, 9, 11, 8
+    q, k, v = (torch.from_numpy(_rand(s, 73 + i)) for i, s in
+               enumerate([(B, H, Lq, d), (B, Hkv, Lk, d), (B, Hkv, Lk, d)]))
+    gq, gk = (torch.from_numpy(1.0 + 0.3 * _rand((d,), 80 + i)) for i in range(2))
+    kv_len = np.array([11, 6])
+    eps = 1e-3
+    qn, kn = F.rms_norm(q, (d,), gq, eps), F.rms_norm(k, (d,), gk, eps)
+    mask = torch.arange(Lk)[None, :] < torch.from_numpy(kv_len)[:, None]
+    causal = torch.ones(Lq, Lk, dtype=torch.bool).tril()
+    attn_mask = mask[:, None, None, :] & causal[None, None]
+    want = F.scaled_dot_product_attention(qn, kn, v, attn_mask=attn_mask,
+                                          enable_gqa=True).numpy()
+    got = impl.attention_qknorm(q.numpy(), k.numpy(), v.numpy(), gq.numpy(), gk.numpy(), eps,
+                                causal=True, kv_len=kv_len)
+    np.testing.assert_allclose(got, want, rtol=0, atol=1e-12)
+
+
+def pin_qknorm_row_scale_invariance(impl):
+    """With eps = 0, scaling any query or key row by a positive factor changes nothing,
+    while scaling v scales the output."""
+    q, k, v = _rand((1, 2, 6, 8), 91), _rand((1, 2, 7, 8), 92), _rand((1, 2, 7, 8), 93)
+    a = np.exp(_rand((1, 2, 6, 1), 94))
+    b = np.exp(_rand((1, 2, 7, 1), 95))
+    o = impl.attention_qknorm(q, k, v, None, None, 0.0, causal=True)
+    np.testing.assert_allclose(impl.attention_qknorm(q * a, k * b, v, None, None, 0.0,
+                                                     causal=True), o, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(impl.attention_qknorm(q, k, 3.0 * v, None, None, 0.0,
+                                                     causal=True), 3.0 * o, rtol=0, atol=1e-12)
+
+
+def pin_qknorm_rows(impl):
+    """attention_qknorm_rows equals the same rows of attention_qknorm."""
+    q, k, v = _rand((2, 4, 9, 8), 96), _rand((2, 2, 10, 8), 97), _rand((2, 2, 10, 8), 98)
+    gq, gk = 1.0 + 0.2 * _rand((8,), 99), 1.0 + 0.2 * _rand((8,), 100)
+    full = impl.attention_qknorm(q, k, v, gq, gk, 1e-5, causal=True, kv_len=np.array([10, 4]))
+    rows = np.array([0, 3, 8])
+    got = impl.attention_qknorm_rows(q, k, v, 1, 3, rows, gq, gk, 1e-5, causal=True,
+                                     kv_len=np.array([10, 4]))
+    np.testing.assert_allclose(got, full[1, 3, rows], rtol=0, atol=1e-14)
+
+
 ALL_PINS = [v for n, v in sorted(globals().items()) if n.startswith("pin_")]

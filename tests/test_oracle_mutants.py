@@ -53,6 +53,18 @@ MUTANTS = {
                           "        pass\n"),
     "ikbo_no_nan": ("y[bad] = np.nan", "y[bad] = 0.0"),
     "ikbo_user_partial_wrong_columns": ("z = xu @ w[:, :K_u].T", "z = xu @ w[:, -K_u:].T"),
+    "rms_mean_as_sum": ("r = 1.0 / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps)",
+                        "r = 1.0 / np.sqrt(np.sum(x * x, axis=-1, keepdims=True) + eps)"),
+    "rms_eps_outside": ("r = 1.0 / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps)",
+                        "r = 1.0 / (np.sqrt(np.mean(x * x, axis=-1, keepdims=True)) + eps)"),
+    "rms_wrong_axis": ("r = 1.0 / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps)",
+                       "r = 1.0 / np.sqrt(np.mean(x * x, axis=-2, keepdims=True) + eps)"),
+    "rms_gamma_ignored": ("        y = y * np.asarray(gamma, np.float64)\n", "        pass\n"),
+    # (swapping the two gains is no mistake: scores depend on their product only)
+    "qknorm_key_gain_dropped": ("return attention(rms_norm(q, gamma_q, eps), rms_norm(k, gamma_k, eps), v,",
+                                "return attention(rms_norm(q, gamma_q, eps), rms_norm(k, None, eps), v,"),
+    "qknorm_v_normalised": ("rms_norm(k, gamma_k, eps), v, causal=causal,",
+                            "rms_norm(k, gamma_k, eps), rms_norm(v, None, eps), causal=causal,"),
     "jagged_heads_interleaved": ("o[qs:qs + lq, h], _ = _head_rows(q[qs:qs + lq, h], k[ks:ks + lk, g]",
                                  "o[qs:qs + lq, h], _ = _head_rows(q[qs:qs + lq, h], k[ks:ks + lk, h % Hkv]"),
 }
