@@ -11,7 +11,8 @@ tensors are those samples rounded to nearest-even and held as raw uint16 bit
 patterns.
 
 Stream ids: Q=0, K=1, V=2, integers (kv_len) = 3, block masks = 4; the
-linear layer's x_user=10, x_cand=11, w=12, bias=13, cand2user order=14.
+linear layer's x_user=10, x_cand=11, w=12, bias=13, cand2user order=14; the
+q/k norm gains 15 and row magnitudes 16.
 """
 from __future__ import annotations
 
@@ -84,6 +85,9 @@ class AttnInputs:
     kv_offsets: np.ndarray | None = None
     block_mask: np.ndarray | None = None
     blk: int = 0
+    gamma_q: np.ndarray | None = None   # q/k RMS-norm gains (float32 [d]), qknorm problems
+    gamma_k: np.ndarray | None = None
+    eps: float = 0.0
     scale: float | None = None
     meta: dict = field(default_factory=dict)
 
@@ -190,6 +194,32 @@ def make_block_sparse(B, H, Hkv, Lq, Lk, d, blk, *, dtype="bf16", causal=False, 
     return w
 
 
+def make_qknorm(B, H, Hkv, Lq, Lk, d, *, causal=False, seed=0, kv_len_range=None, eps=1e-6,
+                 scale=None, gains=True) -> AttnInputs:
+    """A dense bf16 problem for attention on RMS-normalised queries and keys: q and k rows
+    carry magnitudes 3 exp(0.5 N(0,1)) (so normalising matters), gains are
+    1 + 0.2 N(0,1) (float32), v is N(0,1)."""
+    rng = _gen(seed, STREAM_INT + 13)
+    q = normal_f32((B, H, Lq, d), seed, STREAM_Q)
+    k = normal_f32((B, Hkv, Lk, d), seed, STREAM_K)
+    q *= np.float32(3.0) * np.exp(np.float32(0.5) * rng.standard_normal((B, H, Lq, 1))).astype(np.float32)
+    k *= np.float32(3.0) * np.exp(np.float32(0.5) * rng.standard_normal((B, Hkv, Lk, 1))).astype(np.float32)
+    v = _draw((B, Hkv, Lk, d), "bf16", seed, STREAM_V)
+    kv_len = None
+    if kv_len_range is not None:
+        lo, hi = kv_len_range
+        kv_len = _gen(seed, STREAM_INT).integers(lo, hi + 1, size=B).astype(np.int32)
+    w = AttnInputs(f32_to_bf16_bits(q), f32_to_bf16_bits(k), v, "bf16", causal=causal,
+                   kv_len=kv_len, scale=scale)
+    if gains:
+        g = _gen(seed, STREAM_INT + 12).standard_normal((2, d)).astype(np.float32)
+        w.gamma_q = np.float32(1.0) + np.float32(0.2) * g[0]
+        w.gamma_k = np.float32(1.0) + np.float32(0.2) * g[1]
+    w.eps = float(eps)
+    w.meta = dict(kind="qknorm", B=B, H=H, Hkv=Hkv, Lq=Lq, Lk=Lk, d=d, eps=float(eps))
+    return w
+
+
 # The workloads the method is measured on: tiny fp32 parity case, dense causal,
 # in-kernel broadcast, kv_len-masked, long-sequence GQA causal, jagged causal
 # self-attention over sequences of uniformly drawn lengths, and fixed-block
@@ -210,6 +240,8 @@ WORKLOADS = {
     "block_sparse_L16384": dict(kind="block_sparse", B=1, H=16, Hkv=16, Lq=16384, Lk=16384,
                                 d=128, blk=256, window=8, n_global=1, dtype="bf16",
                                 causal=True),
+    "qknorm_gqa_causal_L16384": dict(kind="qknorm", B=1, H=32, Hkv=8, Lq=16384, Lk=16384,
+                                     d=128, dtype="bf16", causal=True),
 }
 
 
@@ -221,6 +253,10 @@ def make_workload(name: str, seed: int = 0) -> AttnInputs:
                           w.pop("d"), seed=seed, **w)
     if kind == "jagged":
         return make_jagged(w.pop("B"), w.pop("H"), w.pop("Hkv"), w.pop("d"), seed=seed, **w)
+    if kind == "qknorm":
+        w.pop("dtype")
+        return make_qknorm(w.pop("B"), w.pop("H"), w.pop("Hkv"), w.pop("Lq"), w.pop("Lk"),
+                           w.pop("d"), seed=seed, **w)
     if kind == "block_sparse":
         return make_block_sparse(w.pop("B"), w.pop("H"), w.pop("Hkv"), w.pop("Lq"), w.pop("Lk"),
                                  w.pop("d"), w.pop("blk"), seed=seed, **w)

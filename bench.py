@@ -12,7 +12,9 @@ float64 oracle on a bounded sample of the same workload on the host cores;
 `variants` holds the other workloads (the broadcast one also in GB/s) and the
 in-kernel broadcast linear layer (both of its launches per step, 2 FLOPs per
 multiply-add of the decomposed products, with torch's hipBLASLt products and
-gather on the same inputs timed beside it for context).
+gather on the same inputs timed beside it for context). A step of the
+q/k-normalised workload is both of its launches (key normalisation, then the
+attention pass with the query normalisation fused).
 """
 from __future__ import annotations
 
@@ -138,11 +140,19 @@ class Runner:
         self.qo = None if w.q_offsets is None else torch.from_numpy(w.q_offsets).cuda()
         self.ko = None if w.kv_offsets is None else torch.from_numpy(w.kv_offsets).cuda()
         self.bm = None if w.block_mask is None else torch.from_numpy(w.block_mask).cuda()
+        self.qknorm = w.meta.get("kind") == "qknorm"
+        if self.qknorm:
+            self.gq = None if w.gamma_q is None else torch.from_numpy(w.gamma_q).cuda()
+            self.gk = None if w.gamma_k is None else torch.from_numpy(w.gamma_k).cuda()
+            self.kn = torch.empty_like(self.k)
         import tiled_attention_attn_amd as taa
         self.taa = taa
 
     def __call__(self):
-        if self.bm is not None:
+        if self.qknorm:
+            self.taa.attn_fwd_qknorm(self.q, self.k, self.v, self.gq, self.gk, self.w.eps, self.o,
+                                     self.kn, causal=self.w.causal, kv_len=self.kv)
+        elif self.bm is not None:
             self.taa.attn_fwd_block_sparse(self.q, self.k, self.v, self.bm, self.w.blk, self.o,
                                            causal=self.w.causal, kv_len=self.kv)
         elif self.qo is not None:
@@ -191,7 +201,10 @@ def sampled_error(run: Runner, seed: int = 1, nrows: int = 4) -> float:
         kvl = None if w.kv_len is None else w.kv_len[u:u + 1]
         qf, kf, vf = (ai.to_f64(x, w.dtype) for x in
                       (w.q[b:b + 1, h:h + 1], w.k[u:u + 1, g:g + 1], w.v[u:u + 1, g:g + 1]))
-        if w.block_mask is not None:
+        if run.qknorm:
+            ref = oracle.attention_qknorm_rows(qf, kf, vf, 0, 0, rows, w.gamma_q, w.gamma_k,
+                                               w.eps, causal=w.causal, kv_len=kvl)
+        elif w.block_mask is not None:
             bm = w.block_mask[0:1] if w.block_mask.shape[0] == 1 else w.block_mask[h:h + 1]
             ref = oracle.attention_block_sparse_rows(qf, kf, vf, bm, w.blk, 0, 0, rows,
                                                      causal=w.causal, kv_len=kvl)

@@ -149,6 +149,35 @@ int attn_fwd_block_sparse(const void* q, const void* k, const void* v, void* o,
                           int dtype, void* stream);
 
 /*
+ * Attention on RMS-normalised queries and keys (q-norm and k-norm fused with
+ * the attention pass). The TLX pages ("How We Built TLX", Chinese translation,
+ * the part on what compiler-inferred layouts make possible; link list, "...
+ * Fusing Norms into GEMM and Attention via TLX") say normalisation can be
+ * fused into attention kernels to save an intermediate memory round trip, and
+ * name no norm; the reading here is RMS normalisation of every query and key
+ * row over d, each with its own gain:
+ *     q' = q / sqrt(mean(q^2) + eps) * gamma_q,  k' = k / sqrt(mean(k^2) + eps) * gamma_k
+ * then attn_fwd(q', k', v). Queries are normalised in registers as the
+ * attention kernel loads them (q' never reaches memory). Keys, which every
+ * workgroup of their head reads many times, are normalised once by a
+ * row-normalisation pass into k_norm, which the attention pass then reads.
+ *   q, k, v, o, B, H, Hkv, Lq, Lk, d, causal, kv_len, scale, stream  as attn_fwd
+ *   gamma_q, gamma_k  [d] fp32 device arrays, or NULL for ones
+ *   eps               finite, >= 0
+ *   k_norm            [B, Hkv, Lk, d] bf16 device workspace, written with the
+ *                     normalised keys (rounded to nearest-even); the caller owns
+ *                     it; it must not alias k
+ * Only dtype = ATTN_BF16 (else ATTN_EUNSUPPORTED). q' and k' are rounded to
+ * bf16 as MFMA operands. Two kernels are enqueued (keys, then attention).
+ * Errors as attn_fwd, plus ATTN_EINVAL for a bad eps, a misaligned gain or
+ * workspace, or a NULL / aliasing k_norm when there are keys.
+ */
+int attn_fwd_qknorm(const void* q, const void* k, const void* v, void* o,
+                    const float* gamma_q, const float* gamma_k, float eps, void* k_norm,
+                    int B, int H, int Hkv, int Lq, int Lk, int d,
+                    int causal, const int32_t* kv_len, float scale, int dtype, void* stream);
+
+/*
  * In-kernel broadcast linear layer: one linear layer over the concatenated
  * features [x_user[cand2user[c]], x_cand[c]] of every candidate c, computed
  * without replicating the user features. "How We Built TLX" (Chinese
@@ -185,7 +214,7 @@ int ikbo_linear(const void* x_user, const void* x_cand, const void* w, const flo
 const char* attn_strerror(int status);
 
 /* ABI version: major * 100 + minor (101: attn_fwd_jagged; 102: attn_fwd_block_sparse;
- * 103: ikbo_linear). */
+ * 103: ikbo_linear; 104: attn_fwd_qknorm). */
 int attn_version(void);
 
 #ifdef __cplusplus

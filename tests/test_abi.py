@@ -28,14 +28,14 @@ def lib():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == ["attn_fwd", "attn_fwd_bcast", "attn_fwd_block_sparse",
-                                    "attn_fwd_jagged", "attn_strerror", "attn_version",
-                                    "ikbo_linear"]
+                                    "attn_fwd_jagged", "attn_fwd_qknorm", "attn_strerror",
+                                    "attn_version", "ikbo_linear"]
 
 
 def test_library_exports_every_declared_symbol(lib):
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert lib.attn_version() == 103
+    assert lib.attn_version() == 104
 
 
 def test_strerror_covers_every_status(lib):
@@ -177,3 +177,30 @@ def ikbo(lib, xu=FAKE, xc=FAKE, w=FAKE, bias=None, c2u=FAKE, y=FAKE, z=FAKE, B_u
 ])
 def test_ikbo_linear_argument_checks(lib, kwargs, status):
     assert ikbo(lib, **kwargs) == status
+
+
+FAKE2 = ctypes.c_void_p(0x2000)
+
+
+def qknorm(lib, q=FAKE, k=FAKE, v=FAKE, o=FAKE, gq=None, gk=None, eps=1e-6, kn=FAKE2, B=1, H=2,
+           Hkv=1, Lq=64, Lk=64, d=128, causal=0, dtype=taa.ATTN_BF16):
+    return lib.attn_fwd_qknorm(q, k, v, o, gq, gk, eps, kn, B, H, Hkv, Lq, Lk, d, causal, None,
+                               0.0, dtype, None)
+
+
+@pytest.mark.parametrize("kwargs,status", [
+    (dict(dtype=taa.ATTN_F32), taa.ATTN_EUNSUPPORTED),   # bf16 only
+    (dict(d=96), taa.ATTN_EUNSUPPORTED),
+    (dict(eps=-1.0), taa.ATTN_EINVAL),
+    (dict(eps=float("inf")), taa.ATTN_EINVAL),
+    (dict(kn=None), taa.ATTN_EINVAL),                    # keys need a workspace
+    (dict(kn=FAKE), taa.ATTN_EINVAL),                    # ... that is not k
+    (dict(gq=ctypes.c_void_p(0x1004)), taa.ATTN_EINVAL), # misaligned gain
+    (dict(kn=ctypes.c_void_p(0x2008)), taa.ATTN_EINVAL),
+    (dict(H=3, Hkv=2), taa.ATTN_EINVAL),                 # the attention checks apply first
+    (dict(o=None), taa.ATTN_EINVAL),
+    (dict(B=0, kn=None), taa.ATTN_OK),                   # nothing to compute
+    (dict(Lq=0, kn=None), taa.ATTN_OK),
+])
+def test_attn_fwd_qknorm_argument_checks(lib, kwargs, status):
+    assert qknorm(lib, **kwargs) == status

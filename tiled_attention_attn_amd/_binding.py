@@ -51,6 +51,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.attn_fwd_block_sparse.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
                                           i32, i32, vp, f32, i32, vp]
     lib.attn_fwd_block_sparse.restype = i32
+    lib.attn_fwd_qknorm.argtypes = [vp, vp, vp, vp, vp, vp, f32, vp, i32, i32, i32, i32, i32,
+                                    i32, i32, vp, f32, i32, vp]
+    lib.attn_fwd_qknorm.restype = i32
     lib.ikbo_linear.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp]
     lib.ikbo_linear.restype = i32
     lib.attn_strerror.argtypes = [i32]
@@ -223,6 +226,38 @@ def attn_fwd_block_sparse(q, k, v, block_mask, blk, o=None, *, causal=False, kv_
                                      block_mask.shape[0], int(blk), B, H, k.shape[1], Lq, Lk, d,
                                      int(bool(causal)), _ptr(kv_len), float(scale),
                                      _dtype_code(q), _stream(stream)))
+    return o
+
+
+def attn_fwd_qknorm(q, k, v, gamma_q=None, gamma_k=None, eps=1e-6, o=None, k_norm=None, *,
+                    causal=False, kv_len=None, scale=0.0, stream=None):
+    """Attention on RMS-normalised queries and keys; returns o.
+
+    q [B,H,Lq,d], k/v [B,Hkv,Lk,d] bf16 as attn_fwd; gamma_q / gamma_k float32 [d] device
+    tensors or None (ones); k_norm: bf16 workspace shaped like k (allocated when None),
+    written with the normalised keys.
+    """
+    import torch
+    lib = load_library()
+    o = _prep(q, k, v, o, {"kv_len": kv_len})
+    B, H, Lq, d = q.shape
+    if k.shape[0] != B:
+        raise ValueError("k/v batch must equal q batch")
+    if kv_len is not None and kv_len.numel() != B:
+        raise ValueError("kv_len must have one entry per batch element")
+    for name, g in (("gamma_q", gamma_q), ("gamma_k", gamma_k)):
+        if g is not None and (g.dtype != torch.float32 or not g.is_cuda or not g.is_contiguous()
+                              or g.numel() != d):
+            raise ValueError(f"{name} must be a contiguous float32 device tensor with d entries")
+    if k_norm is None:
+        k_norm = torch.empty_like(k)
+    elif (k_norm.shape != k.shape or k_norm.dtype != k.dtype or not k_norm.is_cuda
+          or not k_norm.is_contiguous()):
+        raise ValueError("k_norm must be a contiguous device tensor shaped and typed like k")
+    _check(lib.attn_fwd_qknorm(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(gamma_q), _ptr(gamma_k),
+                               float(eps), _ptr(k_norm), B, H, k.shape[1], Lq, k.shape[2], d,
+                               int(bool(causal)), _ptr(kv_len), float(scale), _dtype_code(q),
+                               _stream(stream)))
     return o
 
 

@@ -11,6 +11,8 @@
 
 namespace attn {
 hipError_t launch_ikbo_gemm(GemmParams p, bool gather, bool out_f32, hipStream_t stream);
+hipError_t launch_rmsnorm_rows(const void* x, void* y, const float* gamma, float eps, int64_t rows,
+                               int D, hipStream_t stream);
 hipError_t launch_bf16(const Params& p, int D, bool causal, hipStream_t stream);
 hipError_t launch_f32(const Params& p, int D, bool causal, hipStream_t stream);
 bool plan_bf16(Params& p, int D, bool causal);
@@ -28,7 +30,8 @@ int check_and_launch(const void* q, const void* k, const void* v, void* o,
                      int d, int causal, const int32_t* kv_len, float scale, int dtype,
                      void* stream, const int32_t* q_offsets = nullptr,
                      const int32_t* kv_offsets = nullptr, const uint8_t* block_mask = nullptr,
-                     int blk = 0, int mask_heads = 0) {
+                     int blk = 0, int mask_heads = 0, const float* gamma_q = nullptr,
+                     int qnorm = 0, float eps = 0.f, bool check_only = false) {
   if (dtype != ATTN_F32 && dtype != ATTN_BF16) return ATTN_EUNSUPPORTED;
   if (d != 64 && d != 128) return ATTN_EUNSUPPORTED;
   if (NB < 0 || NKV < 0 || H < 0 || Lq < 0 || Lk < 0 || Hkv < 1) return ATTN_EINVAL;
@@ -59,6 +62,9 @@ int check_and_launch(const void* q, const void* k, const void* v, void* o,
     p.nKB = (Lk + blk - 1) / blk;
     p.mask_heads = mask_heads;
   }
+  p.qnorm = qnorm;
+  p.eps = eps;
+  p.gamma_q = gamma_q;
   p.NB = NB;
   p.NKV = NKV;
   p.H = H;
@@ -72,10 +78,12 @@ int check_and_launch(const void* q, const void* k, const void* v, void* o,
   hipError_t err;
   if (dtype == ATTN_BF16) {
     if (!attn::plan_bf16(p, d, is_causal)) return ATTN_EINVAL;
+    if (check_only) return ATTN_OK;
     err = attn::launch_bf16(p, d, is_causal, (hipStream_t)stream);
   } else {
     const int64_t T = (int64_t)NB * H * ((Lq + kF32Rows - 1) / kF32Rows);
     if (T > 0x7fffffff) return ATTN_EINVAL;
+    if (check_only) return ATTN_OK;
     p.T = (int)T;
     err = attn::launch_f32(p, d, is_causal, (hipStream_t)stream);
   }
@@ -127,6 +135,28 @@ int attn_fwd_jagged(const void* q, const void* k, const void* v, void* o,
     return ATTN_EINVAL;
   return check_and_launch(q, k, v, o, nullptr, B, B, H, Hkv, max_Lq, max_Lk, d, causal, nullptr,
                           scale, dtype, stream, q_offsets, kv_offsets);
+}
+
+int attn_fwd_qknorm(const void* q, const void* k, const void* v, void* o, const float* gamma_q,
+                    const float* gamma_k, float eps, void* k_norm, int B, int H, int Hkv, int Lq,
+                    int Lk, int d, int causal, const int32_t* kv_len, float scale, int dtype,
+                    void* stream) {
+  if (dtype != ATTN_BF16) return ATTN_EUNSUPPORTED;
+  if (d != 64 && d != 128) return ATTN_EUNSUPPORTED;
+  if (!isfinite(eps) || eps < 0.f) return ATTN_EINVAL;
+  if (!aligned16(gamma_q) || !aligned16(gamma_k) || !aligned16(k_norm)) return ATTN_EINVAL;
+  const bool keys = B > 0 && H > 0 && Lq > 0 && Lk > 0;   // keys to normalise
+  if (keys && (k_norm == nullptr || k == nullptr || k_norm == k)) return ATTN_EINVAL;
+  // Every other check (shared with attn_fwd) runs before the first launch.
+  const int pre = check_and_launch(q, k_norm, v, o, nullptr, B, B, H, Hkv, Lq, Lk, d, causal,
+                                   kv_len, scale, dtype, nullptr, nullptr, nullptr, nullptr, 0, 0,
+                                   gamma_q, 1, eps, /*check_only=*/true);
+  if (pre != ATTN_OK) return pre;
+  if (keys && attn::launch_rmsnorm_rows(k, k_norm, gamma_k, eps, (int64_t)B * Hkv * Lk, d,
+                                        (hipStream_t)stream) != hipSuccess)
+    return ATTN_ELAUNCH;
+  return check_and_launch(q, k_norm, v, o, nullptr, B, B, H, Hkv, Lq, Lk, d, causal, kv_len,
+                          scale, dtype, stream, nullptr, nullptr, nullptr, 0, 0, gamma_q, 1, eps);
 }
 
 int ikbo_linear(const void* x_user, const void* x_cand, const void* w, const float* bias,
@@ -189,6 +219,6 @@ const char* attn_strerror(int status) {
   }
 }
 
-int attn_version(void) { return 103; }
+int attn_version(void) { return 104; }
 
 }  // extern "C"

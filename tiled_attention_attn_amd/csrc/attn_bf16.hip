@@ -428,6 +428,28 @@ __global__ __launch_bounds__(W * 64, W == 4 ? 2 : 1) void attn_fwd_bf16_kernel(c
         if (ok) x = *(const u32x4*)(qrow + 16 * s + 8 * half);
         qreg[qb][s] = __builtin_bit_cast(bf16x8, x);
       }
+      // RMS normalisation of the query row (fused: the normalised queries
+      // never leave registers). The two lane halves hold the two halves of
+      // the row; the result is rounded to bf16 as the MFMA operand.
+      if (p.qnorm) {
+        float ss = 0.f;
+#pragma unroll
+        for (int s = 0; s < QS; ++s)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float v = (float)qreg[qb][s][e];
+            ss = __builtin_fmaf(v, v, ss);
+          }
+        ss = halves_sum(ss);
+        const float r = 1.0f / sqrtf(ss * (1.0f / D) + p.eps);
+#pragma unroll
+        for (int s = 0; s < QS; ++s)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float gam = p.gamma_q != nullptr ? p.gamma_q[16 * s + 8 * half + e] : 1.0f;
+            qreg[qb][s][e] = (__bf16)((float)qreg[qb][s][e] * r * gam);
+          }
+      }
     }
 
     f32x16 oacc[kQB][DB];

@@ -34,6 +34,11 @@ struct Params {
   int units;  // dense: (batch group, K/V head) units per chunk; causal tiles of a
               // chunk run row block by row block across its units (heaviest first)
   int waves;  // waves per workgroup of the bf16 kernel (4 or 8)
+  // Query RMS normalisation at load time (bf16 kernel): each query row x
+  // becomes x / sqrt(mean(x^2) + eps) * gamma_q (gamma_q may be nullptr: ones).
+  int qnorm;
+  float eps;
+  const float* gamma_q;      // [D] or nullptr
 };
 
 }  // namespace attn
