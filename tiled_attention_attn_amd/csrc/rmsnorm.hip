@@ -25,45 +25,57 @@ constexpr int kThreads = 256;
 
 }  // namespace
 
+// Each thread handles kRows rows of one lane position; their loads are all
+// issued before any arithmetic so that several are in flight per thread.
+constexpr int kRows = 4;
+
 template <int LPR>
 __global__ __launch_bounds__(kThreads) void rmsnorm_rows_kernel(const __bf16* __restrict__ x,
                                                                 __bf16* __restrict__ y,
                                                                 const float* __restrict__ gamma,
                                                                 float eps, int64_t rows) {
   constexpr int D = 8 * LPR;
-  const int64_t gid = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  const int64_t row = gid / LPR;
-  const int part = (int)(gid % LPR);
-  const bool ok = row < rows;
-  u32x4 raw = {0u, 0u, 0u, 0u};
-  if (ok) raw = *(const u32x4*)(x + row * D + part * 8);
-  const bf16x8 v = __builtin_bit_cast(bf16x8, raw);
-  float f[8];
-  float ss = 0.f;
+  constexpr int kRowsPerPass = kThreads / LPR;     // rows one block covers per pass
+  const int part = threadIdx.x % LPR;
+  const int64_t row0 = (int64_t)blockIdx.x * (kRowsPerPass * kRows) + threadIdx.x / LPR;
+  float g[8];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    f[e] = (float)v[e];
-    ss = __builtin_fmaf(f[e], f[e], ss);
+  for (int e = 0; e < 8; ++e) g[e] = gamma != nullptr ? gamma[part * 8 + e] : 1.0f;
+  u32x4 raw[kRows];
+#pragma unroll
+  for (int i = 0; i < kRows; ++i) {
+    const int64_t row = row0 + (int64_t)i * kRowsPerPass;
+    raw[i] = u32x4{0u, 0u, 0u, 0u};
+    if (row < rows) raw[i] = *(const u32x4*)(x + row * D + part * 8);
   }
-  // The LPR lanes of a row are consecutive and aligned: xor partners stay in it.
 #pragma unroll
-  for (int m = LPR / 2; m >= 1; m >>= 1) ss += __shfl_xor(ss, m);
-  const float r = 1.0f / sqrtf(ss * (1.0f / D) + eps);
-  bf16x8 out;
+  for (int i = 0; i < kRows; ++i) {
+    const int64_t row = row0 + (int64_t)i * kRowsPerPass;
+    const bf16x8 v = __builtin_bit_cast(bf16x8, raw[i]);
+    float f[8];
+    float ss = 0.f;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const float g = gamma != nullptr ? gamma[part * 8 + e] : 1.0f;
-    out[e] = (__bf16)(f[e] * r * g);
+    for (int e = 0; e < 8; ++e) {
+      f[e] = (float)v[e];
+      ss = __builtin_fmaf(f[e], f[e], ss);
+    }
+    // The LPR lanes of a row are consecutive and aligned: xor partners stay in it.
+#pragma unroll
+    for (int m = LPR / 2; m >= 1; m >>= 1) ss += __shfl_xor(ss, m);
+    const float r = 1.0f / sqrtf(ss * (1.0f / D) + eps);
+    bf16x8 out;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) out[e] = (__bf16)(f[e] * r * g[e]);
+    if (row < rows) *(u32x4*)(y + row * D + part * 8) = __builtin_bit_cast(u32x4, out);
   }
-  if (ok) *(u32x4*)(y + row * D + part * 8) = __builtin_bit_cast(u32x4, out);
 }
 
 // rows x D bf16, contiguous; D in {64, 128}.
 hipError_t launch_rmsnorm_rows(const void* x, void* y, const float* gamma, float eps, int64_t rows,
                                int D, hipStream_t stream) {
   if (rows <= 0) return hipSuccess;
-  const int lpr = D / 8;
-  const int64_t blocks = (rows * lpr + kThreads - 1) / kThreads;
+  const int64_t per_block = (int64_t)(kThreads / (D / 8)) * kRows;
+  const int64_t blocks = (rows + per_block - 1) / per_block;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
   const dim3 grid((unsigned)blocks), block(kThreads);
   if (D == 128)
