@@ -7,8 +7,10 @@ A step is one attention forward (one launch of the library's kernel) over the
 workload's synthetic, seeded inputs, which are resident in HBM before timing
 starts. Prints ONE JSON line. `value` is algorithmic TFLOP/s (4*d FLOPs per
 unmasked query/key pair) of the headline workload; `roofline` relates the
-kernel's average launch time to the bf16 MFMA peak; `cpu_baseline` times the
-float64 oracle on a bounded sample of the same workload on the host cores;
+kernel's average launch time to the bf16 MFMA peak (`cold_ms_per_step` is the
+median step time with L2 and the last-level cache flushed before each step);
+`cpu_baseline` times the float64 oracle on a bounded sample of the same
+workload on the host cores;
 `variants` holds the other workloads (the broadcast one also in GB/s) and the
 in-kernel broadcast linear layer (both of its launches per step, 2 FLOPs per
 multiply-add of the decomposed products, with torch's hipBLASLt products and
@@ -182,6 +184,24 @@ def time_steps(fn, steps: int, warmup: int) -> float:
     return start.elapsed_time(end) / steps
 
 
+def time_cold(fn, reps: int = 10) -> float:
+    """Median milliseconds of one step with cold caches: a 512 MiB write before each
+    step evicts L2 and the last-level cache; only the step itself is timed."""
+    import torch
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    times = []
+    for _ in range(reps):
+        flush.fill_(1)
+        start.record()
+        fn()
+        end.record()
+        torch.cuda.synchronize()
+        times.append(start.elapsed_time(end))
+    del flush
+    return float(np.median(times))
+
+
 def sampled_error(run: Runner, seed: int = 1, nrows: int = 4) -> float:
     """Max abs error of a few output rows against the float64 oracle."""
     import oracle
@@ -318,7 +338,9 @@ def linear_variant(name: str, steps: int, warmup: int = 3) -> dict:
     c2u = torch.from_numpy(wl.cand2user).cuda()
     y = torch.empty((B_c, N), dtype=torch.bfloat16, device="cuda")
     z = torch.empty((B_u, N), dtype=torch.float32, device="cuda")
-    ms = time_steps(lambda: taa.ikbo_linear(xu, xc, w, c2u, bias, y, z), steps, warmup)
+    step = lambda: taa.ikbo_linear(xu, xc, w, c2u, bias, y, z)  # noqa: E731
+    ms = time_steps(step, steps, warmup)
+    ms_cold = time_cold(step)
     flops = 2 * (B_u * K_u + B_c * K_c) * N
     nbytes = (2 * (wl.x_user.size + wl.x_cand.size + wl.w.size) + 4 * N + 4 * B_c
               + 2 * B_c * N + 2 * 4 * B_u * N)
@@ -335,7 +357,8 @@ def linear_variant(name: str, steps: int, warmup: int = 3) -> dict:
         lambda: torch.mm(xc, wc_t) + (torch.mm(xu, wu_t).float() + bias_t)[c2u_l].bfloat16(),
         max(5, steps // 2), 3)
     tf = flops / (ms * 1e-3) / 1e12
-    return {"ms_per_step": round(ms, 5), "TFLOP/s": round(tf, 3),
+    return {"ms_per_step": round(ms, 5), "cold_ms_per_step": round(ms_cold, 5),
+            "TFLOP/s": round(tf, 3),
             "frac_of_peak": round(tf / PEAK_TFLOPS["bf16"], 4), "dtype": "bf16",
             "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1),
             "algorithmic_flops_per_step": flops, "algorithmic_bytes_per_step": nbytes,
@@ -364,6 +387,7 @@ def linear_main(args) -> None:
                      "algorithmic_flops_per_launch": ent["algorithmic_flops_per_step"],
                      "algorithmic_bytes_per_launch": ent["algorithmic_bytes_per_step"]},
         "max_abs_err_sampled": ent["max_abs_err_sampled"],
+        "cold_ms_per_step": ent["cold_ms_per_step"],
         "replication_equivalent_TFLOP/s": ent["replication_equivalent_TFLOP/s"],
         "torch_hipblaslt_decomposed_ms": ent["torch_hipblaslt_decomposed_ms"],
     }
@@ -480,6 +504,7 @@ def main():
                      "algorithmic_flops_per_launch": flops,
                      "algorithmic_bytes_per_launch": nbytes},
         "max_abs_err_sampled": err,
+        "cold_ms_per_step": round(time_cold(run), 5),
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w)
@@ -493,7 +518,8 @@ def main():
             msv = time_steps(rv, max(5, args.steps // 2), 3)
             fv, bv = algorithmic_flops(wv), algorithmic_bytes(wv)
             tv = fv / (msv * 1e-3) / 1e12
-            ent = {"ms_per_step": round(msv, 5), "TFLOP/s": round(tv, 3),
+            ent = {"ms_per_step": round(msv, 5), "cold_ms_per_step": round(time_cold(rv, 5), 5),
+                   "TFLOP/s": round(tv, 3),
                    "frac_of_peak": round(tv / PEAK_TFLOPS[wv.dtype], 4), "dtype": wv.dtype,
                    "GB/s": round(bv / (msv * 1e-3) / 1e9, 1),
                    "max_abs_err_sampled": sampled_error(rv)}
