@@ -104,7 +104,12 @@ ikbo_gemm_kernel(const GemmParams p) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int half = lane >> 5, col = lane & 31;
   const int wm = wave / S::kWavesN, wn = wave % S::kWavesN;
-  const int tile = xcd_tile(blockIdx.x, p.tiles);
+  // Persistent grid: a workgroup runs tiles blockIdx.x, +G, +2G, ... (G =
+  // gridDim.x, a multiple of 8 whenever it is below the tile count, so the
+  // workgroup stays on one XCD); one tile's output stores drain while the
+  // next tile's loads and MFMAs run.
+  for (int wl = blockIdx.x; wl < p.tiles; wl += gridDim.x) {
+  const int tile = xcd_tile(wl, p.tiles);
   const int m0 = (tile / p.tiles_n) * TM;
   const int n0 = (tile % p.tiles_n) * TN;
 
@@ -304,11 +309,35 @@ ikbo_gemm_kernel(const GemmParams p) {
         }
       }
   }
+  __syncthreads();   // every wave is done with the LDS stages before the next tile loads
+  }
 }
 
+// Compute units of the current device (cached per device).
+static int device_cus() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess)
+      cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+// One workgroup per slot (kPerCU per CU) when there are more tiles than
+// slots; ATTN_GEMM_PERSIST=0 (read once) launches one workgroup per tile.
 template <int CFG>
 hipError_t launch_cfg(const GemmParams& q, bool gather, bool out_f32, hipStream_t stream) {
-  const dim3 grid((unsigned)q.tiles), block(GemmShape<CFG>::kWaves * 64);
+  static const bool persist = [] {
+    const char* e = getenv("ATTN_GEMM_PERSIST");
+    return !(e != nullptr && e[0] == '0');
+  }();
+  int nblk = q.tiles;
+  const int slots = (device_cus() * GemmShape<CFG>::kPerCU) & ~7;
+  if (persist && slots >= 8 && q.tiles > slots) nblk = slots;
+  const dim3 grid((unsigned)nblk), block(GemmShape<CFG>::kWaves * 64);
   if (gather) {
     if (out_f32) hipLaunchKernelGGL((ikbo_gemm_kernel<CFG, true, true>), grid, block, 0, stream, q);
     else hipLaunchKernelGGL((ikbo_gemm_kernel<CFG, true, false>), grid, block, 0, stream, q);
