@@ -138,3 +138,33 @@ def test_ikbo_linear_full_size_workload_sampled(lib):
     zgot = z[torch.from_numpy(users).cuda()].to(torch.float64).cpu().numpy()
     zref = oracle.ikbo_user_partial(xuf[users], wf, b)
     assert np.max(np.abs(zgot - zref)) <= 1e-3
+
+
+def test_persistent_grid_matches_one_workgroup_per_tile(lib, tmp_path):
+    """A grid of one workgroup per slot (several rounds of tiles each) and one
+    workgroup per tile (ATTN_GEMM_PERSIST=0, child process) compute every tile
+    with the same arithmetic: the outputs are equal bit for bit."""
+    import os
+    import subprocess
+    import sys
+    w = ai.make_linear(40, 30000, 264, 136, 1028, shuffle=True, seed=49)   # 118 x 5 tiles of 256
+    np.savez(tmp_path / "in.npz", xu=w.x_user, xc=w.x_cand, w=w.w, c2u=w.cand2user, b=w.bias)
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    script = (
+        "import sys, numpy as np, torch; sys.path.insert(0, %r); sys.path.insert(0, %r)\n"
+        "import tiled_attention_attn_amd as taa; from gpu_util import to_dev, from_dev, i32_dev\n"
+        "z = np.load(%r)\n"
+        "y, zz = taa.ikbo_linear(to_dev(z['xu'], 'bf16'), to_dev(z['xc'], 'bf16'), to_dev(z['w'], 'bf16'),\n"
+        "                        i32_dev(z['c2u']), torch.from_numpy(z['b']).cuda())\n"
+        "torch.cuda.synchronize(); np.save(%r, from_dev(y))\n"
+    )
+    outs = {}
+    for mode in ("1", "0"):
+        out = tmp_path / f"y{mode}.npy"
+        env = dict(os.environ, ATTN_GEMM_PERSIST=mode)
+        code = script % (root, os.path.join(root, "tests"), str(tmp_path / "in.npz"), str(out))
+        r = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True,
+                           timeout=300)
+        assert r.returncode == 0, r.stderr[-2000:]
+        outs[mode] = np.load(out)
+    assert np.array_equal(outs["1"], outs["0"], equal_nan=True)
