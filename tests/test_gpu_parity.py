@@ -267,24 +267,28 @@ def test_both_schedules_agree_with_oracle(lib, d, causal, tmp_path):
     assert max_err(outs["4"], outs["8"]) <= TOL["bf16"]
 
 
-@pytest.mark.parametrize("Lk,d,causal", [(1000, 64, False), (1000, 128, True), (8192, 128, False),
-                                         (8192, 128, True)],
+@pytest.mark.parametrize("Lk,d,causal,dtype", [(1000, 64, False, "bf16"), (1000, 128, True, "bf16"),
+                                               (8192, 128, False, "bf16"), (8192, 128, True, "bf16"),
+                                               (700, 64, False, "f32"), (700, 128, True, "f32")],
                          ids=lambda v: str(v))
-def test_reference_moves_on_every_tile(lib, Lk, d, causal):
+def test_reference_moves_on_every_tile(lib, Lk, d, causal, dtype):
     """Keys along the query direction, scaled up with the key index: each 64-key tile raises
     every row's maximum by about 12 (in base 2, after the softmax scale) over the last one,
     past the 2^8 bound of the lazy rescaling, so the exact path and the rescale of O run on
-    every tile (4-wave schedule at Lk=1000, 8-wave at 8192)."""
+    every tile (bf16: 4-wave schedule at Lk=1000, 8-wave at 8192; and the fp32 kernel)."""
     B, H, Lq = 1, 2, 300
     alpha = 12.0 / (np.log2(np.e) * np.sqrt(d))          # key scale added per 64 keys
     t = (alpha / 64.0) * np.arange(Lk, dtype=np.float64)
     q = 1.0 + 0.05 * ai.normal_f32((B, H, Lq, d), 61, 0)
     k = (t[None, None, :, None] * (1.0 + 0.01 * ai.normal_f32((B, H, Lk, d), 61, 1))).astype(np.float32)
     v = ai.normal_f32((B, H, Lk, d), 61, 2)
-    qb, kb, vb = (ai.f32_to_bf16_bits(np.asarray(x, dtype=np.float32)) for x in (q, k, v))
-    o = lib.attn_fwd(to_dev(qb, "bf16"), to_dev(kb, "bf16"), to_dev(vb, "bf16"), causal=causal)
+    if dtype == "bf16":
+        qs, ks, vs = (ai.f32_to_bf16_bits(np.asarray(x, dtype=np.float32)) for x in (q, k, v))
+    else:
+        qs, ks, vs = (np.asarray(x, dtype=np.float32) for x in (q, k, v))
+    o = lib.attn_fwd(to_dev(qs, dtype), to_dev(ks, dtype), to_dev(vs, dtype), causal=causal)
     import torch
     torch.cuda.synchronize()
-    want = oracle.attention(ai.to_f64(qb, "bf16"), ai.to_f64(kb, "bf16"), ai.to_f64(vb, "bf16"),
+    want = oracle.attention(ai.to_f64(qs, dtype), ai.to_f64(ks, dtype), ai.to_f64(vs, dtype),
                             causal=causal)
-    assert max_err(from_dev(o), want) <= TOL["bf16"]
+    assert max_err(from_dev(o), want) <= TOL[dtype]
