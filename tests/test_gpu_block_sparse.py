@@ -104,3 +104,28 @@ def test_block_sparse_full_size_workload_sampled(lib):
                                                  causal=w.causal)
         worst = max(worst, max_err(got, ref))
     assert worst <= TOL[w.dtype], worst
+
+
+@pytest.mark.parametrize("Lk,causal", [(1000, False), (4400, True)], ids=lambda v: str(v))
+def test_reference_moves_across_skipped_blocks(lib, Lk, causal):
+    """Scores grow by about 12 (base 2, after the softmax scale) per 64 keys, and about half
+    of the key blocks are skipped: the running maximum jumps past the lazy-rescale bound on
+    every kept tile, often right after a skipped block (4-wave schedule at Lk=1000, 8-wave at
+    4400)."""
+    import torch
+    B, H, Lq, d, blk = 1, 2, 600, 128, 128
+    alpha = 12.0 / (np.log2(np.e) * np.sqrt(d))
+    t = (alpha / 64.0) * np.arange(Lk, dtype=np.float64)
+    q = 1.0 + 0.05 * ai.normal_f32((B, H, Lq, d), 63, 0)
+    k = t[None, None, :, None] * (1.0 + 0.01 * ai.normal_f32((B, H, Lk, d), 63, 1))
+    v = ai.normal_f32((B, H, Lk, d), 63, 2)
+    qb, kb, vb = (ai.f32_to_bf16_bits(np.asarray(x, dtype=np.float32)) for x in (q, k, v))
+    nq, nk = -(-Lq // blk), -(-Lk // blk)
+    mask = (np.random.default_rng(63).random((H, nq, nk)) < 0.5).astype(np.uint8)
+    mask[:, :, 0] = 1                                   # every row keeps at least one block
+    o = lib.attn_fwd_block_sparse(to_dev(qb, "bf16"), to_dev(kb, "bf16"), to_dev(vb, "bf16"),
+                                  torch.from_numpy(mask).cuda(), blk, causal=causal)
+    torch.cuda.synchronize()
+    want = oracle.attention_block_sparse(ai.to_f64(qb, "bf16"), ai.to_f64(kb, "bf16"),
+                                         ai.to_f64(vb, "bf16"), mask, blk, causal=causal)
+    assert max_err(from_dev(o), want) <= TOL["bf16"]
