@@ -200,11 +200,12 @@ int attn_fwd_qknorm(const void* q, const void* k, const void* v, void* o,
  *             caller owns it (it is also a result) and it must not alias y
  * Products are exact in fp32 and accumulate in fp32. All pointers are device
  * pointers, 16-byte aligned. K_u and K_c are multiples of 8, N a multiple of
- * 4, K_u + K_c <= 2^20 and N * (K_u + K_c) * 2 < 2^31; either K may be 0 (that
- * half contributes nothing). B_c > 0 needs B_u >= 1. Two kernels are enqueued
- * on `stream` (z, then y); the call does not synchronise. Errors: ATTN_EINVAL
- * for a bad size, a NULL or misaligned pointer that the sizes make used;
- * ATTN_EUNSUPPORTED for another y_dtype; ATTN_ELAUNCH.
+ * 4, K_u + K_c <= 2^20, N * (K_u + K_c) * 2 < 2^31 and, when y is bf16 and
+ * B_c > 0, N < 2^22; either K may be 0 (that half contributes nothing).
+ * B_c > 0 needs B_u >= 1. Two kernels are enqueued on `stream` (z, then y);
+ * the call does not synchronise. Errors: ATTN_EINVAL for a bad size, a NULL
+ * or misaligned pointer that the sizes make used; ATTN_EUNSUPPORTED for
+ * another y_dtype; ATTN_ELAUNCH.
  */
 int ikbo_linear(const void* x_user, const void* x_cand, const void* w, const float* bias,
                 const int32_t* cand2user, void* y, float* z,

@@ -171,6 +171,7 @@ def ikbo(lib, xu=FAKE, xc=FAKE, w=FAKE, bias=None, c2u=FAKE, y=FAKE, z=FAKE, B_u
     (dict(bias=ctypes.c_void_p(0x1004)), taa.ATTN_EINVAL),
     (dict(K_u=1 << 20, K_c=8), taa.ATTN_EINVAL),           # K above 2^20
     (dict(K_u=65536, K_c=0, N=16384), taa.ATTN_EINVAL),    # weight past 2^31 bytes
+    (dict(K_u=0, K_c=0, N=1 << 22), taa.ATTN_EINVAL),      # bf16 tile rows past 2^31 bytes
     (dict(N=0), taa.ATTN_OK),
     (dict(B_u=0, B_c=0), taa.ATTN_OK),
     (dict(B_c=0, z=None), taa.ATTN_EINVAL),      # z is written whenever there are users

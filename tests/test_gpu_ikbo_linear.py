@@ -168,3 +168,47 @@ def test_persistent_grid_matches_one_workgroup_per_tile(lib, tmp_path):
         assert r.returncode == 0, r.stderr[-2000:]
         outs[mode] = np.load(out)
     assert np.array_equal(outs["1"], outs["0"], equal_nan=True)
+
+
+# Forced tile configuration -> (B_c, N) giving more tiles than slots (CUs x workgroups per CU).
+PERSIST_CFGS = {
+    "0": (16500, 1028),   # 256 x 256 tiles: 65 x 5 = 325 on 256 slots; a 4-column tail
+    "1": (8000, 1032),    # 128 x 128: 63 x 9 = 567 on 512 slots; an 8-column last tile
+    "2": (8000, 576),     # 128 x 64: 63 x 9 = 567 on 512 slots
+}
+
+
+@pytest.mark.parametrize("cfg", sorted(PERSIST_CFGS))
+def test_persistent_rounds_each_tile_config(lib, tmp_path, cfg):
+    """Each tile configuration forced (ATTN_GEMM_CFG, child process) on a grid with more
+    tiles than slots: workgroups run several tiles, interior and edge ones, and a tile's bf16
+    output is stored behind the next tile's first loads. Candidate depths K_c = 0, 40, 128,
+    200 give 0, 1, 2 and 4 stages of K (40 and 200 cut the last one). Against the oracle."""
+    import os
+    import subprocess
+    import sys
+    B_c, N = PERSIST_CFGS[cfg]
+    ws = [ai.make_linear(50, B_c, 64, K_c, N, shuffle=True, seed=51 + i)
+          for i, K_c in enumerate((0, 40, 128, 200))]
+    for i, w in enumerate(ws):
+        np.savez(tmp_path / f"in{i}.npz", xu=w.x_user, xc=w.x_cand, w=w.w, c2u=w.cand2user,
+                 b=w.bias)
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    script = (
+        "import sys, numpy as np, torch; sys.path.insert(0, %r); sys.path.insert(0, %r)\n"
+        "import tiled_attention_attn_amd as taa; from gpu_util import to_dev, from_dev, i32_dev\n"
+        "for i in range(%d):\n"
+        "    z = np.load('%s/in%%d.npz' %% i)\n"
+        "    y, zz = taa.ikbo_linear(to_dev(z['xu'], 'bf16'), to_dev(z['xc'], 'bf16'),\n"
+        "                            to_dev(z['w'], 'bf16'), i32_dev(z['c2u']),\n"
+        "                            torch.from_numpy(z['b']).cuda())\n"
+        "    torch.cuda.synchronize()\n"
+        "    np.save('%s/y%%d.npy' %% i, from_dev(y)); np.save('%s/z%%d.npy' %% i, from_dev(zz))\n"
+        "    print('case', i, 'done', flush=True)\n"
+    ) % (root, os.path.join(root, "tests"), len(ws), tmp_path, tmp_path, tmp_path)
+    env = dict(os.environ, ATTN_GEMM_CFG=cfg)
+    r = subprocess.run([sys.executable, "-c", script], env=env, capture_output=True, text=True,
+                       timeout=300)
+    assert r.returncode == 0, r.stderr[-2000:]
+    for i, w in enumerate(ws):
+        check(w, np.load(tmp_path / f"y{i}.npy"), np.load(tmp_path / f"z{i}.npy"))

@@ -171,6 +171,8 @@ int ikbo_linear(const void* x_user, const void* x_cand, const void* w, const flo
   if (N == 0 || (B_u == 0 && B_c == 0)) return ATTN_OK;
   // Weight rows are addressed with 32-bit offsets; activations are split by rows.
   if ((int64_t)(N - 1) * K * 2 + K * 2 > 0x7fffffff) return ATTN_EINVAL;
+  // bf16 output is stored with 32-bit offsets within 256-row tiles.
+  if (y_dtype == ATTN_BF16 && B_c > 0 && N >= (1 << 22)) return ATTN_EINVAL;
   if ((int64_t)B_c * N > ((int64_t)1 << 46) || (int64_t)B_u * N > ((int64_t)1 << 46))
     return ATTN_EINVAL;
   auto need = [](const void* ptr, bool used) { return !used || (ptr != nullptr && aligned16(ptr)); };

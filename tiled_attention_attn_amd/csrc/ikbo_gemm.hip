@@ -20,9 +20,12 @@
 // grid would leave CUs idle), split over its waves as blocks of
 // v_mfma_f32_32x32x16_bf16 computed transposed (C^T = B A^T), so that each
 // lane holds one output row and runs of 4 consecutive columns. The wave tile
-// sets the LDS reads per MFMA (128 x 64 reads 6 fragments per 8 MFMAs). K advances 64 at a time through two LDS stages filled with
-// direct-to-LDS buffer loads; LDS rows are padded by one 16-byte chunk so that
-// operand reads are free of bank conflicts.
+// sets the LDS reads per MFMA (128 x 64 reads 6 fragments per 8 MFMAs). K
+// advances 64 at a time through two LDS stages filled with direct-to-LDS
+// buffer loads; LDS rows are padded by one 16-byte chunk so that operand
+// reads are free of bank conflicts. With bf16 output, a tile's results wait
+// in registers until the next tile's first loads are issued and are stored
+// behind them, so that the stores drain while that tile computes.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <stdlib.h>
@@ -35,9 +38,11 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 #define LDS_AS __attribute__((address_space(3)))
 
@@ -53,6 +58,13 @@ constexpr int kSchedMFMA = 0x008, kSchedDSRead = 0x100;
 
 // s_waitcnt vmcnt(0): wait for this wave's direct-to-LDS loads.
 __device__ __forceinline__ void wait_vm() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// s_waitcnt vmcnt(N): at most N of this wave's vector memory operations (loads
+// and stores, which gfx9 counts together and retires in issue order) remain.
+template <int N>
+__device__ __forceinline__ void wait_vm_n() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
 
 // Workgroups are dispatched round-robin over the 8 XCDs (XCD x runs ids x,
 // x+8, ...). Give each XCD a contiguous range of tiles, so the column tiles
@@ -100,16 +112,51 @@ ikbo_gemm_kernel(const GemmParams p) {
   __shared__ u32x4 bbuf0[kChunksB];
   __shared__ u32x4 bbuf1[kChunksB];
 
-  const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int half = lane >> 5, col = lane & 31;
   const int wm = wave / S::kWavesN, wn = wave % S::kWavesN;
   // Persistent grid: a workgroup runs tiles blockIdx.x, +G, +2G, ... (G =
   // gridDim.x, a multiple of 8 whenever it is below the tile count, so the
-  // workgroup stays on one XCD); one tile's output stores drain while the
-  // next tile's loads and MFMAs run.
+  // workgroup stays on one XCD).
+  // bf16 output: a whole tile's results wait in registers (converted and
+  // lane-swapped) until the next tile's addend and first two stages of loads
+  // are issued; its stores follow them and drain under that tile's first two
+  // stages. Edge tiles (rows past M or columns past N) store at once. gfx9
+  // counts loads and stores in one counter (vmcnt) and retires them in issue
+  // order, so a wave waits for a stage with a count that leaves the later
+  // stores outstanding; every store is therefore issued, whatever the tile.
+  constexpr int kMinLoads = kLoadsA / kWaves + kLoadsB / kWaves;  // per wave and stage
+  constexpr int kStores = MB * NB * 2;                            // 16-byte stores per wave
+  u32x4 pend[MB][NB][2];
+  int pm0 = -1, pn0 = 0;
+  const uint32_t crow = (uint32_t)p.N * 2;
+  // One offset per lane: row wm*WTM + col, column wn*WTN + 8*half of the
+  // tile; block row i goes in the scalar offset, the column block in the
+  // instruction's immediate. With nothing pending (pm0 < 0) the range is
+  // empty and the stores are dropped.
+  auto store_pending = [&](int col, int half) __attribute__((always_inline)) {
+    const uint32_t svoff = (uint32_t)(wm * WTM + col) * crow + (uint32_t)(wn * WTN + 8 * half) * 2;
+    const bool any = pm0 >= 0;
+    const __amdgpu_buffer_rsrc_t crs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)((char*)p.c + (any ? (size_t)pm0 * crow + (size_t)pn0 * 2 : 0)), (short)0,
+        any ? (int)((uint32_t)TM * crow) : 0, kBufferWord3);
+#pragma unroll
+    for (int i = 0; i < MB; ++i)
+#pragma unroll
+      for (int j = 0; j < NB; ++j)
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+          __builtin_amdgcn_raw_buffer_store_b128(pend[i][j][q], crs, svoff + (j * 32 + 16 * q) * 2,
+                                                 (int)((uint32_t)(i * 32) * crow), 0);
+  };
   for (int wl = blockIdx.x; wl < p.tiles; wl += gridDim.x) {
   const int tile = xcd_tile(wl, p.tiles);
+  // Per-lane indices are recomputed every tile (the empty asm hides that
+  // they are loop-invariant): hoisted out of the tile loop they would stay
+  // live across the tile boundary, where the pending output needs the room.
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
+  const int lane = tid & 63;
+  const int half = lane >> 5, col = lane & 31;
   const int m0 = (tile / p.tiles_n) * TM;
   const int n0 = (tile % p.tiles_n) * TN;
 
@@ -125,33 +172,35 @@ ikbo_gemm_kernel(const GemmParams p) {
 
   // Wave load n fills LDS chunks 64n .. 64n+63 of a stage; chunk q holds row
   // q / kPitch, column chunk q % kPitch (chunk kRowChunks is the pad).
+  // The pad chunk of every row (column chunk kRowChunks) takes the
+  // out-of-range offset: it reads as zero without a memory request.
   uint32_t aoff[kPerA], boff[kPerB];
-  int acol[kPerA], bcol[kPerB];
 #pragma unroll
   for (int j = 0; j < kPerA; ++j) {
     const int q = (wave + j * kWaves) * 64 + lane;
-    acol[j] = q % kPitch;
-    aoff[j] = (uint32_t)(q / kPitch) * a_row + (uint32_t)acol[j] * 16;
+    const int c = q % kPitch;
+    aoff[j] = c < kRowChunks ? (uint32_t)(q / kPitch) * a_row + (uint32_t)c * 16 : kOutOfRange;
   }
 #pragma unroll
   for (int j = 0; j < kPerB; ++j) {
     const int q = (wave + j * kWaves) * 64 + lane;
-    bcol[j] = q % kPitch;
-    boff[j] = (uint32_t)(q / kPitch) * b_row + (uint32_t)bcol[j] * 16;
+    const int c = q % kPitch;
+    boff[j] = c < kRowChunks ? (uint32_t)(q / kPitch) * b_row + (uint32_t)c * 16 : kOutOfRange;
   }
-  // Stage s covers K columns 64s .. 64s+63; chunks past K, and the pad
-  // chunk of every row (column chunk kRowChunks), take the out-of-range
-  // offset: they read as zero without a memory request.
+  // Stage s covers K columns 64s .. 64s+63; in a last stage cut by K, the
+  // chunks past K take the out-of-range offset too.
   // (Offsets are passed as plain uint32_t values: in this template an
   // array-element argument made the host pass drop the kernel's stub.)
   auto load_stage = [&](u32x4* adst, u32x4* bdst, int s) __attribute__((always_inline)) {
     const uint32_t koff = (uint32_t)s * (kBK * 2);
+    const bool ragged = p.K - s * kBK < kBK;                  // chunks past K in this stage
     const int lim = min((p.K - s * kBK) >> 3, kRowChunks);   // valid column chunks
 #pragma unroll
     for (int j = 0; j < kPerA; ++j) {
       const int n = wave + j * kWaves;
       if (j < kPerA - 1 || n < kLoadsA) {
-        const uint32_t o = acol[j] < lim ? aoff[j] + koff : kOutOfRange;
+        uint32_t o = aoff[j] + koff;   // pad lanes stay out of range
+        if (ragged && (n * 64 + lane) % kPitch >= lim) o = kOutOfRange;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(arsrc, (void LDS_AS*)(adst + n * 64), 16,
                                                  (uint32_t)o, 0, 0, 0);
       }
@@ -160,7 +209,8 @@ ikbo_gemm_kernel(const GemmParams p) {
     for (int j = 0; j < kPerB; ++j) {
       const int n = wave + j * kWaves;
       if (j < kPerB - 1 || n < kLoadsB) {
-        const uint32_t o = bcol[j] < lim ? boff[j] + koff : kOutOfRange;
+        uint32_t o = boff[j] + koff;
+        if (ragged && (n * 64 + lane) % kPitch >= lim) o = kOutOfRange;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(brsrc, (void LDS_AS*)(bdst + n * 64), 16,
                                                  (uint32_t)o, 0, 0, 0);
       }
@@ -176,15 +226,20 @@ ikbo_gemm_kernel(const GemmParams p) {
   // out-of-range zrow starts the row at NaN, which the sum keeps. N is a
   // multiple of 4: each run of 4 columns is wholly inside or outside.
   f32x16 acc[MB][NB];
+  int zr[MB];   // the row indices first, so that their loads share one wait
+#pragma unroll
+  for (int i = 0; i < MB; ++i) {
+    const int m = m0 + wm * WTM + i * 32 + col;
+    zr[i] = GATHER && m < p.M ? p.zrow[m] : 0;
+  }
 #pragma unroll
   for (int i = 0; i < MB; ++i) {
     const float* src = nullptr;
     bool bad = false;
     if constexpr (GATHER) {
-      const int m = m0 + wm * WTM + i * 32 + col;
-      const int zr = m < p.M ? p.zrow[m] : 0;
-      bad = zr < 0 || zr >= p.Mz;
-      src = p.z + (size_t)(bad ? 0 : zr) * p.N;
+      bad = zr[i] < 0 || zr[i] >= p.Mz;
+      const int zr_ = zr[i];
+      src = p.z + (size_t)(bad ? 0 : zr_) * p.N;
     } else {
       src = p.bias;
     }
@@ -251,13 +306,31 @@ ikbo_gemm_kernel(const GemmParams p) {
   };
 
   const int nst = (p.K + kBK - 1) / kBK;
-  if (nst > 0) {
-    load_stage(abuf0, bbuf0, 0);
-    wait_vm();
-    __syncthreads();
-    if (nst > 1) load_stage(abuf1, bbuf1, 1);
-    read(abuf0, bbuf0, 0, 0);
+  if (nst > 0) load_stage(abuf0, bbuf0, 0);
+  if (nst > 1) load_stage(abuf1, bbuf1, 1);
+  __builtin_amdgcn_sched_barrier(0);
+  if constexpr (!OUT_F32) store_pending(col, half);   // the previous tile's, after the loads
+  __builtin_amdgcn_sched_barrier(0);
+  // Workgroup barrier without __syncthreads()'s release fence, which would
+  // wait for the pending stores too. Each wave has waited (vmcnt) for its own
+  // loads of the stage about to be read and waits here for its LDS reads
+  // (lgkmcnt); the empty asm statements keep the compiler from moving memory
+  // accesses across the barrier.
+  auto lds_barrier = [&]() __attribute__((always_inline)) {
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0); vmcnt, expcnt unchanged
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+  // Wait for the addend and stage 0: what may remain is stage 1's loads (at
+  // least kMinLoads per wave) and the pending stores (at least kStores).
+  if constexpr (!OUT_F32) {
+    if (nst > 1) wait_vm_n<kMinLoads + kStores>(); else wait_vm_n<kStores>();
+  } else {
+    if (nst > 1) wait_vm_n<kMinLoads>(); else wait_vm();
   }
+  lds_barrier();
+  if (nst > 0) read(abuf0, bbuf0, 0, 0);
   // At the barrier that ends stage t every wave has finished reading buffer
   // t % 2 (the barrier waits for LDS reads) and stage t + 1 has landed; the
   // loads of stage t + 2 then go into buffer t % 2, and substep 3 of stage t
@@ -268,8 +341,8 @@ ikbo_gemm_kernel(const GemmParams p) {
                   __attribute__((always_inline)) {
     stage(ab, bb);
     __builtin_amdgcn_sched_barrier(0);   // keep substep 3's MFMAs after the barrier
-    wait_vm();
-    __syncthreads();
+    if (!OUT_F32 && t == 0) wait_vm_n<kStores>(); else wait_vm();
+    lds_barrier();
     __builtin_amdgcn_sched_barrier(0);
     if (t + 2 < nst) load_stage(ab, bb, t + 2);
     read(nab, nbb, 0, 0);
@@ -285,32 +358,75 @@ ikbo_gemm_kernel(const GemmParams p) {
     mfma(1);
   }
 
-  // Epilogue: store the accumulators (rows past M and column runs past N
-  // are skipped). Staging the tile through LDS for row-contiguous stores
-  // measured slower: every workgroup reaches this point at once and the
-  // stores then run at the HBM write rate either way.
+  // Epilogue. fp32 output: store the accumulators (rows past M and column
+  // runs past N are skipped). bf16 output: convert them into the pending
+  // registers.
+  if constexpr (OUT_F32) {
 #pragma unroll
-  for (int i = 0; i < MB; ++i) {
-    const int m = m0 + wm * WTM + i * 32 + col;
-    if (m >= p.M) continue;
+    for (int i = 0; i < MB; ++i) {
+      const int m = m0 + wm * WTM + i * 32 + col;
+      if (m >= p.M) continue;
 #pragma unroll
-    for (int j = 0; j < NB; ++j)
+      for (int j = 0; j < NB; ++j)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int n = n0 + wn * WTN + j * 32 + 8 * g + 4 * half;
-        if (n >= p.N) continue;
-        const f32x4 v = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
-                         acc[i][j][4 * g + 3]};
-        if constexpr (OUT_F32) {
+        for (int g = 0; g < 4; ++g) {
+          const int n = n0 + wn * WTN + j * 32 + 8 * g + 4 * half;
+          if (n >= p.N) continue;
+          const f32x4 v = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
+                           acc[i][j][4 * g + 3]};
           *(f32x4*)((float*)p.c + (size_t)m * p.N + n) = v;
-        } else {
-          const bf16x4 h = {(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
-          *(bf16x4*)((__bf16*)p.c + (size_t)m * p.N + n) = h;
         }
+    }
+  } else {
+    // Lanes l and l + 32 hold the same row: lane l columns 8g .. 8g+3 of
+    // each group g, lane l + 32 columns 8g+4 .. 8g+7. One lane-half swap per
+    // pair of groups (2q, 2q+1) gives lane l all eight columns of group 2q
+    // and lane l + 32 those of group 2q+1, for 16-byte stores.
+#pragma unroll
+    for (int i = 0; i < MB; ++i)
+#pragma unroll
+      for (int j = 0; j < NB; ++j)
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          uint32_t w[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const bf16x2 h = {(__bf16)acc[i][j][8 * q + 2 * e], (__bf16)acc[i][j][8 * q + 2 * e + 1]};
+            w[e] = __builtin_bit_cast(uint32_t, h);
+          }
+          const auto s0 = __builtin_amdgcn_permlane32_swap(w[0], w[2], false, false);
+          const auto s1 = __builtin_amdgcn_permlane32_swap(w[1], w[3], false, false);
+          pend[i][j][q] = u32x4{s0[0], s1[0], s0[1], s1[1]};
+        }
+    if (m0 + TM <= p.M && n0 + TN <= p.N) {
+      pm0 = m0;
+      pn0 = n0;
+    } else {
+      pm0 = -1;
+#pragma unroll
+      for (int i = 0; i < MB; ++i) {
+        const int m = m0 + wm * WTM + i * 32 + col;
+#pragma unroll
+        for (int j = 0; j < NB; ++j)
+#pragma unroll
+          for (int q = 0; q < 2; ++q) {
+            const int n = n0 + wn * WTN + j * 32 + 8 * (2 * q + half);
+            if (m < p.M && n < p.N) {
+              __bf16* dst = (__bf16*)p.c + (size_t)m * p.N + n;
+              if (n + 8 <= p.N) {
+                *(u32x4*)dst = pend[i][j][q];
+              } else {
+                const u32x2 v = {pend[i][j][q][0], pend[i][j][q][1]};
+                *(u32x2*)dst = v;
+              }
+            }
+          }
       }
+    }
   }
   __syncthreads();   // every wave is done with the LDS stages before the next tile loads
   }
+  if constexpr (!OUT_F32) store_pending(threadIdx.x & 31, (threadIdx.x >> 5) & 1);
 }
 
 // Compute units of the current device (cached per device).
@@ -374,6 +490,7 @@ int pick_cfg(int M, int N) {
 // by splitting M into chunks with their own base pointers.
 hipError_t launch_ikbo_gemm(GemmParams p, bool gather, bool out_f32, hipStream_t stream) {
   if (p.M <= 0 || p.N <= 0) return hipSuccess;
+  if (!out_f32 && p.N >= (1 << 22)) return hipErrorInvalidValue;   // 32-bit tile offsets
   const int cfg = pick_cfg(p.M, p.N);
   const int tm = cfg == 0 ? 256 : 128, tn = cfg == 0 ? 256 : cfg == 1 ? 128 : 64;
   const int64_t row = (int64_t)p.lda * 2;
