@@ -175,6 +175,7 @@ PERSIST_CFGS = {
     "0": (16500, 1028),   # 256 x 256 tiles: 65 x 5 = 325 on 256 slots; a 4-column tail
     "1": (8000, 1032),    # 128 x 128: 63 x 9 = 567 on 512 slots; an 8-column last tile
     "2": (8000, 576),     # 128 x 64: 63 x 9 = 567 on 512 slots
+    "3": (8000, 576),     # 128 x 64, four stages: 567 on 256 slots
 }
 
 

@@ -79,7 +79,10 @@ __device__ __forceinline__ int xcd_tile(int w, int T) {
 // Tile configurations (TM x TN per workgroup, waves as WM x WN):
 //   0: 256 x 256, 2 x 4 waves of 128 x 64, one workgroup per CU;
 //   1: 128 x 128, 2 x 2 waves of 64 x 64, two per CU;
-//   2: 128 x 64,  2 x 2 waves of 64 x 32, two per CU (small grids).
+//   2: 128 x 64,  2 x 2 waves of 64 x 32, two per CU (small grids);
+//   3: 128 x 64 as 2, one per CU with four LDS stages (grids of at most one
+//      tile per CU: one wave per SIMD hides load latency only by loading
+//      further ahead).
 // All keep the accumulators in architected VGPRs.
 template <int CFG>
 struct GemmShape {
@@ -89,15 +92,19 @@ struct GemmShape {
   static constexpr int kWaves = kWavesM * kWavesN;
   static constexpr int MB = TM / kWavesM / 32;     // 32 x 32 blocks per wave, rows
   static constexpr int NB = TN / kWavesN / 32;     // and columns
-  static constexpr int kPerCU = CFG == 0 ? 1 : 2;
+  static constexpr int kPerCU = CFG == 0 || CFG == 3 ? 1 : 2;
+  static constexpr int kStages = CFG == 3 ? 4 : 2;
+  // Workgroups per CU for the register budget: 3 runs one (its LDS allows no
+  // more) but takes the budget of two, 256 registers per wave. With the whole
+  // file the compiler moves the accumulators to AGPRs and copies each addend
+  // load into them behind its own wait.
+  static constexpr int kRegsPerCU = CFG == 0 ? 1 : 2;
 };
 
 template <int CFG, bool GATHER, bool OUT_F32>
-__global__ __launch_bounds__(CFG == 0 ? 512 : 256, CFG == 0 ? 1 : 2) void
+__global__ __launch_bounds__(GemmShape<CFG>::kWaves * 64, GemmShape<CFG>::kRegsPerCU) void
 ikbo_gemm_kernel(const GemmParams p) {
   using S = GemmShape<CFG>;
-  static_assert(S::kWaves * 64 == (CFG == 0 ? 512 : 256) && S::kPerCU == (CFG == 0 ? 1 : 2),
-                "launch bounds match the wave layout");
   constexpr int kWaves = S::kWaves, MB = S::MB, NB = S::NB, TM = S::TM, TN = S::TN;
   constexpr int WTM = MB * 32, WTN = NB * 32;     // wave tile
   constexpr int kChunksA = TM * kPitch, kChunksB = TN * kPitch;   // chunks per stage
@@ -106,26 +113,34 @@ ikbo_gemm_kernel(const GemmParams p) {
   constexpr int kPerB = (kLoadsB + kWaves - 1) / kWaves;
   static_assert(kChunksA % 64 == 0 && kChunksB % 64 == 0, "a stage is whole wave loads");
   // Separate arrays per stage buffer: the compiler then knows that reads of
-  // one buffer do not wait for direct-to-LDS loads still landing in the other.
+  // one buffer do not wait for direct-to-LDS loads still landing in another.
+  constexpr int kRingA = S::kStages > 2 ? kChunksA : 1, kRingB = S::kStages > 2 ? kChunksB : 1;
   __shared__ u32x4 abuf0[kChunksA];
   __shared__ u32x4 abuf1[kChunksA];
+  __shared__ u32x4 abuf2[kRingA];
+  __shared__ u32x4 abuf3[kRingA];
   __shared__ u32x4 bbuf0[kChunksB];
   __shared__ u32x4 bbuf1[kChunksB];
+  __shared__ u32x4 bbuf2[kRingB];
+  __shared__ u32x4 bbuf3[kRingB];
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave / S::kWavesN, wn = wave % S::kWavesN;
   // Persistent grid: a workgroup runs tiles blockIdx.x, +G, +2G, ... (G =
   // gridDim.x, a multiple of 8 whenever it is below the tile count, so the
   // workgroup stays on one XCD).
-  // bf16 output: a whole tile's results wait in registers (converted and
-  // lane-swapped) until the next tile's addend and first two stages of loads
-  // are issued; its stores follow them and drain under that tile's first two
-  // stages. Edge tiles (rows past M or columns past N) store at once. gfx9
-  // counts loads and stores in one counter (vmcnt) and retires them in issue
-  // order, so a wave waits for a stage with a count that leaves the later
-  // stores outstanding; every store is therefore issued, whatever the tile.
+  // bf16 output with two stages: a whole tile's results wait in registers
+  // (converted and lane-swapped) until the next tile's addend and first two
+  // stages of loads are issued; its stores follow them and drain under that
+  // tile's first two stages. Edge tiles (rows past M or columns past N), and
+  // the four-stage configuration (picked for grids of one round), store at
+  // once. gfx9 counts loads and stores in one counter (vmcnt) and retires
+  // them in issue order, so a wave waits for a stage with a count that leaves
+  // the later stores outstanding; every store is therefore issued, whatever
+  // the tile.
   constexpr int kMinLoads = kLoadsA / kWaves + kLoadsB / kWaves;  // per wave and stage
   constexpr int kStores = MB * NB * 2;                            // 16-byte stores per wave
+  constexpr bool kPend = !OUT_F32 && S::kStages == 2;
   u32x4 pend[MB][NB][2];
   int pm0 = -1, pn0 = 0;
   const uint32_t crow = (uint32_t)p.N * 2;
@@ -255,6 +270,14 @@ ikbo_gemm_kernel(const GemmParams p) {
         for (int e = 0; e < 4; ++e) acc[i][j][4 * g + e] = v[e];
       }
   }
+  if constexpr (S::kStages > 2) {
+    // Keep the accumulators in VGPRs: in AGPRs, every addend load above is
+    // copied over behind a wait of its own.
+#pragma unroll
+    for (int i = 0; i < MB; ++i)
+#pragma unroll
+      for (int j = 0; j < NB; ++j) asm volatile("" : "+v"(acc[i][j]));
+  }
 
   // Fragments of one k-substep (16 of K): MB of A and NB of B, two slots.
   bf16x8 av[2][MB], bv[2][NB];
@@ -306,11 +329,6 @@ ikbo_gemm_kernel(const GemmParams p) {
   };
 
   const int nst = (p.K + kBK - 1) / kBK;
-  if (nst > 0) load_stage(abuf0, bbuf0, 0);
-  if (nst > 1) load_stage(abuf1, bbuf1, 1);
-  __builtin_amdgcn_sched_barrier(0);
-  if constexpr (!OUT_F32) store_pending(col, half);   // the previous tile's, after the loads
-  __builtin_amdgcn_sched_barrier(0);
   // Workgroup barrier without __syncthreads()'s release fence, which would
   // wait for the pending stores too. Each wave has waited (vmcnt) for its own
   // loads of the stage about to be read and waits here for its LDS reads
@@ -322,40 +340,91 @@ ikbo_gemm_kernel(const GemmParams p) {
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
   };
-  // Wait for the addend and stage 0: what may remain is stage 1's loads (at
-  // least kMinLoads per wave) and the pending stores (at least kStores).
-  if constexpr (!OUT_F32) {
-    if (nst > 1) wait_vm_n<kMinLoads + kStores>(); else wait_vm_n<kStores>();
-  } else {
-    if (nst > 1) wait_vm_n<kMinLoads>(); else wait_vm();
-  }
-  lds_barrier();
-  if (nst > 0) read(abuf0, bbuf0, 0, 0);
-  // At the barrier that ends stage t every wave has finished reading buffer
-  // t % 2 (the barrier waits for LDS reads) and stage t + 1 has landed; the
-  // loads of stage t + 2 then go into buffer t % 2, and substep 3 of stage t
-  // runs while substep 0 of stage t + 1 is read (past the last stage that
-  // read is of unused data). Stages go in pairs so that every LDS access
-  // names one buffer; an odd last stage runs after the loop.
-  auto step = [&](u32x4* ab, u32x4* bb, u32x4* nab, u32x4* nbb, int t)
-                  __attribute__((always_inline)) {
-    stage(ab, bb);
-    __builtin_amdgcn_sched_barrier(0);   // keep substep 3's MFMAs after the barrier
-    if (!OUT_F32 && t == 0) wait_vm_n<kStores>(); else wait_vm();
-    lds_barrier();
+  if constexpr (S::kStages == 2) {
+    if (nst > 0) load_stage(abuf0, bbuf0, 0);
+    if (nst > 1) load_stage(abuf1, bbuf1, 1);
     __builtin_amdgcn_sched_barrier(0);
-    if (t + 2 < nst) load_stage(ab, bb, t + 2);
-    read(nab, nbb, 0, 0);
-    mfma(1);
-  };
-  int t = 0;
-  for (; t + 1 < nst; t += 2) {
-    step(abuf0, bbuf0, abuf1, bbuf1, t);
-    step(abuf1, bbuf1, abuf0, bbuf0, t + 1);
-  }
-  if (t < nst) {
-    stage(abuf0, bbuf0);
-    mfma(1);
+    if constexpr (kPend) store_pending(col, half);   // the previous tile's, after the loads
+    __builtin_amdgcn_sched_barrier(0);
+    // Wait for the addend and stage 0: what may remain is stage 1's loads (at
+    // least kMinLoads per wave) and the pending stores (kStores).
+    if constexpr (kPend) {
+      if (nst > 1) wait_vm_n<kMinLoads + kStores>(); else wait_vm_n<kStores>();
+    } else {
+      if (nst > 1) wait_vm_n<kMinLoads>(); else wait_vm();
+    }
+    lds_barrier();
+    if (nst > 0) read(abuf0, bbuf0, 0, 0);
+    // At the barrier that ends stage t every wave has finished reading buffer
+    // t % 2 (the barrier waits for LDS reads) and stage t + 1 has landed; the
+    // loads of stage t + 2 then go into buffer t % 2, and substep 3 of stage t
+    // runs while substep 0 of stage t + 1 is read (past the last stage that
+    // read is of unused data). Stages go in pairs so that every LDS access
+    // names one buffer; an odd last stage runs after the loop.
+    auto step = [&](u32x4* ab, u32x4* bb, u32x4* nab, u32x4* nbb, int t)
+                    __attribute__((always_inline)) {
+      stage(ab, bb);
+      __builtin_amdgcn_sched_barrier(0);   // keep substep 3's MFMAs after the barrier
+      if (kPend && t == 0) wait_vm_n<kStores>(); else wait_vm();
+      lds_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      if (t + 2 < nst) load_stage(ab, bb, t + 2);
+      read(nab, nbb, 0, 0);
+      mfma(1);
+    };
+    int t = 0;
+    for (; t + 1 < nst; t += 2) {
+      step(abuf0, bbuf0, abuf1, bbuf1, t);
+      step(abuf1, bbuf1, abuf0, bbuf0, t + 1);
+    }
+    if (t < nst) {
+      stage(abuf0, bbuf0);
+      mfma(1);
+    }
+  } else {
+    // Four stages: stage t lives in buffer t % 4 and loads run three stages
+    // ahead. A wave waits only for its own loads of the next stage; the ones
+    // it issued after them (up to two stages, at least kMinLoads each) stay
+    // in flight.
+    auto wait_stage = [&](int after) __attribute__((always_inline)) {
+      if (after >= 3) wait_vm_n<3 * kMinLoads>();
+      else if (after == 2) wait_vm_n<2 * kMinLoads>();
+      else if (after == 1) wait_vm_n<kMinLoads>();
+      else wait_vm();
+    };
+    if (nst > 0) load_stage(abuf0, bbuf0, 0);
+    if (nst > 1) load_stage(abuf1, bbuf1, 1);
+    if (nst > 2) load_stage(abuf2, bbuf2, 2);
+    if (nst > 3) load_stage(abuf3, bbuf3, 3);
+    if (nst > 0) {
+      wait_stage(min(nst - 1, 3));
+      lds_barrier();
+      read(abuf0, bbuf0, 0, 0);
+    }
+    // At the barrier that ends stage t every wave has finished reading buffer
+    // t % 4 and stage t + 1 has landed; the loads of stage t + 4 then go into
+    // buffer t % 4. The stages issued by then end at min(t + 3, nst - 1).
+    auto step = [&](u32x4* ab, u32x4* bb, u32x4* nab, u32x4* nbb, int t)
+                    __attribute__((always_inline)) {
+      stage(ab, bb);
+      __builtin_amdgcn_sched_barrier(0);   // keep substep 3's MFMAs after the barrier
+      wait_stage(min(t + 3, nst - 1) - (t + 1));
+      lds_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      if (t + 4 < nst) load_stage(ab, bb, t + 4);
+      read(nab, nbb, 0, 0);
+      mfma(1);
+    };
+    int t = 0;
+    for (; t + 3 < nst; t += 4) {
+      step(abuf0, bbuf0, abuf1, bbuf1, t);
+      step(abuf1, bbuf1, abuf2, bbuf2, t + 1);
+      step(abuf2, bbuf2, abuf3, bbuf3, t + 2);
+      step(abuf3, bbuf3, abuf0, bbuf0, t + 3);
+    }
+    if (t < nst) step(abuf0, bbuf0, abuf1, bbuf1, t);
+    if (t + 1 < nst) step(abuf1, bbuf1, abuf2, bbuf2, t + 1);
+    if (t + 2 < nst) step(abuf2, bbuf2, abuf3, bbuf3, t + 2);
   }
 
   // Epilogue. fp32 output: store the accumulators (rows past M and column
@@ -398,7 +467,7 @@ ikbo_gemm_kernel(const GemmParams p) {
           const auto s1 = __builtin_amdgcn_permlane32_swap(w[1], w[3], false, false);
           pend[i][j][q] = u32x4{s0[0], s1[0], s0[1], s1[1]};
         }
-    if (m0 + TM <= p.M && n0 + TN <= p.N) {
+    if (kPend && m0 + TM <= p.M && n0 + TN <= p.N) {
       pm0 = m0;
       pn0 = n0;
     } else {
@@ -426,7 +495,7 @@ ikbo_gemm_kernel(const GemmParams p) {
   }
   __syncthreads();   // every wave is done with the LDS stages before the next tile loads
   }
-  if constexpr (!OUT_F32) store_pending(threadIdx.x & 31, (threadIdx.x >> 5) & 1);
+  if constexpr (kPend) store_pending(threadIdx.x & 31, (threadIdx.x >> 5) & 1);
 }
 
 // Compute units of the current device (cached per device).
@@ -471,17 +540,19 @@ int64_t cfg_tiles(int cfg, int64_t M, int64_t N) {
   return ((M + tm - 1) / tm) * ((N + tn - 1) / tn);
 }
 
-// The largest tile that still gives every CU a workgroup (256 CUs); the
-// environment variable ATTN_GEMM_CFG=0|1|2 (read once) forces one.
+// The largest tile that still gives every CU a workgroup (256 CUs), and the
+// four-stage configuration when 128 x 64 tiles fit one round at one per CU;
+// the environment variable ATTN_GEMM_CFG=0|1|2|3 (read once) forces one.
 int pick_cfg(int M, int N) {
   static const int forced = [] {
     const char* e = getenv("ATTN_GEMM_CFG");
     return e ? atoi(e) : -1;
   }();
-  if (forced >= 0 && forced <= 2) return forced;
+  if (forced >= 0 && forced <= 3) return forced;
   if (cfg_tiles(0, M, N) >= 256) return 0;
   if (cfg_tiles(1, M, N) >= 256) return 1;
-  return 2;
+  const int cus = device_cus();
+  return cfg_tiles(2, M, N) <= (cus > 0 ? cus : 256) ? 3 : 2;
 }
 
 }  // namespace
@@ -510,7 +581,8 @@ hipError_t launch_ikbo_gemm(GemmParams p, bool gather, bool out_f32, hipStream_t
     q.tiles = (int)tiles;
     const hipError_t err = cfg == 0   ? launch_cfg<0>(q, gather, out_f32, stream)
                            : cfg == 1 ? launch_cfg<1>(q, gather, out_f32, stream)
-                                      : launch_cfg<2>(q, gather, out_f32, stream);
+                           : cfg == 2 ? launch_cfg<2>(q, gather, out_f32, stream)
+                                      : launch_cfg<3>(q, gather, out_f32, stream);
     if (err != hipSuccess) return err;
   }
   return hipSuccess;
