@@ -50,6 +50,7 @@ namespace attn {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
@@ -741,24 +742,35 @@ __global__ __launch_bounds__(W * 64, W == 4 ? 2 : 1) void attn_fwd_bf16_kernel(c
     }
 
     // ---- epilogue: O = O^T / l, round to bf16, store ---------------------------
+    // Lanes l and l + 32 hold the same row: lane l columns 8m .. 8m+3 of each
+    // group m of a 32-column block, lane l + 32 columns 8m+4 .. 8m+7. One
+    // lane-half swap per pair of groups (2q, 2q+1) gives lane l the eight
+    // columns of group 2q and lane l + 32 those of group 2q+1: half as many
+    // stores, 16 bytes each. The swap runs in every lane; only the stores
+    // depend on the row.
     if (active) {
 #pragma unroll
       for (int qb = 0; qb < kQB; ++qb) {
         const float l = halves_sum(l_run[qb]);
         const float inv = (l > 0.f) ? 1.f / l : 0.f;
         const int row = me.row0 + 32 * qb + col;
-        if (row < me.lq) {
-          __bf16* orow = og + (size_t)row * q_rs;
+        __bf16* orow = og + (size_t)row * q_rs;
 #pragma unroll
-          for (int b = 0; b < DB; ++b)
+        for (int b = 0; b < DB; ++b)
 #pragma unroll
-            for (int m4 = 0; m4 < 4; ++m4) {
-              bf16x4 w;
+          for (int q = 0; q < 2; ++q) {
+            uint32_t w[4];
 #pragma unroll
-              for (int j = 0; j < 4; ++j) w[j] = (__bf16)(oacc[qb][b][m4 * 4 + j] * inv);
-              *(bf16x4*)(orow + b * 32 + m4 * 8 + half * 4) = w;
+            for (int e = 0; e < 4; ++e) {
+              const bf16x2 h = {(__bf16)(oacc[qb][b][8 * q + 2 * e] * inv),
+                                (__bf16)(oacc[qb][b][8 * q + 2 * e + 1] * inv)};
+              w[e] = __builtin_bit_cast(uint32_t, h);
             }
-        }
+            const auto s0 = __builtin_amdgcn_permlane32_swap(w[0], w[2], false, false);
+            const auto s1 = __builtin_amdgcn_permlane32_swap(w[1], w[3], false, false);
+            const u32x4 v = {s0[0], s1[0], s0[1], s1[1]};
+            if (row < me.lq) *(u32x4*)(orow + b * 32 + 16 * q + 8 * half) = v;
+          }
       }
     }
   }
