@@ -172,8 +172,26 @@ ikbo_gemm_kernel(const GemmParams p) {
   asm volatile("" : "+v"(tid));
   const int lane = tid & 63;
   const int half = lane >> 5, col = lane & 31;
-  const int m0 = (tile / p.tiles_n) * TM;
-  const int n0 = (tile % p.tiles_n) * TN;
+  int rb, cb;
+  if constexpr (CFG == 3) {
+    // Column groups of 8 tiles, row blocks inside a group: an XCD's share of
+    // the tile order then spans fewer columns of B. On the user half of the
+    // broadcast layer (16 x 16 tiles) an XCD's 32 tiles read 4 row blocks of
+    // A and 8 column tiles of B, 2 + 2 MB, instead of 1 + 4.2 MB, within its
+    // 4 MB L2.
+    constexpr int kGW = 8;
+    const int nrb = p.tiles / p.tiles_n;
+    const int grp = tile / (kGW * nrb);
+    const int gcols = min(kGW, p.tiles_n - grp * kGW);
+    const int r = tile - grp * kGW * nrb;
+    rb = r / gcols;
+    cb = grp * kGW + r % gcols;
+  } else {
+    rb = tile / p.tiles_n;
+    cb = tile % p.tiles_n;
+  }
+  const int m0 = rb * TM;
+  const int n0 = cb * TN;
 
   // Buffer descriptors start at the tile's first row and end with the last
   // valid row's K-th element: chunks of rows past M (or N) read as zero.
