@@ -213,3 +213,37 @@ def test_persistent_rounds_each_tile_config(lib, tmp_path, cfg):
     assert r.returncode == 0, r.stderr[-2000:]
     for i, w in enumerate(ws):
         check(w, np.load(tmp_path / f"y{i}.npy"), np.load(tmp_path / f"z{i}.npy"))
+
+
+def test_four_stage_ring_remainders(lib, tmp_path):
+    """Configuration 3 (four LDS stages, loads three stages ahead) forced on K depths whose
+    stage counts leave every remainder of the ring: 3, 5, 6 and 7 stages of 64 (some cut by
+    K), in the fp32 user half (K_u) and the bf16 candidate half (K_c). Against the oracle."""
+    import os
+    import subprocess
+    import sys
+    shapes = [(136, 320), (384, 448), (200, 392), (448, 136)]   # (K_u, K_c)
+    ws = [ai.make_linear(40, 1500, K_u, K_c, 264, shuffle=True, seed=61 + i)
+          for i, (K_u, K_c) in enumerate(shapes)]
+    for i, w in enumerate(ws):
+        np.savez(tmp_path / f"in{i}.npz", xu=w.x_user, xc=w.x_cand, w=w.w, c2u=w.cand2user,
+                 b=w.bias)
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    script = (
+        "import sys, numpy as np, torch; sys.path.insert(0, %r); sys.path.insert(0, %r)\n"
+        "import tiled_attention_attn_amd as taa; from gpu_util import to_dev, from_dev, i32_dev\n"
+        "for i in range(%d):\n"
+        "    z = np.load('%s/in%%d.npz' %% i)\n"
+        "    y, zz = taa.ikbo_linear(to_dev(z['xu'], 'bf16'), to_dev(z['xc'], 'bf16'),\n"
+        "                            to_dev(z['w'], 'bf16'), i32_dev(z['c2u']),\n"
+        "                            torch.from_numpy(z['b']).cuda())\n"
+        "    torch.cuda.synchronize()\n"
+        "    np.save('%s/y%%d.npy' %% i, from_dev(y)); np.save('%s/z%%d.npy' %% i, from_dev(zz))\n"
+        "    print('case', i, 'done', flush=True)\n"
+    ) % (root, os.path.join(root, "tests"), len(ws), tmp_path, tmp_path, tmp_path)
+    env = dict(os.environ, ATTN_GEMM_CFG="3")
+    r = subprocess.run([sys.executable, "-c", script], env=env, capture_output=True, text=True,
+                       timeout=300)
+    assert r.returncode == 0, r.stderr[-2000:]
+    for i, w in enumerate(ws):
+        check(w, np.load(tmp_path / f"y{i}.npy"), np.load(tmp_path / f"z{i}.npy"))
