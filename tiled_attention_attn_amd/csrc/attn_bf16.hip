@@ -707,9 +707,12 @@ __global__ __launch_bounds__(W * 64, W == 4 ? 2 : 1) void attn_fwd_bf16_kernel(c
       if (active) {
         const bool do_sm = t < my_total;
         if (t <= my_total) {
-          __builtin_amdgcn_s_setprio(1);
+          // Priority for the MFMA stream at d = 64 only: measured with two
+          // workgroups per SIMD pair, it helps d = 64 and slows d = 128 (the
+          // broadcast workload) by a few percent.
+          if constexpr (D == 64) __builtin_amdgcn_s_setprio(1);
           pvqk(sacc, kcur, vprev);
-          __builtin_amdgcn_s_setprio(0);
+          if constexpr (D == 64) __builtin_amdgcn_s_setprio(0);
         }
         if (do_sm) {
           const bool masked = t >= my_full;
