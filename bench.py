@@ -426,6 +426,75 @@ def linear_cpu_baseline(name: str, budget_s: float = 15.0) -> dict:
                       f"the layer's {per_cand:.4g} decomposed FLOPs per candidate"}
 
 
+def ceiling(reps: int = 3) -> dict:
+    """Sustained rates of the units the kernels use, measured on this GPU (median of
+    `reps` timed launches after one warm launch, HIP events on the launch stream):
+    bf16 MFMA from registers with N(0,1) operands (what attention inputs look like to
+    the matrix cores) and with constant operands, v_exp_f32, scalar fp32 FMA, LDS reads
+    (plain 16-byte and the transposing 8-byte form) and an HBM copy."""
+    import torch
+    from tiled_attention_attn_amd import _binding as b
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def timed(fn) -> float:
+        fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            start.record()
+            fn()
+            end.record()
+            torch.cuda.synchronize()
+            ts.append(start.elapsed_time(end))
+        return float(np.median(ts))
+
+    out = {}
+    lanes = 65536
+    ops_n = to_device(ai.f32_to_bf16_bits(ai.normal_f32((lanes * 128,), 0, 20)), "bf16")
+    ops_c = torch.full((lanes * 128,), 1.0, dtype=torch.bfloat16, device="cuda")
+    wg, waves, iters = 512, 8, 40000
+    sink = torch.empty(wg * waves * 64, dtype=torch.float32, device="cuda")
+    flops = wg * waves * iters * 8 * 32768
+    for name, ops in (("mfma_bf16_normal_operands", ops_n), ("mfma_bf16_constant_operands", ops_c)):
+        ms = timed(lambda: b.ceiling_mfma_bf16(ops, sink, wg, waves, iters))
+        tf = flops / (ms * 1e-3) / 1e12
+        out[name] = {"TFLOP/s": round(tf, 1), "frac_of_spec": round(tf / PEAK_TFLOPS["bf16"], 4),
+                     "ms": round(ms, 3)}
+    del ops_n, ops_c, sink
+    wg = 2048
+    sink = torch.empty(wg * 512, dtype=torch.float32, device="cuda")
+    iters = 20000
+    ms = timed(lambda: b.ceiling_exp2(sink, wg, iters))
+    n = wg * 256 * iters * 16
+    out["v_exp_f32"] = {"G/s": round(n / (ms * 1e-3) / 1e9, 1),
+                        "per_CU_per_clk_at_2.4GHz": round(n / (ms * 1e-3) / 256 / 2.4e9, 2),
+                        "ms": round(ms, 3)}
+    iters = 65536
+    ms = timed(lambda: b.ceiling_fma(sink, wg, iters))
+    n = wg * 256 * iters * 16
+    out["v_fma_f32"] = {"TFLOP/s": round(2 * n / (ms * 1e-3) / 1e12, 2),
+                        "per_CU_per_clk_at_2.4GHz": round(n / (ms * 1e-3) / 256 / 2.4e9, 2),
+                        "ms": round(ms, 3)}
+    wg, iters = 512, 32768
+    for name, tr, nb in (("lds_read_b128", 0, 16), ("lds_read_b64_tr_b16", 1, 8)):
+        ms = timed(lambda: b.ceiling_lds_read(sink, wg, iters, tr))
+        by = wg * 512 * iters * 8 * nb
+        out[name] = {"TB/s": round(by / (ms * 1e-3) / 1e12, 2),
+                     "B_per_CU_per_clk_at_2.4GHz": round(by / (ms * 1e-3) / 256 / 2.4e9, 1),
+                     "ms": round(ms, 3)}
+    del sink
+    nbytes = 1 << 30
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    ms = timed(lambda: b.ceiling_copy(dst, src))
+    gbs = 2 * nbytes / (ms * 1e-3) / 1e9
+    out["hbm_copy"] = {"GB/s": round(gbs, 1), "frac_of_spec": round(gbs / PEAK_HBM_GBS, 4),
+                       "bytes_copied": nbytes, "ms": round(ms, 3)}
+    del src, dst
+    torch.cuda.empty_cache()
+    return out
+
+
 def traffic_for(workload: str):
     """HBM bytes per launch (per step for the linear layer) measured with rocprofv3
     counters, if they were taken on the current kernel source."""
@@ -449,6 +518,8 @@ def main():
                     choices=sorted(ai.WORKLOADS) + sorted(ai.LINEAR_WORKLOADS))
     ap.add_argument("--no-variants", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--ceiling-only", action="store_true",
+                    help="only run the ceiling microbenchmarks and print their JSON")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run 5 plain device copies of MIB MiB (calibrates HBM byte counters)")
     args = ap.parse_args()
@@ -470,6 +541,10 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes_read": n, "bytes_written": n, "copies": 5}))
+        return
+
+    if args.ceiling_only:
+        print(json.dumps({"ceiling": ceiling()}))
         return
 
     if args.workload in ai.LINEAR_WORKLOADS:

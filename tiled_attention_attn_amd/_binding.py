@@ -60,6 +60,15 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.attn_strerror.restype = ctypes.c_char_p
     lib.attn_version.argtypes = []
     lib.attn_version.restype = i32
+    i64 = ctypes.c_int64
+    lib.attn_ceiling_mfma_bf16.argtypes = [vp, i64, vp, i32, i32, i32, vp]
+    lib.attn_ceiling_exp2.argtypes = [vp, i32, i32, vp]
+    lib.attn_ceiling_fma.argtypes = [vp, i32, i32, vp]
+    lib.attn_ceiling_lds_read.argtypes = [vp, i32, i32, i32, vp]
+    lib.attn_ceiling_copy.argtypes = [vp, vp, i64, vp]
+    for fn in (lib.attn_ceiling_mfma_bf16, lib.attn_ceiling_exp2, lib.attn_ceiling_fma,
+               lib.attn_ceiling_lds_read, lib.attn_ceiling_copy):
+        fn.restype = i32
     _lib = lib
     return lib
 
@@ -302,3 +311,57 @@ def ikbo_linear(x_user, x_cand, w, cand2user, bias=None, y=None, z=None, *, out_
                            _ptr(y), _ptr(z), B_u, B_c, K_u, K_c, N, _dtype_code(y),
                            _stream(stream)))
     return y, z
+
+
+# --- ceiling microbenchmarks (include/attn_ceiling.h) ----------------------------------------
+
+def _probe_check(status: int, name: str):
+    if status != 0:
+        raise RuntimeError(f"{name}: status {status}")
+
+
+def ceiling_mfma_bf16(operands, out, workgroups, waves, iters, stream=None):
+    """Enqueue the bf16 matrix-core probe. operands: bf16 device tensor holding
+    operand_lanes x 128 values (16 operand vectors of 8 per lane); out: float32 device
+    tensor of workgroups*waves*64 entries. FLOPs = workgroups*waves*iters*8*32768."""
+    lanes = operands.numel() // 128
+    if out.numel() < workgroups * waves * 64 or lanes < 1:
+        raise ValueError("ceiling_mfma_bf16: buffers too small")
+    _probe_check(load_library().attn_ceiling_mfma_bf16(_ptr(operands), lanes, _ptr(out),
+                                                       int(workgroups), int(waves), int(iters),
+                                                       _stream(stream)), "attn_ceiling_mfma_bf16")
+
+
+def ceiling_exp2(out, workgroups, iters, stream=None):
+    """Enqueue the v_exp_f32 probe: workgroups*256*iters*16 exponentials."""
+    if out.numel() < workgroups * 256:
+        raise ValueError("ceiling_exp2: out too small")
+    _probe_check(load_library().attn_ceiling_exp2(_ptr(out), int(workgroups), int(iters),
+                                                  _stream(stream)), "attn_ceiling_exp2")
+
+
+def ceiling_fma(out, workgroups, iters, stream=None):
+    """Enqueue the scalar fp32 FMA probe: workgroups*256*iters*16 FMAs."""
+    if out.numel() < workgroups * 256:
+        raise ValueError("ceiling_fma: out too small")
+    _probe_check(load_library().attn_ceiling_fma(_ptr(out), int(workgroups), int(iters),
+                                                 _stream(stream)), "attn_ceiling_fma")
+
+
+def ceiling_lds_read(out, workgroups, iters, transposed, stream=None):
+    """Enqueue the LDS read probe: workgroups*512*iters*8 reads of 16 bytes
+    (ds_read_b128) or 8 bytes (transposed: ds_read_b64_tr_b16)."""
+    if out.numel() < workgroups * 512:
+        raise ValueError("ceiling_lds_read: out too small")
+    _probe_check(load_library().attn_ceiling_lds_read(_ptr(out), int(workgroups), int(iters),
+                                                      int(bool(transposed)), _stream(stream)),
+                 "attn_ceiling_lds_read")
+
+
+def ceiling_copy(dst, src, stream=None):
+    """Enqueue an HBM copy of src into dst (same byte size, a multiple of 16)."""
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != nbytes:
+        raise ValueError("ceiling_copy: dst and src sizes differ")
+    _probe_check(load_library().attn_ceiling_copy(_ptr(dst), _ptr(src), nbytes, _stream(stream)),
+                 "attn_ceiling_copy")

@@ -100,6 +100,12 @@ __device__ __forceinline__ int xcd_remap(int w, int T, int chunk) {
   return ((s / chunk) * NX + x) * chunk + (s % chunk);
 }
 
+// A wave-uniform 64-bit value, moved to scalar registers.
+__device__ __forceinline__ uint64_t uniform_u64(uint64_t x) {
+  return ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(x >> 32)) << 32) |
+         (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)x);
+}
+
 struct WaveTask {
   int batch;   // query-side batch entry
   int row0;    // first query row of the wave
@@ -244,7 +250,16 @@ __global__ __launch_bounds__(W * 64, W == 4 ? 2 : 1) void attn_fwd_bf16_kernel(c
     return t;
   };
 
-  const WaveTask me = task_of(wave);
+  // The wave's own task is wave-uniform; moving it to scalar registers lets
+  // the compiler treat everything derived from it (loop bounds, buffer
+  // descriptors) as uniform.
+  WaveTask me = task_of(wave);
+  me.batch = __builtin_amdgcn_readfirstlane(me.batch);
+  me.row0 = __builtin_amdgcn_readfirstlane(me.row0);
+  me.lq = __builtin_amdgcn_readfirstlane(me.lq);
+  me.kvb = __builtin_amdgcn_readfirstlane(me.kvb);
+  me.valid = __builtin_amdgcn_readfirstlane((int)me.valid) != 0;
+  me.bad = __builtin_amdgcn_readfirstlane((int)me.bad) != 0;
   // element offset of row 0 of this wave's (sequence, head)
   size_t q_base = ((size_t)me.batch * p.H + h) * (size_t)p.Lq * D;
   if (jagged) q_base = me.valid ? (size_t)p.q_offsets[me.batch] * q_rs + (size_t)h * D : 0;
@@ -265,20 +280,22 @@ __global__ __launch_bounds__(W * 64, W == 4 ? 2 : 1) void attn_fwd_bf16_kernel(c
 
   // Per-lane byte offsets, inside a K/V tile, of the chunks this lane loads:
   // wave load n writes LDS chunks 64n .. 64n+63 (lane i -> chunk 64n + i);
-  // chunk q of the padded tile is row q / pitch, column q % pitch, and pad
-  // columns re-read column 0 of their row. Wave w issues loads w, w+4, ...
+  // chunk q of the padded tile is row q / pitch, column q % pitch. Pad columns
+  // get an offset past any buffer range (ranges stay below 2^31 bytes), so
+  // those lanes make no memory request. Wave w issues loads w, w+W, ...
+  constexpr uint32_t kNoLoad = 0x80000000u;
   uint32_t koff[TL::KPER], voff[TL::VPER];
 #pragma unroll
   for (int j = 0; j < TL::KPER; ++j) {
     const int q = (wave + j * kWaves) * 64 + lane;
     const int r = q / KPITCH, cc = q % KPITCH;
-    koff[j] = (uint32_t)(r * (kv_rs * 2) + (cc < NC ? cc : 0) * 16);
+    koff[j] = cc < NC ? (uint32_t)(r * (kv_rs * 2) + cc * 16) : kNoLoad;
   }
 #pragma unroll
   for (int j = 0; j < TL::VPER; ++j) {
     const int q = (wave + j * kWaves) * 64 + lane;
     const int r = q / VPITCH, cc = q % VPITCH;
-    voff[j] = (uint32_t)(r * (kv_rs * 2) + (cc < NC ? cc : 0) * 16);
+    voff[j] = cc < NC ? (uint32_t)(r * (kv_rs * 2) + cc * 16) : kNoLoad;
   }
 
   // One pass per distinct K/V batch among the waves (normally exactly one).
@@ -361,7 +378,8 @@ __global__ __launch_bounds__(W * 64, W == 4 ? 2 : 1) void attn_fwd_bf16_kernel(c
       const WaveTask t = task_of(w);
       if (t.valid && !t.bad && t.kvb == kvb) ntiles = max(ntiles, tiles_touching(keys_needed(t)));
     }
-    const bool active = me.valid && !me.bad && me.kvb == kvb;
+    ntiles = __builtin_amdgcn_readfirstlane(ntiles);
+    const bool active = __builtin_amdgcn_readfirstlane(me.valid && !me.bad && me.kvb == kvb) != 0;
     if (ntiles == 0) {
       if (active) {
         const int row = me.row0 + col;  // no valid key: output rows are 0
@@ -372,48 +390,61 @@ __global__ __launch_bounds__(W * 64, W == 4 ? 2 : 1) void attn_fwd_bf16_kernel(c
       }
       continue;
     }
-    const int my_total = active ? tiles_touching(keys_needed(me)) : 0;
+    // Per-wave tile counts are wave-uniform; readfirstlane says so to the
+    // compiler, so that branches on them stay scalar branches.
+    const int my_total =
+        __builtin_amdgcn_readfirstlane(active ? tiles_touching(keys_needed(me)) : 0);
     // tiles whose every key is valid for every row of this wave (no mask
     // needed); with tiles in increasing key order they come first
     int full_keys = nvalid;
     if (CAUSAL) full_keys = min(full_keys, me.row0 + 1);
-    const int my_full = active ? min(tiles_inside(full_keys), my_total) : 0;
+    const int my_full =
+        __builtin_amdgcn_readfirstlane(active ? min(tiles_inside(full_keys), my_total) : 0);
 
     size_t kv_base = ((size_t)kvb * p.Hkv + g) * (size_t)p.Lk * D;   // elements
     if (jagged) kv_base = (size_t)p.kv_offsets[kvb] * kv_rs + (size_t)g * D;
     const char* __restrict__ kg = (const char*)p.k + kv_base * 2;
     const char* __restrict__ vg = (const char*)p.v + kv_base * 2;
 
-    // Direct-to-LDS buffer loads of tile t. The buffer descriptor spans this
-    // (batch, head)'s Lk rows, so chunks of rows past the end read as zero
-    // (those keys are masked or never read); the tile offset is a scalar.
-    // (jagged: the range ends with the last row of this head, so later
-    // rows, which belong to other heads or sequences, read as zero too)
-    const uint32_t kv_bytes =
+    // Direct-to-LDS buffer loads of tile t. Each tile gets its own buffer
+    // descriptor: the base is the tile's first row and the range is the bytes
+    // of this (batch, head)'s valid rows from there on (none for a tile past
+    // the end). A lane's only offset is its own chunk offset, so the range
+    // check is the plain per-lane one: chunks of rows past the end read as
+    // zero (those keys are masked or never read), and so do the pad lanes.
+    // (jagged: the range ends with the last row of this head, so later rows,
+    // which belong to other heads or sequences, read as zero too)
+    // The pass's K/V base addresses and valid byte range are wave-uniform:
+    // kept in scalar registers, the per-tile descriptor is scalar arithmetic
+    // (a descriptor the compiler cannot prove uniform costs a loop per load).
+    const uint32_t kv_bytes = __builtin_amdgcn_readfirstlane(
         jagged ? (nvalid > 0 ? (uint32_t)(nvalid - 1) * (kv_rs * 2) + D * 2 : 0u)
-               : (uint32_t)p.Lk * (D * 2);
-    const __amdgpu_buffer_rsrc_t krsrc =
-        __builtin_amdgcn_make_buffer_rsrc((void*)kg, (short)0, (int)kv_bytes, kBufferWord3);
-    const __amdgpu_buffer_rsrc_t vrsrc =
-        __builtin_amdgcn_make_buffer_rsrc((void*)vg, (short)0, (int)kv_bytes, kBufferWord3);
-    auto load_tile = [&](__amdgpu_buffer_rsrc_t rsrc, u32x4* dst, int t, const uint32_t* off,
-                         auto per_c, auto nloads_c) __attribute__((always_inline)) {
+               : (uint32_t)p.Lk * (D * 2));
+    const uint64_t kaddr = uniform_u64((uint64_t)(uintptr_t)kg);
+    const uint64_t vaddr = uniform_u64((uint64_t)(uintptr_t)vg);
+    auto load_tile = [&](uint64_t base, u32x4* dst, int t, const uint32_t* off, auto per_c,
+                         auto nloads_c) __attribute__((always_inline)) {
       constexpr int PER = decltype(per_c)::value, NLOADS = decltype(nloads_c)::value;
-      const uint32_t tile_off = (uint32_t)t * (BN * kv_rs * 2);
+      const uint32_t tile_off = (uint32_t)t * (uint32_t)(BN * kv_rs * 2);
+      // both below 2^31: a signed max, which has a scalar instruction (an
+      // unsigned saturating subtract would go to a vector register)
+      const int left = max((int)kv_bytes - (int)tile_off, 0);
+      const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(uintptr_t)(base + tile_off), (short)0, left, kBufferWord3);
 #pragma unroll
       for (int j = 0; j < PER; ++j) {
         const int n = wave + j * kWaves;
         if (j < PER - 1 || n < NLOADS)
           __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (void LDS_AS*)(dst + n * 64), 16, off[j],
-                                                   tile_off, 0, 0);
+                                                   0, 0, 0);
       }
     };
     auto load_k = [&](u32x4* dst, int t) __attribute__((always_inline)) {
-      load_tile(krsrc, dst, t, koff, std::integral_constant<int, TL::KPER>{},
+      load_tile(kaddr, dst, t, koff, std::integral_constant<int, TL::KPER>{},
                 std::integral_constant<int, TL::KLOADS>{});
     };
     auto load_v = [&](u32x4* dst, int t) __attribute__((always_inline)) {
-      load_tile(vrsrc, dst, t, voff, std::integral_constant<int, TL::VPER>{},
+      load_tile(vaddr, dst, t, voff, std::integral_constant<int, TL::VPER>{},
                 std::integral_constant<int, TL::VLOADS>{});
     };
     // Q^T operands: block qb, lane holds query row0+32qb+col, d = 16*s + 8*half + 0..7.
@@ -476,54 +507,81 @@ __global__ __launch_bounds__(W * 64, W == 4 ? 2 : 1) void attn_fwd_bf16_kernel(c
     // O += P(t-1) V(t-1), then S(t) = K(t) Q^T, so P(t-1) is dead before S(t)
     // is born. Operand reads run two MFMAs ahead through the whole stream
     // (a V^T operand is two reads, a K operand one), so the matrix pipe does
-    // not wait at the seam between the products.
-    auto pvqk = [&](f32x16 (&sacc)[kQB][KB], const u32x4* kb, const u32x4* vb32)
-                    __attribute__((always_inline)) {
+    // not wait at the seam between the products. PV_C / QK_C (compile time)
+    // drop one of the products: the first tile of a pass has no PV product
+    // and the step after the last tile no QK product.
+    auto pvqk = [&](f32x16 (&sacc)[kQB][KB], const u32x4* kb, const u32x4* vb32, auto pv_c,
+                    auto qk_c) __attribute__((always_inline)) {
       static_assert(kQB == 1, "one query block per wave");
+      constexpr bool PV = decltype(pv_c)::value, QK = decltype(qk_c)::value;
       const u32x4* kl = kb + col * KPITCH + half;
       const LDS_AS char* vb = (const LDS_AS char*)vb32 + vlane;
       constexpr int NK = QS * KB, NV = PS * DB;
       bf16x8 ka[QS][KB], va[NV];
+      if constexpr (PV) {
 #pragma unroll
-      for (int step = 0; step < NV; ++step) {
-        const int o1 = ((step / DB) * 16) * (VPITCH * 16) + (step % DB) * 64;
-        const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)(vb + o1));
-        const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-            (LDS_AS bf16x4*)(vb + o1 + 8 * (VPITCH * 16)));
-        va[step] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        for (int step = 0; step < NV; ++step) {
+          const int o1 = ((step / DB) * 16) * (VPITCH * 16) + (step % DB) * 64;
+          const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)(vb + o1));
+          const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+              (LDS_AS bf16x4*)(vb + o1 + 8 * (VPITCH * 16)));
+          va[step] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        }
+#pragma unroll
+        for (int step = 0; step < NV; ++step)
+          oacc[0][step % DB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              va[step], pprev[0][step / DB], oacc[0][step % DB], 0, 0, 0);
       }
+      if constexpr (QK) {
 #pragma unroll
-      for (int step = 0; step < NV; ++step)
-        oacc[0][step % DB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            va[step], pprev[0][step / DB], oacc[0][step % DB], 0, 0, 0);
+        for (int s = 0; s < QS; ++s)
 #pragma unroll
-      for (int s = 0; s < QS; ++s)
-#pragma unroll
-        for (int kbk = 0; kbk < KB; ++kbk)
-          ka[s][kbk] = __builtin_bit_cast(bf16x8, kl[kbk * 32 * KPITCH + 2 * s]);
-#pragma unroll
-      for (int kbk = 0; kbk < KB; ++kbk)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) sacc[0][kbk][i] = 0.f;
-#pragma unroll
-      for (int s = 0; s < QS; ++s)
+          for (int kbk = 0; kbk < KB; ++kbk)
+            ka[s][kbk] = __builtin_bit_cast(bf16x8, kl[kbk * 32 * KPITCH + 2 * s]);
 #pragma unroll
         for (int kbk = 0; kbk < KB; ++kbk)
-          sacc[0][kbk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[s][kbk], qreg[0][s],
-                                                                 sacc[0][kbk], 0, 0, 0);
-      __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 4, 0);
 #pragma unroll
-      for (int i = 0; i < NV - 2; ++i) {
-        __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, 0);
+          for (int i = 0; i < 16; ++i) sacc[0][kbk][i] = 0.f;
+#pragma unroll
+        for (int s = 0; s < QS; ++s)
+#pragma unroll
+          for (int kbk = 0; kbk < KB; ++kbk)
+            sacc[0][kbk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[s][kbk], qreg[0][s],
+                                                                   sacc[0][kbk], 0, 0, 0);
+      }
+      if constexpr (PV && QK) {
+        __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 4, 0);
+#pragma unroll
+        for (int i = 0; i < NV - 2; ++i) {
+          __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 2, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < NK; ++i) {
+          __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 2, 0);
+      } else if constexpr (PV) {
+        __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 4, 0);
+#pragma unroll
+        for (int i = 0; i < NV - 2; ++i) {
+          __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 2, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 2, 0);
+      } else if constexpr (QK) {
         __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 2, 0);
-      }
 #pragma unroll
-      for (int i = 0; i < NK; ++i) {
-        __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 1, 0);
+        for (int i = 0; i < NK - 2; ++i) {
+          __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 2, 0);
       }
-      __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 2, 0);
     };
+    using kOn = std::true_type;
+    using kOff = std::false_type;
     // Online softmax of block qb for tile t (base 2, scale folded into c);
     // produces the next PV operand and returns the rescale factor of O.
     auto softmax = [&](f32x16 (&sacc)[KB], int qb, int tile, bool masked, bf16x8 (&pout)[PS]) __attribute__((always_inline)) -> float {
@@ -620,7 +678,7 @@ __global__ __launch_bounds__(W * 64, W == 4 ? 2 : 1) void attn_fwd_bf16_kernel(c
       // 32 MFMAs per pass.
       if (t <= my_total) {
         __builtin_amdgcn_s_setprio(1);
-        pvqk(sacc, kb, vb);
+        pvqk(sacc, kb, vb, kOn{}, kOn{});
         __builtin_amdgcn_s_setprio(0);
       }
     };
@@ -691,30 +749,30 @@ __global__ __launch_bounds__(W * 64, W == 4 ? 2 : 1) void attn_fwd_bf16_kernel(c
     // Iteration t runs the MFMA stream O += P(t-1) V(t-1), S(t) = K(t) Q^T,
     // then the softmax of S(t), while K(t+1) and V(t) stream into the other
     // buffers; the two workgroups on a SIMD pair overlap each other's MFMA
-    // and softmax work. As in the 8-wave loop, P starts zeroed with V(0) in
-    // the buffer the empty first PV reads, and the score tile after the last
-    // is computed and never read. The loop is unrolled by two so every access
-    // names one fixed LDS buffer.
+    // and softmax work. Every wave runs iterations 0 .. ntiles (the loads and
+    // the barrier are shared); a wave with n tiles of its own computes
+    // S(0) alone at t = 0, both products for t < n, the last PV product
+    // alone at t = n, and nothing after that. The loop is unrolled by two so
+    // every access names one fixed LDS buffer.
     f32x16 sacc[kQB][KB];
-    auto iteration = [&](auto parity, int t) {
+    // modes: 0 loads and barrier only, 1 first tile (QK), 2 both products, 3 last PV
+    auto iteration = [&](auto parity, auto mode, int t) __attribute__((always_inline)) {
       constexpr int PAR = decltype(parity)::value;
+      constexpr int MODE = decltype(mode)::value;
       u32x4* kcur = PAR ? kbuf1 : kbuf0;
       u32x4* knext = PAR ? kbuf0 : kbuf1;
       u32x4* vprev = PAR ? vbuf0 : vbuf1;
       u32x4* vcur = PAR ? vbuf1 : vbuf0;
       if (t + 1 < ntiles) load_k(knext, tile_of(t + 1));
       if (t < ntiles) load_v(vcur, tile_of(t));
-      if (active) {
-        const bool do_sm = t < my_total;
-        if (t <= my_total) {
-          // Priority for the MFMA stream at d = 64 only: measured with two
-          // workgroups per SIMD pair, it helps d = 64 and slows d = 128 (the
-          // broadcast workload) by a few percent.
-          if constexpr (D == 64) __builtin_amdgcn_s_setprio(1);
-          pvqk(sacc, kcur, vprev);
-          if constexpr (D == 64) __builtin_amdgcn_s_setprio(0);
-        }
-        if (do_sm) {
+      if constexpr (MODE != 0) {
+        // Priority for the MFMA stream at d = 64 only: measured with two
+        // workgroups per SIMD pair, it helps d = 64 and slows d = 128 (the
+        // broadcast workload) by a few percent.
+        if constexpr (D == 64) __builtin_amdgcn_s_setprio(1);
+        pvqk(sacc, kcur, vprev, std::bool_constant<MODE != 1>{}, std::bool_constant<MODE != 3>{});
+        if constexpr (D == 64) __builtin_amdgcn_s_setprio(0);
+        if constexpr (MODE != 3) {
           const bool masked = t >= my_full;
 #pragma unroll
           for (int qb = 0; qb < kQB; ++qb) {
@@ -729,18 +787,32 @@ __global__ __launch_bounds__(W * 64, W == 4 ? 2 : 1) void attn_fwd_bf16_kernel(c
       wait_vm();
       __syncthreads();
     };
-#pragma unroll
-    for (int ps = 0; ps < PS; ++ps) pprev[0][ps] = bf16x8{};
+    using Even = std::integral_constant<int, 0>;
+    using Odd = std::integral_constant<int, 1>;
+    using Idle = std::integral_constant<int, 0>;
+    using First = std::integral_constant<int, 1>;
+    using Both = std::integral_constant<int, 2>;
+    using Last = std::integral_constant<int, 3>;
     load_k(kbuf0, tile_of(0));
-    load_v(vbuf1, tile_of(0));
     wait_vm();
     __syncthreads();
     int t = 0;
-    for (; t + 1 <= ntiles; t += 2) {
-      iteration(std::integral_constant<int, 0>{}, t);
-      iteration(std::integral_constant<int, 1>{}, t + 1);
+    const int n = active ? my_total : 0;   // tiles this wave computes
+    if (n > 0) {
+      iteration(Even{}, First{}, 0);
+      for (t = 1; t + 1 < n; t += 2) {
+        iteration(Odd{}, Both{}, t);
+        iteration(Even{}, Both{}, t + 1);
+      }
+      if (t < n) iteration(Odd{}, Both{}, t++);
+      if (t & 1) iteration(Odd{}, Last{}, t);
+      else iteration(Even{}, Last{}, t);
+      ++t;
     }
-    if (t <= ntiles) iteration(std::integral_constant<int, 0>{}, t);
+    for (; t <= ntiles; ++t) {
+      if (t & 1) iteration(Odd{}, Idle{}, t);
+      else iteration(Even{}, Idle{}, t);
+    }
 
     }
 
