@@ -267,17 +267,24 @@ def test_both_schedules_agree_with_oracle(lib, d, causal, tmp_path):
     assert max_err(outs["4"], outs["8"]) <= TOL["bf16"]
 
 
-@pytest.mark.parametrize("Lk,d,causal,dtype", [(1000, 64, False, "bf16"), (1000, 128, True, "bf16"),
-                                               (8192, 128, False, "bf16"), (8192, 128, True, "bf16"),
-                                               (700, 64, False, "f32"), (700, 128, True, "f32")],
+_MOVES = [(1000, 64, False, "bf16"), (1000, 128, True, "bf16"), (8192, 128, False, "bf16"),
+          (8192, 128, True, "bf16")]
+
+
+@pytest.mark.parametrize("Lk,d,causal,dtype,growth",
+                         [c + (g,) for c in _MOVES for g in (12.0, 80.0)]
+                         + [(700, 64, False, "f32", 12.0), (700, 128, True, "f32", 12.0)],
                          ids=lambda v: str(v))
-def test_reference_moves_on_every_tile(lib, Lk, d, causal, dtype):
+def test_reference_moves_on_every_tile(lib, Lk, d, causal, dtype, growth):
     """Keys along the query direction, scaled up with the key index: each 64-key tile raises
-    every row's maximum by about 12 (in base 2, after the softmax scale) over the last one,
-    past the 2^8 bound of the lazy rescaling, so the exact path and the rescale of O run on
-    every tile (bf16: 4-wave schedule at Lk=1000, 8-wave at 8192; and the fp32 kernel)."""
+    every row's maximum by `growth` (in base 2, after the softmax scale) over the last one.
+    At 80, past the 2^64 bound of the bf16 kernel's lazy rescaling, its exact path and the
+    rescale of O run on every tile; at 12 the reference moves every few tiles (bf16: 4-wave
+    schedule at Lk=1000, 8-wave at 8192). The fp32 kernel, which rescales exactly on every
+    tile, runs the growth of 12 (at 80 its scores reach ~600, where fp32 dot products alone
+    err by more than the 1e-4 bar)."""
     B, H, Lq = 1, 2, 300
-    alpha = 12.0 / (np.log2(np.e) * np.sqrt(d))          # key scale added per 64 keys
+    alpha = growth / (np.log2(np.e) * np.sqrt(d))          # key scale added per 64 keys
     t = (alpha / 64.0) * np.arange(Lk, dtype=np.float64)
     q = 1.0 + 0.05 * ai.normal_f32((B, H, Lq, d), 61, 0)
     k = (t[None, None, :, None] * (1.0 + 0.01 * ai.normal_f32((B, H, Lk, d), 61, 1))).astype(np.float32)

@@ -131,11 +131,15 @@ __device__ __forceinline__ float halves_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// Lazy rescaling: the reference used for the exponent stays put while every
+// Lazy rescaling: the reference r used for the exponent 2^(u - r) moves to
+// the row max on a row's first unmasked tile and then stays put while every
 // probability it gives is at most 2^kTau (base 2), checked through the tile's
-// row sums; probabilities may then exceed 1 by at most that factor, which
-// bf16 and fp32 carry as well. The final division by the row sum uses the
-// same reference, so the result is unchanged up to rounding.
+// partial row sums; probabilities may then exceed 1 by at most that factor,
+// which bf16 and fp32 carry as well. The final division by the row sum uses
+// the same reference, so the result is unchanged up to rounding. A reference
+// at the row max makes the largest probability exactly 1, with no bf16
+// rounding error against the fp32 row sum: rows dominated by one key keep
+// that key's value exactly.
 constexpr float kTau = 8.0f;
 constexpr float kSumLimit = 256.0f;   // 2^kTau
 
@@ -460,10 +464,17 @@ __global__ __launch_bounds__(W * 64, W == 4 ? 2 : 1) void attn_fwd_bf16_kernel(c
         if (ok) x = *(const u32x4*)(qrow + 16 * s + 8 * half);
         qreg[qb][s] = __builtin_bit_cast(bf16x8, x);
       }
-      // RMS normalisation of the query row (fused: the normalised queries
-      // never leave registers). The two lane halves hold the two halves of
-      // the row; the result is rounded to bf16 as the MFMA operand.
-      if (p.qnorm) {
+      // The softmax scale c = scale * log2(e) is folded into the query
+      // operands (one bf16 rounding of c * q), so the score MFMAs produce
+      // base-2 logits directly. RMS normalisation of the query row is fused
+      // the same way: the normalised queries never leave registers (the two
+      // lane halves hold the two halves of the row).
+      if (!p.qnorm) {
+#pragma unroll
+        for (int s = 0; s < QS; ++s)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) qreg[qb][s][e] = (__bf16)((float)qreg[qb][s][e] * c);
+      } else {
         float ss = 0.f;
 #pragma unroll
         for (int s = 0; s < QS; ++s)
@@ -479,7 +490,7 @@ __global__ __launch_bounds__(W * 64, W == 4 ? 2 : 1) void attn_fwd_bf16_kernel(c
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
             const float gam = p.gamma_q != nullptr ? p.gamma_q[16 * s + 8 * half + e] : 1.0f;
-            qreg[qb][s][e] = (__bf16)((float)qreg[qb][s][e] * r * gam);
+            qreg[qb][s][e] = (__bf16)((float)qreg[qb][s][e] * r * (gam * c));
           }
       }
     }
@@ -491,11 +502,24 @@ __global__ __launch_bounds__(W * 64, W == 4 ? 2 : 1) void attn_fwd_bf16_kernel(c
       for (int b = 0; b < DB; ++b)
 #pragma unroll
         for (int i = 0; i < 16; ++i) oacc[qb][b][i] = 0.f;
-    float m_run[kQB], l_run[kQB];   // reference max (raw scores) and this lane's partial sum
+    // Online-softmax state of the lane's query row, in base-2 logit units u
+    // (the queries carry the scale): the reference r (scores are
+    // exponentiated as 2^(u - r)), this lane's partial row sum, and pen =
+    // +inf while the row has seen no unmasked key (0 after), which sends the
+    // first tile through the exact path. With kSeed, -r replicated over one
+    // accumulator block is the starting value of the score MFMAs, which then
+    // produce u - r directly and the exponent needs no subtraction (16
+    // registers, which the 4-wave schedules can spare).
+    constexpr bool kSeed = W == 4;
+    float r_ref[kQB], l_run[kQB], pen[kQB];
+    f32x16 neg_r[kQB];
 #pragma unroll
     for (int qb = 0; qb < kQB; ++qb) {
-      m_run[qb] = -INFINITY;
+      r_ref[qb] = 0.f;
       l_run[qb] = 0.f;
+      pen[qb] = INFINITY;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) neg_r[qb][i] = 0.f;
     }
     bf16x8 pprev[kQB][PS];          // probabilities of the previous tile (PV operand)
 
@@ -539,15 +563,12 @@ __global__ __launch_bounds__(W * 64, W == 4 ? 2 : 1) void attn_fwd_bf16_kernel(c
           for (int kbk = 0; kbk < KB; ++kbk)
             ka[s][kbk] = __builtin_bit_cast(bf16x8, kl[kbk * 32 * KPITCH + 2 * s]);
 #pragma unroll
-        for (int kbk = 0; kbk < KB; ++kbk)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) sacc[0][kbk][i] = 0.f;
-#pragma unroll
         for (int s = 0; s < QS; ++s)
 #pragma unroll
           for (int kbk = 0; kbk < KB; ++kbk)
-            sacc[0][kbk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[s][kbk], qreg[0][s],
-                                                                   sacc[0][kbk], 0, 0, 0);
+            sacc[0][kbk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                ka[s][kbk], qreg[0][s], s > 0 ? sacc[0][kbk] : kSeed ? neg_r[0] : f32x16{}, 0,
+                0, 0);
       }
       if constexpr (PV && QK) {
         __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 4, 0);
@@ -582,8 +603,9 @@ __global__ __launch_bounds__(W * 64, W == 4 ? 2 : 1) void attn_fwd_bf16_kernel(c
     };
     using kOn = std::true_type;
     using kOff = std::false_type;
-    // Online softmax of block qb for tile t (base 2, scale folded into c);
-    // produces the next PV operand and returns the rescale factor of O.
+    // Online softmax of block qb for tile t: sacc holds u - r, the base-2
+    // logits relative to the row's reference; produces the next PV operand
+    // and returns the rescale factor of O.
     auto softmax = [&](f32x16 (&sacc)[KB], int qb, int tile, bool masked, bf16x8 (&pout)[PS]) __attribute__((always_inline)) -> float {
       if (masked) {
         const int key0 = tile * BN;
@@ -598,35 +620,39 @@ __global__ __launch_bounds__(W * 64, W == 4 ? 2 : 1) void attn_fwd_bf16_kernel(c
             if (dead) sacc[kbk][i] = -INFINITY;
           }
       }
-      // Exponentials against reference mc (base 2), rounded to bf16 as the
-      // next PV operand; returns this lane's partial row sum (fp32).
-      auto exps = [&](float mc) __attribute__((always_inline)) -> float {
-        float ps4[4] = {0.f, 0.f, 0.f, 0.f};   // four independent partial sums
+      // Exponentials 2^(sacc - d), rounded to bf16 as the next PV operand;
+      // returns this lane's partial row sum (fp32), started at `first`.
+      auto exps = [&](auto shifted_c, float d, float first) __attribute__((always_inline)) -> float {
+        float ps4[4] = {first, 0.f, 0.f, 0.f};   // four independent partial sums
 #pragma unroll
         for (int ps = 0; ps < PS; ++ps)
 #pragma unroll
           for (int j = 0; j < 8; ++j) {
-            const float e =
-                __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[ps >> 1][(ps & 1) * 8 + j], c, -mc));
+            float x = sacc[ps >> 1][(ps & 1) * 8 + j];
+            if constexpr (decltype(shifted_c)::value) x -= d;
+            const float e = __builtin_amdgcn_exp2f(x);
             ps4[j & 3] += e;
             pout[ps][j] = (__bf16)e;
           }
         return (ps4[0] + ps4[1]) + (ps4[2] + ps4[3]);
       };
+      // sacc holds u - r (seeded) or u; shift: what the exponent subtracts
+      const float shift = kSeed ? 0.f : r_ref[qb];
       // Fast path: keep the current reference. Every probability is at most
       // its lane's partial sum, so if no lane's sum exceeds 2^kTau the tile
-      // is done without forming the row max and O needs no rescale. A -inf
-      // reference (first tile of a pass) gives inf or NaN sums and falls
+      // is done without forming the row max and O needs no rescale. A row
+      // that has seen no unmasked key starts its sum at +inf and falls
       // through, as does a row whose scores grew.
       {
-        const float rs = exps(m_run[qb] * c);
+        const float rs = exps(std::bool_constant<!kSeed>{}, shift, pen[qb]);
         if (__ballot(!(rs <= kSumLimit)) == 0) {
           l_run[qb] += rs;
           return 1.f;
         }
       }
-      // Exact path: row max (max chains, then one exchange between the lane
-      // halves); the reference moves to it.
+      // Exact path: the row max of sacc (max chains, then one exchange
+      // between the lane halves). The reference moves up to the row max, or,
+      // on a row's first unmasked tile, to it from wherever it was.
       float pm[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) pm[j] = vmax(sacc[0][2 * j], sacc[0][2 * j + 1]);
@@ -636,13 +662,19 @@ __global__ __launch_bounds__(W * 64, W == 4 ? 2 : 1) void attn_fwd_bf16_kernel(c
         for (int j = 0; j < 8; ++j) pm[j] = vmax(pm[j], vmax(sacc[kbk][2 * j], sacc[kbk][2 * j + 1]));
       float mx = vmax(vmax(vmax(pm[0], pm[1]), vmax(pm[2], pm[3])),
                       vmax(vmax(pm[4], pm[5]), vmax(pm[6], pm[7])));
-      mx = halves_max(mx);
-      const float m_old = m_run[qb];
-      const float m_use = vmax(m_old, mx);
-      const float alpha = (m_old == m_use || m_use == -INFINITY)
-                              ? 1.f : __builtin_amdgcn_exp2f((m_old - m_use) * c);
-      m_run[qb] = m_use;
-      const float rs = exps(m_use == -INFINITY ? 0.f : m_use * c);
+      mx = halves_max(mx) - shift;   // row max of u - r
+      const bool seen = pen[qb] == 0.f;
+      // d: how far the reference moves (0 while a row has no unmasked key)
+      const float d = seen ? vmax(mx, 0.f) : (mx == -INFINITY ? 0.f : mx);
+      // O and l are still 0 on an unseen row: no rescale
+      const float alpha = (!seen || d == 0.f) ? 1.f : __builtin_amdgcn_exp2f(-d);
+      r_ref[qb] += d;
+      if constexpr (kSeed) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) neg_r[qb][i] = -r_ref[qb];
+      }
+      if (mx != -INFINITY) pen[qb] = 0.f;
+      const float rs = exps(std::true_type{}, shift + d, 0.f);
       l_run[qb] = l_run[qb] * alpha + rs;
       return alpha;
     };
