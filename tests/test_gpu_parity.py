@@ -277,12 +277,12 @@ _MOVES = [(1000, 64, False, "bf16"), (1000, 128, True, "bf16"), (8192, 128, Fals
                          ids=lambda v: str(v))
 def test_reference_moves_on_every_tile(lib, Lk, d, causal, dtype, growth):
     """Keys along the query direction, scaled up with the key index: each 64-key tile raises
-    every row's maximum by `growth` (in base 2, after the softmax scale) over the last one.
-    At 80, past the 2^64 bound of the bf16 kernel's lazy rescaling, its exact path and the
-    rescale of O run on every tile; at 12 the reference moves every few tiles (bf16: 4-wave
-    schedule at Lk=1000, 8-wave at 8192). The fp32 kernel, which rescales exactly on every
-    tile, runs the growth of 12 (at 80 its scores reach ~600, where fp32 dot products alone
-    err by more than the 1e-4 bar)."""
+    every row's maximum by `growth` (in base 2, after the softmax scale) over the last one,
+    past the 2^8 bound of the bf16 kernel's lazy rescaling, so its exact path and the
+    rescale of O run on every tile (4-wave schedule at Lk=1000, 8-wave at 8192); 80 also
+    drives the probabilities of earlier tiles far below the fp32 range. The fp32 kernel,
+    which rescales exactly on every tile, runs the growth of 12 (at 80 its scores reach
+    ~600, where fp32 dot products alone err by more than the 1e-4 bar)."""
     B, H, Lq = 1, 2, 300
     alpha = growth / (np.log2(np.e) * np.sqrt(d))          # key scale added per 64 keys
     t = (alpha / 64.0) * np.arange(Lk, dtype=np.float64)

@@ -506,11 +506,14 @@ __global__ __launch_bounds__(W * 64, W == 4 ? 2 : 1) void attn_fwd_bf16_kernel(c
     // (the queries carry the scale): the reference r (scores are
     // exponentiated as 2^(u - r)), this lane's partial row sum, and pen =
     // +inf while the row has seen no unmasked key (0 after), which sends the
-    // first tile through the exact path. With kSeed, -r replicated over one
-    // accumulator block is the starting value of the score MFMAs, which then
-    // produce u - r directly and the exponent needs no subtraction (16
-    // registers, which the 4-wave schedules can spare).
-    constexpr bool kSeed = W == 4;
+    // first tile through the exact path. -r replicated over one accumulator
+    // block is the starting value of the score MFMAs, which then produce
+    // u - r directly, so the exponent needs no subtraction. The 4-wave
+    // schedules keep that block (16 registers) across the loop; the 8-wave
+    // one has no registers to spare and writes it from r before each score
+    // product, into registers that hold nothing live at that point.
+    constexpr bool kSeed = true;
+    constexpr bool kKeepSeed = W == 4;
     float r_ref[kQB], l_run[kQB], pen[kQB];
     f32x16 neg_r[kQB];
 #pragma unroll
@@ -557,6 +560,13 @@ __global__ __launch_bounds__(W * 64, W == 4 ? 2 : 1) void attn_fwd_bf16_kernel(c
               va[step], pprev[0][step / DB], oacc[0][step % DB], 0, 0, 0);
       }
       if constexpr (QK) {
+        f32x16 seed;
+        if constexpr (kKeepSeed) {
+          seed = neg_r[0];
+        } else {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) seed[i] = -r_ref[0];
+        }
 #pragma unroll
         for (int s = 0; s < QS; ++s)
 #pragma unroll
@@ -567,8 +577,7 @@ __global__ __launch_bounds__(W * 64, W == 4 ? 2 : 1) void attn_fwd_bf16_kernel(c
 #pragma unroll
           for (int kbk = 0; kbk < KB; ++kbk)
             sacc[0][kbk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                ka[s][kbk], qreg[0][s], s > 0 ? sacc[0][kbk] : kSeed ? neg_r[0] : f32x16{}, 0,
-                0, 0);
+                ka[s][kbk], qreg[0][s], s > 0 ? sacc[0][kbk] : seed, 0, 0, 0);
       }
       if constexpr (PV && QK) {
         __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 4, 0);
@@ -669,7 +678,7 @@ __global__ __launch_bounds__(W * 64, W == 4 ? 2 : 1) void attn_fwd_bf16_kernel(c
       // O and l are still 0 on an unseen row: no rescale
       const float alpha = (!seen || d == 0.f) ? 1.f : __builtin_amdgcn_exp2f(-d);
       r_ref[qb] += d;
-      if constexpr (kSeed) {
+      if constexpr (kKeepSeed) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) neg_r[qb][i] = -r_ref[qb];
       }
