@@ -32,7 +32,9 @@
  * Ownership and concurrency. The caller owns every buffer. The library keeps
  * no state between calls and allocates nothing; calls are reentrant. Work is
  * enqueued on `stream` (a hipStream_t; NULL = the default stream) and the
- * call returns without synchronising. o must not alias q, k or v.
+ * call returns without synchronising: every input must be ready, and every
+ * buffer the call writes must stay allocated and untouched, in that stream's
+ * order. o must not alias q, k or v.
  *
  * Schedules. bf16 problems with d = 128 and Lk >= 4096 run an 8-wave
  * workgroup schedule, others a 4-wave one; both compute the same result to
@@ -62,7 +64,9 @@ typedef enum {
                              bf16 with (Lk + 64) * d * 2 > 2^31 - 1 bytes per K/V head
                              (jagged: (max_Lk + 64) * Hkv * d * 2) */
   ATTN_EUNSUPPORTED = -2, /* head dim d not in {64, 128}, or unknown dtype */
-  ATTN_ELAUNCH = -3       /* the HIP launch reported an error */
+  ATTN_ELAUNCH = -3       /* the HIP launch reported an error. An error left pending by an
+                             earlier HIP call on the calling thread is cleared before each
+                             launch, so this status is about this call's launches only */
 } attn_status;
 
 typedef enum { ATTN_F32 = 0, ATTN_BF16 = 1 } attn_dtype;

@@ -29,3 +29,19 @@ def max_err(got: np.ndarray, want: np.ndarray) -> float:
     if got.size == 0:
         return 0.0
     return float(np.max(np.abs(got - want)))
+
+
+def nan_filled(like, shape=None, dtype=None):
+    """A device tensor shaped and typed like `like` (or as given), filled with NaN: a
+    sentinel that shows any output element a kernel leaves unwritten."""
+    import torch
+    if shape is None:
+        return torch.full_like(like, float("nan"))
+    return torch.full(shape, float("nan"), dtype=dtype, device="cuda")
+
+
+def assert_all_written(t, what="output"):
+    """Every element of t is finite: no NaN sentinel survived (checked on the device; one
+    boolean comes back)."""
+    import torch
+    assert bool(torch.isfinite(t).all().item()), f"{what}: some elements were never written"

@@ -1,6 +1,7 @@
 """The C ABI on the CPU: the library loads, exports every declared entry point,
 and rejects bad arguments before making any HIP call (no GPU needed)."""
 import ctypes
+import glob
 import os
 import re
 
@@ -9,27 +10,46 @@ import pytest
 import tiled_attention_attn_amd as taa
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "attn.h")
+INCLUDE = os.path.join(ROOT, "include")
+HEADER = os.path.join(INCLUDE, "attn.h")
+CSRC = os.path.join(ROOT, "tiled_attention_attn_amd", "csrc")
 
 
-def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**((?:attn|ikbo)_\w+)\s*\(", text, flags=re.M)))
+def declared_functions(path=None):
+    """Function names declared in one header, or in every header under include/."""
+    paths = [path] if path else sorted(glob.glob(os.path.join(INCLUDE, "*.h")))
+    names = set()
+    for p in paths:
+        text = re.sub(r"/\*.*?\*/", "", open(p).read(), flags=re.S)
+        names |= set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**((?:attn|ikbo)_\w+)\s*\(", text,
+                                flags=re.M))
+    return sorted(names)
+
+
+def _stale() -> bool:
+    """The library is missing or older than one of its sources or headers."""
+    if not os.path.exists(taa.LIB_PATH):
+        return True
+    built = os.path.getmtime(taa.LIB_PATH)
+    srcs = glob.glob(os.path.join(CSRC, "*")) + glob.glob(os.path.join(INCLUDE, "*.h"))
+    return any(os.path.getmtime(p) > built for p in srcs)
 
 
 @pytest.fixture(scope="module")
 def lib():
-    if not os.path.exists(taa.LIB_PATH):   # build only when nothing is built yet
+    if _stale():   # never test an old build against new sources
         from tiled_attention_attn_amd.build import build
         build()
     return taa.load_library()
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == ["attn_fwd", "attn_fwd_bcast", "attn_fwd_block_sparse",
-                                    "attn_fwd_jagged", "attn_fwd_qknorm", "attn_strerror",
-                                    "attn_version", "ikbo_linear"]
+    assert declared_functions(HEADER) == ["attn_fwd", "attn_fwd_bcast", "attn_fwd_block_sparse",
+                                          "attn_fwd_jagged", "attn_fwd_qknorm", "attn_strerror",
+                                          "attn_version", "ikbo_linear"]
+    assert declared_functions(os.path.join(INCLUDE, "attn_ceiling.h")) == [
+        "attn_ceiling_copy", "attn_ceiling_exp2", "attn_ceiling_fma", "attn_ceiling_lds_read",
+        "attn_ceiling_mfma_bf16"]
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -205,3 +225,20 @@ def qknorm(lib, q=FAKE, k=FAKE, v=FAKE, o=FAKE, gq=None, gk=None, eps=1e-6, kn=F
 ])
 def test_attn_fwd_qknorm_argument_checks(lib, kwargs, status):
     assert qknorm(lib, **kwargs) == status
+
+
+def test_ceiling_probe_argument_checks(lib):
+    """The ceiling probes reject bad arguments with -1 before any HIP call; an empty copy
+    launches nothing and succeeds."""
+    assert lib.attn_ceiling_mfma_bf16(None, 1, FAKE, 1, 8, 1, None) == -1
+    assert lib.attn_ceiling_mfma_bf16(FAKE, 0, FAKE, 1, 8, 1, None) == -1    # no operand lanes
+    assert lib.attn_ceiling_mfma_bf16(FAKE, 1, FAKE, 1, 6, 1, None) == -1    # waves not 4 or 8
+    assert lib.attn_ceiling_mfma_bf16(MISALIGNED, 1, FAKE, 1, 8, 1, None) == -1
+    assert lib.attn_ceiling_mfma_bf16(FAKE, 1, FAKE, 0, 8, 1, None) == -1    # no workgroups
+    assert lib.attn_ceiling_exp2(None, 1, 1, None) == -1
+    assert lib.attn_ceiling_exp2(FAKE, 0, 1, None) == -1
+    assert lib.attn_ceiling_fma(FAKE, 1, 0, None) == -1                      # no iterations
+    assert lib.attn_ceiling_lds_read(None, 1, 1, 0, None) == -1
+    assert lib.attn_ceiling_copy(FAKE, FAKE, 17, None) == -1                 # not 16-byte units
+    assert lib.attn_ceiling_copy(MISALIGNED, FAKE, 16, None) == -1
+    assert lib.attn_ceiling_copy(FAKE, FAKE, 0, None) == 0

@@ -5,7 +5,7 @@ import pytest
 
 import attn_inputs as ai
 import oracle
-from gpu_util import TOL, from_dev, i32_dev, max_err, to_dev
+from gpu_util import TOL, assert_all_written, from_dev, i32_dev, max_err, nan_filled, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -88,9 +88,11 @@ def test_block_sparse_full_size_workload_sampled(lib):
     import torch
     w = ai.make_workload("block_sparse_L16384", seed=0)
     q, k, v = (to_dev(x, w.dtype) for x in (w.q, w.k, w.v))
-    o = lib.attn_fwd_block_sparse(q, k, v, torch.from_numpy(w.block_mask).cuda(), w.blk,
-                                  causal=w.causal)
+    o = nan_filled(q)
+    lib.attn_fwd_block_sparse(q, k, v, torch.from_numpy(w.block_mask).cuda(), w.blk, o,
+                              causal=w.causal)
     torch.cuda.synchronize()
+    assert_all_written(o)
     rng = np.random.default_rng(11)
     B, H, Lq, _ = w.q.shape
     worst = 0.0

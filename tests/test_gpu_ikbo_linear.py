@@ -12,7 +12,7 @@ import pytest
 
 import attn_inputs as ai
 import oracle
-from gpu_util import from_dev, i32_dev, to_dev
+from gpu_util import assert_all_written, from_dev, i32_dev, nan_filled, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -123,8 +123,13 @@ def test_ikbo_linear_full_size_workload_sampled(lib):
     import torch
     w = ai.make_linear_workload("ikbo_linear_Bc65536", seed=0)
     xu, xc, wt = (to_dev(x, "bf16") for x in (w.x_user, w.x_cand, w.w))
-    y, z = lib.ikbo_linear(xu, xc, wt, i32_dev(w.cand2user), torch.from_numpy(w.bias).cuda())
+    B_u, N = w.x_user.shape[0], w.w.shape[0]
+    y = nan_filled(None, (w.x_cand.shape[0], N), torch.bfloat16)
+    z = nan_filled(None, (B_u, N), torch.float32)
+    lib.ikbo_linear(xu, xc, wt, i32_dev(w.cand2user), torch.from_numpy(w.bias).cuda(), y, z)
     torch.cuda.synchronize()
+    assert_all_written(y, "y")
+    assert_all_written(z, "z")
     rng = np.random.default_rng(13)
     B_c = w.x_cand.shape[0]
     rows = np.unique(np.concatenate([[0, 127, 128, B_c - 1], rng.integers(0, B_c, 60)]))

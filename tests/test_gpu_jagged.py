@@ -5,7 +5,7 @@ import pytest
 
 import attn_inputs as ai
 import oracle
-from gpu_util import TOL, from_dev, i32_dev, max_err, to_dev
+from gpu_util import TOL, assert_all_written, from_dev, i32_dev, max_err, nan_filled, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -98,9 +98,11 @@ def test_jagged_full_size_workload_sampled(lib):
     import torch
     w = ai.make_workload("jagged_causal_B32", seed=0)
     q, k, v = (to_dev(x, w.dtype) for x in (w.q, w.k, w.v))
-    o = lib.attn_fwd_jagged(q, k, v, i32_dev(w.q_offsets), i32_dev(w.kv_offsets),
-                            w.meta["max_Lq"], w.meta["max_Lk"], causal=w.causal)
+    o = nan_filled(q)
+    lib.attn_fwd_jagged(q, k, v, i32_dev(w.q_offsets), i32_dev(w.kv_offsets),
+                        w.meta["max_Lq"], w.meta["max_Lk"], o, causal=w.causal)
     torch.cuda.synchronize()
+    assert_all_written(o)
     rng = np.random.default_rng(9)
     B, H, Hkv = len(w.q_offsets) - 1, w.q.shape[1], w.k.shape[1]
     worst = 0.0

@@ -9,7 +9,7 @@ import pytest
 
 import attn_inputs as ai
 import oracle
-from gpu_util import TOL, from_dev, i32_dev, max_err, to_dev
+from gpu_util import TOL, assert_all_written, from_dev, i32_dev, max_err, nan_filled, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -205,12 +205,14 @@ def test_full_size_workload_sampled(lib, name):
     w = ai.make_workload(name, seed=0)
     dtype = w.dtype
     q, k, v = (to_dev(x, dtype) for x in (w.q, w.k, w.v))
+    o = nan_filled(q)
     if w.cand2user is not None:
-        o = lib.attn_fwd_bcast(q, k, v, i32_dev(w.cand2user), causal=w.causal,
-                               kv_len=i32_dev(w.kv_len))
+        lib.attn_fwd_bcast(q, k, v, i32_dev(w.cand2user), o, causal=w.causal,
+                           kv_len=i32_dev(w.kv_len))
     else:
-        o = lib.attn_fwd(q, k, v, causal=w.causal, kv_len=i32_dev(w.kv_len))
+        lib.attn_fwd(q, k, v, o, causal=w.causal, kv_len=i32_dev(w.kv_len))
     torch.cuda.synchronize()
+    assert_all_written(o, name)
     rng = np.random.default_rng(7)
     NB, H, Lq, d = w.q.shape
     worst = 0.0

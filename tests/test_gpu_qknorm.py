@@ -6,7 +6,7 @@ import pytest
 
 import attn_inputs as ai
 import oracle
-from gpu_util import TOL, from_dev, i32_dev, max_err, to_dev
+from gpu_util import TOL, assert_all_written, from_dev, i32_dev, max_err, nan_filled, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -85,9 +85,11 @@ def test_qknorm_full_size_workload_sampled(lib):
     import torch
     w = ai.make_workload("qknorm_gqa_causal_L16384", seed=0)
     q, k, v = (to_dev(x, "bf16") for x in (w.q, w.k, w.v))
-    o = lib.attn_fwd_qknorm(q, k, v, torch.from_numpy(w.gamma_q).cuda(),
-                            torch.from_numpy(w.gamma_k).cuda(), w.eps, causal=w.causal)
+    o = nan_filled(q)
+    lib.attn_fwd_qknorm(q, k, v, torch.from_numpy(w.gamma_q).cuda(),
+                        torch.from_numpy(w.gamma_k).cuda(), w.eps, o, causal=w.causal)
     torch.cuda.synchronize()
+    assert_all_written(o)
     rng = np.random.default_rng(17)
     B, H, Lq, _ = w.q.shape
     worst = 0.0

@@ -3,6 +3,12 @@
 Argument marshalling only: shapes, dtypes and devices of torch tensors are
 checked and their device pointers handed to the C ABI. Every step of the
 computation runs in the library's HIP kernels; there is no fallback path.
+
+Streams: every call takes `stream=` (a torch stream; default torch's current
+one) and enqueues its kernels there without synchronising. Tensors the binding
+allocates for a call (outputs not passed in, the uint8 copy of a bool block
+mask, the key workspace) are allocated with that stream current, so torch's
+caching allocator reuses them only in that stream's order.
 """
 from __future__ import annotations
 
@@ -99,7 +105,7 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
-def _prep(q, k, v, o, extra):
+def _prep(q, k, v, o, extra, stream=None):
     import torch
     for name, t in (("q", q), ("k", k), ("v", v)):
         if not t.is_cuda:
@@ -115,7 +121,7 @@ def _prep(q, k, v, o, extra):
     if q.shape[3] != k.shape[3]:
         raise ValueError("q and k must have the same head dimension")
     if o is None:
-        o = torch.empty_like(q)
+        o = _on(stream, lambda: torch.empty_like(q))
     elif o.shape != q.shape or o.dtype != q.dtype or not o.is_contiguous() or not o.is_cuda:
         raise ValueError("o must be a contiguous device tensor shaped and typed like q")
     for name, t in extra.items():
@@ -124,10 +130,24 @@ def _prep(q, k, v, o, extra):
     return o
 
 
-def _stream(stream):
+def _torch_stream(stream):
+    """The torch stream the work is enqueued on: `stream`, or torch's current one."""
     import torch
-    s = torch.cuda.current_stream() if stream is None else stream
-    return ctypes.c_void_p(s.cuda_stream)
+    return torch.cuda.current_stream() if stream is None else stream
+
+
+def _stream(stream):
+    return ctypes.c_void_p(_torch_stream(stream).cuda_stream)
+
+
+def _on(stream, fn):
+    """Run fn (an allocation, or a conversion that allocates) with `stream` current, so that
+    torch's caching allocator ties the new memory to the stream the kernels use: memory
+    freed by the caller (or, for temporaries, when this call returns) is then only reused
+    by work ordered after those kernels on that stream."""
+    import torch
+    with torch.cuda.stream(_torch_stream(stream)):
+        return fn()
 
 
 def attn_fwd(q, k, v, o=None, *, causal=False, kv_len=None, scale=0.0, stream=None):
@@ -138,7 +158,7 @@ def attn_fwd(q, k, v, o=None, *, causal=False, kv_len=None, scale=0.0, stream=No
     Enqueued on `stream` (default: torch's current stream); not synchronised.
     """
     lib = load_library()
-    o = _prep(q, k, v, o, {"kv_len": kv_len})
+    o = _prep(q, k, v, o, {"kv_len": kv_len}, stream)
     B, H, Lq, d = q.shape
     if k.shape[0] != B:
         raise ValueError("k/v batch must equal q batch (use attn_fwd_bcast for a broadcast)")
@@ -158,7 +178,7 @@ def attn_fwd_bcast(q, k, v, cand2user, o=None, *, causal=False, kv_len=None, sca
     kv_len int32 [B_u] device tensor or None. Returns o [B_c,H,Lq,d].
     """
     lib = load_library()
-    o = _prep(q, k, v, o, {"cand2user": cand2user, "kv_len": kv_len})
+    o = _prep(q, k, v, o, {"cand2user": cand2user, "kv_len": kv_len}, stream)
     B_c, H, Lq, d = q.shape
     B_u = k.shape[0]
     if cand2user.numel() != B_c:
@@ -195,7 +215,7 @@ def attn_fwd_jagged(q, k, v, q_offsets, kv_offsets, max_lq, max_lk, o=None, *, c
     if q_offsets.numel() != kv_offsets.numel() or q_offsets.numel() < 1:
         raise ValueError("q_offsets and kv_offsets must both hold B+1 entries")
     if o is None:
-        o = torch.empty_like(q)
+        o = _on(stream, lambda: torch.empty_like(q))
     elif o.shape != q.shape or o.dtype != q.dtype or not o.is_contiguous() or not o.is_cuda:
         raise ValueError("o must be a contiguous device tensor shaped and typed like q")
     B = q_offsets.numel() - 1
@@ -216,13 +236,13 @@ def attn_fwd_block_sparse(q, k, v, block_mask, blk, o=None, *, causal=False, kv_
     """
     import torch
     lib = load_library()
-    o = _prep(q, k, v, o, {"kv_len": kv_len})
+    o = _prep(q, k, v, o, {"kv_len": kv_len}, stream)
     B, H, Lq, d = q.shape
     Lk = k.shape[2]
     if k.shape[0] != B:
         raise ValueError("k/v batch must equal q batch")
-    if block_mask.dtype == torch.bool:
-        block_mask = block_mask.to(torch.uint8)
+    if block_mask.dtype == torch.bool:   # converted on the kernels' stream, ahead of them
+        block_mask = _on(stream, lambda: block_mask.to(torch.uint8))
     if (block_mask.dtype != torch.uint8 or not block_mask.is_cuda or not block_mask.is_contiguous()
             or block_mask.dim() != 3):
         raise ValueError("block_mask must be a contiguous 3-D uint8 device tensor")
@@ -248,7 +268,7 @@ def attn_fwd_qknorm(q, k, v, gamma_q=None, gamma_k=None, eps=1e-6, o=None, k_nor
     """
     import torch
     lib = load_library()
-    o = _prep(q, k, v, o, {"kv_len": kv_len})
+    o = _prep(q, k, v, o, {"kv_len": kv_len}, stream)
     B, H, Lq, d = q.shape
     if k.shape[0] != B:
         raise ValueError("k/v batch must equal q batch")
@@ -259,7 +279,7 @@ def attn_fwd_qknorm(q, k, v, gamma_q=None, gamma_k=None, eps=1e-6, o=None, k_nor
                               or g.numel() != d):
             raise ValueError(f"{name} must be a contiguous float32 device tensor with d entries")
     if k_norm is None:
-        k_norm = torch.empty_like(k)
+        k_norm = _on(stream, lambda: torch.empty_like(k))
     elif (k_norm.shape != k.shape or k_norm.dtype != k.dtype or not k_norm.is_cuda
           or not k_norm.is_contiguous()):
         raise ValueError("k_norm must be a contiguous device tensor shaped and typed like k")
@@ -298,12 +318,13 @@ def ikbo_linear(x_user, x_cand, w, cand2user, bias=None, y=None, z=None, *, out_
                              or not bias.is_contiguous() or bias.numel() != N):
         raise ValueError("bias must be a contiguous float32 device tensor with N entries")
     if y is None:
-        y = torch.empty((B_c, N), dtype=out_dtype or torch.bfloat16, device=x_cand.device)
+        y = _on(stream, lambda: torch.empty((B_c, N), dtype=out_dtype or torch.bfloat16,
+                                            device=x_cand.device))
     elif (tuple(y.shape) != (B_c, N) or not y.is_cuda or not y.is_contiguous()
           or y.dtype not in (torch.bfloat16, torch.float32)):
         raise ValueError("y must be a contiguous [B_c, N] bfloat16 or float32 device tensor")
     if z is None:
-        z = torch.empty((B_u, N), dtype=torch.float32, device=x_user.device)
+        z = _on(stream, lambda: torch.empty((B_u, N), dtype=torch.float32, device=x_user.device))
     elif (tuple(z.shape) != (B_u, N) or z.dtype != torch.float32 or not z.is_cuda
           or not z.is_contiguous()):
         raise ValueError("z must be a contiguous [B_u, N] float32 device tensor")

@@ -894,6 +894,9 @@ __global__ __launch_bounds__(W * 64, W == 4 ? 2 : 1) void attn_fwd_bf16_kernel(c
 
 // Host-side launcher (one instance per head dim, causal flag and wave count).
 hipError_t launch_bf16(const Params& p, int D, bool causal, hipStream_t stream) {
+  // An error left pending by an earlier HIP call on this thread is dropped
+  // here, so that the status returned after the launch is this launch's.
+  (void)hipGetLastError();
   dim3 grid(p.T), block(p.waves * 64);
 #define ATTN_LAUNCH(DD, CC, WW)                                                                 \
   do {                                                                                          \

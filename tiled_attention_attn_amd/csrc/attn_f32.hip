@@ -119,6 +119,9 @@ __global__ __launch_bounds__(kF32Rows) void attn_fwd_f32_kernel(const Params p) 
 }
 
 hipError_t launch_f32(const Params& p, int D, bool causal, hipStream_t stream) {
+  // An error left pending by an earlier HIP call on this thread is dropped
+  // here, so that the status returned after the launch is this launch's.
+  (void)hipGetLastError();
   const int nrb = (p.Lq + kF32Rows - 1) / kF32Rows;
   dim3 grid((unsigned)((size_t)p.NB * p.H * nrb)), block(kF32Rows);
   if (D == 128) {

@@ -541,6 +541,9 @@ hipError_t launch_cfg(const GemmParams& q, bool gather, bool out_f32, hipStream_
   const int slots = (device_cus() * GemmShape<CFG>::kPerCU) & ~7;
   if (persist && slots >= 8 && q.tiles > slots) nblk = slots;
   const dim3 grid((unsigned)nblk), block(GemmShape<CFG>::kWaves * 64);
+  // An error left pending by an earlier HIP call on this thread is dropped
+  // here, so that the status returned after the launch is this launch's.
+  (void)hipGetLastError();
   if (gather) {
     if (out_f32) hipLaunchKernelGGL((ikbo_gemm_kernel<CFG, true, true>), grid, block, 0, stream, q);
     else hipLaunchKernelGGL((ikbo_gemm_kernel<CFG, true, false>), grid, block, 0, stream, q);

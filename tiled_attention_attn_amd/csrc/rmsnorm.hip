@@ -78,6 +78,9 @@ hipError_t launch_rmsnorm_rows(const void* x, void* y, const float* gamma, float
   const int64_t blocks = (rows + per_block - 1) / per_block;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
   const dim3 grid((unsigned)blocks), block(kThreads);
+  // An error left pending by an earlier HIP call on this thread is dropped
+  // here, so that the status returned after the launch is this launch's.
+  (void)hipGetLastError();
   if (D == 128)
     hipLaunchKernelGGL(rmsnorm_rows_kernel<16>, grid, block, 0, stream, (const __bf16*)x,
                        (__bf16*)y, gamma, eps, rows);
