@@ -1,22 +1,27 @@
 """Benchmark of the fused tiled attention forward on one MI355X.
 
 python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-variants]
-                [--no-cpu-baseline]
+                [--no-cpu-baseline] [--no-ceiling] [--ceiling-only]
 
 A step is one attention forward (one launch of the library's kernel) over the
 workload's synthetic, seeded inputs, which are resident in HBM before timing
 starts. Prints ONE JSON line. `value` is algorithmic TFLOP/s (4*d FLOPs per
-unmasked query/key pair) of the headline workload; `roofline` relates the
-kernel's average launch time to the bf16 MFMA peak (`cold_ms_per_step` is the
-median step time with L2 and the last-level cache flushed before each step);
-`cpu_baseline` times the float64 oracle on a bounded sample of the same
-workload on the host cores;
-`variants` holds the other workloads (the broadcast one also in GB/s) and the
-in-kernel broadcast linear layer (both of its launches per step, 2 FLOPs per
-multiply-add of the decomposed products, with torch's hipBLASLt products and
-gather on the same inputs timed beside it for context). A step of the
-q/k-normalised workload is both of its launches (key normalisation, then the
-attention pass with the query normalisation fused).
+unmasked query/key pair) of the headline workload, from HIP events around the
+timed launches on the launch stream. `roofline` relates it to the bf16 MFMA
+spec peak and to the peak the ceiling probes measure on the same GPU in the
+same run (`frac_of_measured_peak`), warm (back-to-back launches) and cold
+(`cold_ms_per_step`: median step time with L2 and the last-level cache
+flushed by a 512 MiB write before each step). `ceiling` holds those probes:
+MFMA with N(0,1) and constant operands, v_exp_f32, fp32 FMA, LDS reads and
+an HBM copy. `cpu_baseline` times the float64 oracle on the host cores (one
+thread per core of this job's share), over the whole workload where that
+takes seconds and on a labelled sample otherwise. `variants` holds the other
+workloads (the broadcast one also in GB/s), each with its own fractions, error
+and CPU baseline, and the in-kernel broadcast linear layer (both of its
+launches per step, 2 FLOPs per multiply-add of the decomposed products, with
+torch's hipBLASLt products and gather on the same inputs timed beside it for
+context). A step of the q/k-normalised workload is both of its launches (key
+normalisation, then the attention pass with the query normalisation fused).
 """
 from __future__ import annotations
 
@@ -202,8 +207,9 @@ def time_cold(fn, reps: int = 10) -> float:
     return float(np.median(times))
 
 
-def sampled_error(run: Runner, seed: int = 1, nrows: int = 4) -> float:
-    """Max abs error of a few output rows against the float64 oracle."""
+def sampled_error(run: Runner, seed: int = 1, nrows: int = 4) -> tuple[float, dict]:
+    """Max abs error of a few output rows against the float64 oracle, and where it is
+    (batch entry or sequence b, head h, query row, column)."""
     import oracle
     import torch
     w = run.w
@@ -211,7 +217,7 @@ def sampled_error(run: Runner, seed: int = 1, nrows: int = 4) -> float:
     if w.q_offsets is not None:
         return _sampled_error_jagged(run, rng, nrows)
     NB, H, Lq, _ = w.q.shape
-    worst = 0.0
+    worst, where = 0.0, {}
     for _ in range(2):
         b, h = int(rng.integers(NB)), int(rng.integers(H))
         rows = np.unique(np.concatenate([[0, Lq - 1], rng.integers(0, Lq, nrows)]))
@@ -230,16 +236,20 @@ def sampled_error(run: Runner, seed: int = 1, nrows: int = 4) -> float:
                                                      causal=w.causal, kv_len=kvl)
         else:
             ref = oracle.attention_rows(qf, kf, vf, 0, 0, rows, causal=w.causal, kv_len=kvl)
-        worst = max(worst, float(np.abs(got - ref).max()))
-    return worst
+        err = np.abs(got - ref)
+        i, j = np.unravel_index(int(np.argmax(err)), err.shape)
+        if err[i, j] >= worst:
+            worst = float(err[i, j])
+            where = {"b": b, "h": h, "row": int(rows[i]), "col": int(j)}
+    return worst, where
 
 
-def _sampled_error_jagged(run: Runner, rng, nrows: int) -> float:
+def _sampled_error_jagged(run: Runner, rng, nrows: int) -> tuple[float, dict]:
     import oracle
     import torch
     w = run.w
     H, Hkv = w.q.shape[1], w.k.shape[1]
-    worst = 0.0
+    worst, where = 0.0, {}
     for _ in range(2):
         b, h = int(rng.integers(len(w.q_offsets) - 1)), int(rng.integers(H))
         qs, qe = int(w.q_offsets[b]), int(w.q_offsets[b + 1])
@@ -253,73 +263,166 @@ def _sampled_error_jagged(run: Runner, rng, nrows: int) -> float:
             ai.to_f64(w.q[qs:qe, h:h + 1], w.dtype), ai.to_f64(w.k[ks:ke, g:g + 1], w.dtype),
             ai.to_f64(w.v[ks:ke, g:g + 1], w.dtype), [0, qe - qs], [0, ke - ks], 0, 0, rows,
             causal=w.causal)
-        worst = max(worst, float(np.abs(got - ref).max()))
-    return worst
+        err = np.abs(got - ref)
+        i, j = np.unravel_index(int(np.argmax(err)), err.shape)
+        if err[i, j] >= worst:
+            worst = float(err[i, j])
+            where = {"b": b, "h": h, "row": int(rows[i]), "col": int(j)}
+    return worst, where
 
 
-def cpu_baseline(w: ai.AttnInputs, budget_s: float = 15.0) -> dict:
-    """Time the float64 oracle, as it stands, on a bounded sample of rows.
+def oracle_threads() -> tuple[int, int]:
+    """(threads the oracle runs on, cores in this process's affinity set). The threads are
+    the affinity set, capped by OMP_NUM_THREADS when it is set (this job's share of the
+    host's cores)."""
+    aff = len(os.sched_getaffinity(0))
+    env = os.environ.get("OMP_NUM_THREADS", "")
+    n = min(aff, int(env)) if env.isdigit() and int(env) > 0 else aff
+    return max(1, n), aff
 
-    Rows are drawn uniformly over (batch entry, head, query row) so causal and
-    kv_len masking weigh in as in the full workload; the oracle computes each
-    row's full score row (masked keys included), but only unmasked pairs count
-    as algorithmic FLOPs, as on the GPU. Heads are added until the time budget is spent.
-    """
+
+def _units(w: ai.AttnInputs):
+    """(batch entry or sequence, head) pairs of a workload with their query-row counts."""
+    if w.q_offsets is not None:
+        lq = np.diff(w.q_offsets)
+        return [(b, h, int(lq[b])) for b in range(len(lq)) for h in range(w.q.shape[1])
+                if lq[b] > 0]
+    NB, H, Lq, _ = w.q.shape
+    return [(b, h, Lq) for b in range(NB) for h in range(H)]
+
+
+def _allowed_pairs(w: ai.AttnInputs, b: int, h: int, rows: np.ndarray) -> int:
+    """Unmasked (query, key) pairs of the given query rows of (b, h)."""
+    if w.q_offsets is not None:
+        lk = int(np.diff(w.kv_offsets)[b])
+        return int((np.minimum(rows + 1, lk) if w.causal else np.full(len(rows), lk)).sum())
+    Lk = w.k.shape[2]
+    u = b if w.cand2user is None else int(w.cand2user[b])
+    n = Lk if w.kv_len is None else int(min(max(w.kv_len[u], 0), Lk))
+    top = np.minimum(rows + 1, n) if w.causal else np.full(len(rows), n)
+    if w.block_mask is None:
+        return int(top.sum())
+    bm = w.block_mask[0 if w.block_mask.shape[0] == 1 else h]
+    total = 0
+    for kb in range(bm.shape[1]):
+        lo, hi = kb * w.blk, min((kb + 1) * w.blk, n)
+        on = bm[rows // w.blk, kb] != 0
+        total += int(np.maximum(np.minimum(top, hi) - lo, 0)[on].sum())
+    return total
+
+
+def _oracle_unit(w: ai.AttnInputs, b: int, h: int, rows) -> int:
+    """The oracle as it stands on one (batch entry or sequence b, head h): every query row
+    (rows None) or the given ones. Returns the algorithmic FLOPs of those rows (4 d per
+    unmasked pair), which is what the GPU is credited with for the same rows."""
     import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:
-        cores = os.cpu_count() or 1
-    rng = np.random.default_rng(123)
-    heads_done, flops, t_total = 0, 0, 0.0
-    rows_per_head = 256
-    if w.q_offsets is not None:   # jagged: random (sequence, head) pairs
-        H, d, Hkv = w.q.shape[1], w.q.shape[2], w.k.shape[1]
-        while t_total < budget_s and heads_done < 4096:
-            b, h = int(rng.integers(len(w.q_offsets) - 1)), int(rng.integers(H))
-            qs, qe = int(w.q_offsets[b]), int(w.q_offsets[b + 1])
-            ks, ke = int(w.kv_offsets[b]), int(w.kv_offsets[b + 1])
-            if qe == qs:
-                continue
-            rows = np.sort(rng.choice(qe - qs, size=min(rows_per_head, qe - qs), replace=False))
-            g = h // (H // Hkv)
-            qf, kf, vf = (ai.to_f64(x, w.dtype) for x in
-                          (w.q[qs:qe, h:h + 1], w.k[ks:ke, g:g + 1], w.v[ks:ke, g:g + 1]))
-            t0 = time.perf_counter()
-            oracle.attention_jagged_rows(qf, kf, vf, [0, qe - qs], [0, ke - ks], 0, 0, rows,
-                                         causal=w.causal)
-            t_total += time.perf_counter() - t0
-            valid = np.minimum(rows + 1, ke - ks) if w.causal else np.full(len(rows), ke - ks)
-            flops += 4 * d * int(valid.sum())
-            heads_done += 1
-        return {"value": flops / t_total / 1e12, "unit": "TFLOP/s", "cores": int(cores),
-                "kind": "oracle",
-                "sample": f"{heads_done} random (sequence, head) pairs x up to {rows_per_head} "
-                          f"random query rows of {w.meta} ({flops:.3e} algorithmic FLOPs in "
-                          f"{t_total:.1f} s)"}
-    NB, H, Lq, d = w.q.shape
-    Hkv, Lk = w.k.shape[1], w.k.shape[2]
-    while t_total < budget_s and heads_done < 4096:
-        b, h = int(rng.integers(NB)), int(rng.integers(H))
-        rows = np.sort(rng.choice(Lq, size=min(rows_per_head, Lq), replace=False))
-        u = b if w.cand2user is None else int(w.cand2user[b])
+    d = w.q.shape[-1]
+    if w.q_offsets is not None:
+        H, Hkv = w.q.shape[1], w.k.shape[1]
         g = h // (H // Hkv)
-        qf = ai.to_f64(w.q[b:b + 1, h:h + 1], w.dtype)
-        kf = ai.to_f64(w.k[u:u + 1, g:g + 1], w.dtype)
-        vf = ai.to_f64(w.v[u:u + 1, g:g + 1], w.dtype)
-        kvl = None if w.kv_len is None else w.kv_len[u:u + 1]
-        t0 = time.perf_counter()
-        oracle.attention_rows(qf, kf, vf, 0, 0, rows, causal=w.causal, kv_len=kvl)
-        t_total += time.perf_counter() - t0
-        n = Lk if kvl is None else int(min(max(kvl[0], 0), Lk))
-        valid = np.minimum(rows + 1, n) if w.causal else np.full(len(rows), n)
-        flops += 4 * d * int(valid.sum())
-        heads_done += 1
-    return {"value": flops / t_total / 1e12, "unit": "TFLOP/s", "cores": int(cores),
-            "kind": "oracle",
-            "sample": f"{heads_done} random (batch, head) pairs x {rows_per_head} random query "
-                      f"rows of {w.meta} ({flops:.3e} algorithmic FLOPs in {t_total:.1f} s)"}
+        qs, qe = int(w.q_offsets[b]), int(w.q_offsets[b + 1])
+        ks, ke = int(w.kv_offsets[b]), int(w.kv_offsets[b + 1])
+        qf, kf, vf = (ai.to_f64(x, w.dtype) for x in
+                      (w.q[qs:qe, h:h + 1], w.k[ks:ke, g:g + 1], w.v[ks:ke, g:g + 1]))
+        if rows is None:
+            oracle.attention_jagged(qf, kf, vf, [0, qe - qs], [0, ke - ks], causal=w.causal,
+                                    scale=w.scale)
+            rows = np.arange(qe - qs)
+        else:
+            oracle.attention_jagged_rows(qf, kf, vf, [0, qe - qs], [0, ke - ks], 0, 0, rows,
+                                         causal=w.causal, scale=w.scale)
+        return 4 * d * _allowed_pairs(w, b, h, rows)
+    H, Hkv = w.q.shape[1], w.k.shape[1]
+    g = h // (H // Hkv)
+    u = b if w.cand2user is None else int(w.cand2user[b])
+    qf, kf, vf = (ai.to_f64(x, w.dtype) for x in
+                  (w.q[b:b + 1, h:h + 1], w.k[u:u + 1, g:g + 1], w.v[u:u + 1, g:g + 1]))
+    kvl = None if w.kv_len is None else w.kv_len[u:u + 1]
+    if w.meta.get("kind") == "qknorm":
+        if rows is None:
+            oracle.attention_qknorm(qf, kf, vf, w.gamma_q, w.gamma_k, w.eps, causal=w.causal,
+                                    kv_len=kvl, scale=w.scale)
+        else:
+            oracle.attention_qknorm_rows(qf, kf, vf, 0, 0, rows, w.gamma_q, w.gamma_k, w.eps,
+                                         causal=w.causal, kv_len=kvl, scale=w.scale)
+    elif w.block_mask is not None:
+        bm = w.block_mask[0:1] if w.block_mask.shape[0] == 1 else w.block_mask[h:h + 1]
+        if rows is None:
+            oracle.attention_block_sparse(qf, kf, vf, bm, w.blk, causal=w.causal, kv_len=kvl,
+                                          scale=w.scale)
+        else:
+            oracle.attention_block_sparse_rows(qf, kf, vf, bm, w.blk, 0, 0, rows,
+                                               causal=w.causal, kv_len=kvl, scale=w.scale)
+    elif rows is None:
+        oracle.attention(qf, kf, vf, causal=w.causal, kv_len=kvl, scale=w.scale)
+    else:
+        oracle.attention_rows(qf, kf, vf, 0, 0, rows, causal=w.causal, kv_len=kvl,
+                              scale=w.scale)
+    if rows is None:
+        rows = np.arange(w.q.shape[2])
+    return 4 * d * _allowed_pairs(w, b, h, rows)
+
+
+def cpu_baseline(w: ai.AttnInputs, full: bool, budget_s: float = 15.0) -> dict:
+    """Time the float64 oracle, as it stands, on the host cores: one thread per core of
+    this job's share (see oracle_threads), each running the oracle on one (batch entry or
+    sequence, head) at a time, with the BLAS inside each call single-threaded.
+
+    full: every (b, h) pair and every query row, the whole workload. Otherwise a bounded
+    sample: random pairs with up to 256 random query rows each (so causal and kv_len
+    masking weigh in as in the whole workload), submitted until `budget_s` of wall time
+    is spent. The oracle computes each sampled row's full score row, masked keys
+    included; only unmasked pairs count as FLOPs, as on the GPU."""
+    import concurrent.futures as cf
+    import contextlib
+    try:
+        from threadpoolctl import threadpool_limits
+        blas_one = threadpool_limits(1)
+    except Exception:
+        blas_one = contextlib.nullcontext()
+    threads, aff = oracle_threads()
+    units = _units(w)
+    rng = np.random.default_rng(123)
+    flops, done = 0, 0
+    t0 = time.perf_counter()
+    with blas_one, cf.ThreadPoolExecutor(threads) as ex:
+        if full:
+            for f in ex.map(lambda u: _oracle_unit(w, u[0], u[1], None), units):
+                flops += f
+            done = len(units)
+        else:
+            order = rng.permutation(len(units))
+            pending, i = set(), 0
+            while True:
+                while len(pending) < threads and time.perf_counter() - t0 < budget_s:
+                    b, h, L = units[order[i % len(units)]]
+                    i += 1
+                    rows = np.sort(rng.choice(L, size=min(256, L), replace=False))
+                    pending.add(ex.submit(_oracle_unit, w, b, h, rows))
+                if not pending:
+                    break
+                finished, pending = cf.wait(pending, return_when=cf.FIRST_COMPLETED)
+                for f in finished:
+                    flops += f.result()
+                    done += 1
+    wall = time.perf_counter() - t0
+    unit_name = "(sequence, head)" if w.q_offsets is not None else "(batch entry, head)"
+    what = {k: v for k, v in w.meta.items() if k != "kind"}
+    if full:
+        sample = (f"the whole workload: all {done} {unit_name} pairs, every query row "
+                  f"({flops:.3e} algorithmic FLOPs in {wall:.1f} s) of {what}")
+    else:
+        sample = (f"sampled: {done} random {unit_name} pairs x up to 256 random query rows "
+                  f"({flops:.3e} algorithmic FLOPs in {wall:.1f} s) of {what}")
+    return {"value": flops / wall / 1e12, "unit": "TFLOP/s", "cores": threads,
+            "affinity_cores": aff, "kind": "oracle", "full": bool(full),
+            "seconds": round(wall, 2), "sample": sample}
+
+
+# Workloads whose whole oracle run stays within seconds on the host: the CPU baseline
+# runs them in full; the others (the oracle materialises every score row, about
+# 4.4 TFLOP of fp64 work on the L=16384 shapes) are sampled.
+CPU_FULL = {"fp32_tiny", "dense_causal_L2048", "bcast_Bc1024_Bu32", "masked_kvlen_L4096_d64"}
 
 
 def linear_variant(name: str, steps: int, warmup: int = 3) -> dict:
@@ -366,6 +469,9 @@ def linear_variant(name: str, steps: int, warmup: int = 3) -> dict:
                 round(2 * B_c * (K_u + K_c) * N / (ms * 1e-3) / 1e12, 3),
             "torch_hipblaslt_decomposed_ms": round(ms_torch, 5),
             "max_abs_err_sampled": float(np.abs(got - ref).max()),
+            "max_abs_err_sampled_at": {"candidate": int(rows[np.unravel_index(
+                int(np.argmax(np.abs(got - ref))), got.shape)[0]]),
+                "col": int(np.unravel_index(int(np.argmax(np.abs(got - ref))), got.shape)[1])},
             "config": dict(wl.meta)}
 
 
@@ -396,15 +502,20 @@ def linear_main(args) -> None:
     print(json.dumps(out))
 
 
-def linear_cpu_baseline(name: str, budget_s: float = 15.0) -> dict:
-    """The float64 oracle on random batches of candidates (replicated features, as it
-    stands), scaled to the layer's decomposed FLOPs per candidate."""
+def linear_cpu_baseline(name: str, budget_s: float = 10.0) -> dict:
+    """The float64 oracle, as it stands (replicated features), on random batches of 256
+    candidates, one batch per thread of this job's share of the host cores (BLAS inside
+    each call single-threaded), submitted until `budget_s` of wall time is spent; scaled
+    to the layer's decomposed FLOPs per candidate, the unit the GPU is credited in."""
+    import concurrent.futures as cf
+    import contextlib
     import oracle
     try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+        from threadpoolctl import threadpool_limits
+        blas_one = threadpool_limits(1)
     except Exception:
-        cores = os.cpu_count() or 1
+        blas_one = contextlib.nullcontext()
+    threads, aff = oracle_threads()
     wl = ai.make_linear_workload(name, seed=0)
     B_u, K_u = wl.x_user.shape
     B_c, K_c = wl.x_cand.shape
@@ -412,18 +523,28 @@ def linear_cpu_baseline(name: str, budget_s: float = 15.0) -> dict:
     xuf, _, wf, bf = wl.f64()
     per_cand = 2 * (B_u * K_u + B_c * K_c) * N / B_c
     rng = np.random.default_rng(123)
-    done, t_total = 0, 0.0
-    while t_total < budget_s and done < B_c:
-        rows = np.sort(rng.choice(B_c, size=256, replace=False))
-        xcf = ai.to_f64(wl.x_cand[rows], "bf16")
-        t0 = time.perf_counter()
-        oracle.ikbo_linear(xuf, xcf, wf, wl.cand2user[rows], bf)
-        t_total += time.perf_counter() - t0
-        done += len(rows)
-    return {"value": per_cand * done / t_total / 1e12, "unit": "TFLOP/s", "cores": int(cores),
-            "kind": "oracle",
-            "sample": f"{done} random candidates in batches of 256 ({t_total:.1f} s), scaled to "
-                      f"the layer's {per_cand:.4g} decomposed FLOPs per candidate"}
+
+    def batch(rows):
+        oracle.ikbo_linear(xuf, ai.to_f64(wl.x_cand[rows], "bf16"), wf, wl.cand2user[rows], bf)
+        return len(rows)
+
+    done = 0
+    t0 = time.perf_counter()
+    with blas_one, cf.ThreadPoolExecutor(threads) as ex:
+        pending = set()
+        while True:
+            while len(pending) < threads and time.perf_counter() - t0 < budget_s:
+                pending.add(ex.submit(batch, np.sort(rng.choice(B_c, size=256, replace=False))))
+            if not pending:
+                break
+            finished, pending = cf.wait(pending, return_when=cf.FIRST_COMPLETED)
+            done += sum(f.result() for f in finished)
+    wall = time.perf_counter() - t0
+    return {"value": per_cand * done / wall / 1e12, "unit": "TFLOP/s", "cores": threads,
+            "affinity_cores": aff, "kind": "oracle", "full": False, "seconds": round(wall, 2),
+            "sample": f"sampled: {done} random candidates of {B_c} in batches of 256 "
+                      f"({wall:.1f} s), scaled to the layer's {per_cand:.4g} decomposed "
+                      f"FLOPs per candidate"}
 
 
 def ceiling(reps: int = 3) -> dict:
@@ -518,6 +639,8 @@ def main():
                     choices=sorted(ai.WORKLOADS) + sorted(ai.LINEAR_WORKLOADS))
     ap.add_argument("--no-variants", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-ceiling", action="store_true",
+                    help="skip the ceiling microbenchmarks (and the measured-peak fractions)")
     ap.add_argument("--ceiling-only", action="store_true",
                     help="only run the ceiling microbenchmarks and print their JSON")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -553,12 +676,29 @@ def main():
     w = ai.make_workload(args.workload, seed=0)
     run = Runner(w)
     ms = time_steps(run, args.steps, args.warmup)
+    ms_cold = time_cold(run)
     flops = algorithmic_flops(w)
     nbytes = algorithmic_bytes(w)
     tflops = flops / (ms * 1e-3) / 1e12
+    tf_cold = flops / (ms_cold * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.dtype]
-    err = sampled_error(run)
+    err, err_at = sampled_error(run)
     traffic = traffic_for(args.workload)
+    del run
+    torch.cuda.empty_cache()
+    ceil = None if args.no_ceiling else ceiling()
+    measured = None if ceil is None else ceil["mfma_bf16_normal_operands"]["TFLOP/s"]
+    roofline = {"bound": "mfma", "achieved": round(tflops, 3), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(tflops / peak, 4), "traffic": traffic,
+                "achieved_cold": round(tf_cold, 3), "frac_cold": round(tf_cold / peak, 4),
+                "algorithmic_flops_per_launch": flops, "algorithmic_bytes_per_launch": nbytes}
+    if measured and w.dtype == "bf16":
+        roofline.update({
+            "measured_peak": measured,
+            "measured_peak_source": "ceiling.mfma_bf16_normal_operands: v_mfma_f32_32x32x16_bf16 "
+                                    "from registers, N(0,1) operands, this GPU, this run",
+            "frac_of_measured_peak": round(tflops / measured, 4),
+            "frac_cold_of_measured_peak": round(tf_cold / measured, 4)})
     out = {
         "metric": METRIC,
         "value": round(tflops, 3),
@@ -574,15 +714,15 @@ def main():
         "data": "synthetic (seeded N(0,1), Philox streams)",
         "config": {"workload": args.workload, **{k: v for k, v in w.meta.items() if k != "kind"},
                    "causal": w.causal},
-        "roofline": {"bound": "mfma", "achieved": round(tflops, 3), "peak": peak,
-                     "unit": "TFLOP/s", "frac": round(tflops / peak, 4), "traffic": traffic,
-                     "algorithmic_flops_per_launch": flops,
-                     "algorithmic_bytes_per_launch": nbytes},
+        "roofline": roofline,
         "max_abs_err_sampled": err,
-        "cold_ms_per_step": round(time_cold(run), 5),
+        "max_abs_err_sampled_at": err_at,
+        "cold_ms_per_step": round(ms_cold, 5),
     }
+    if ceil is not None:
+        out["ceiling"] = ceil
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w)
+        out["cpu_baseline"] = cpu_baseline(w, args.workload in CPU_FULL)
     if not args.no_variants:
         variants = {}
         for name in sorted(ai.WORKLOADS):
@@ -591,22 +731,34 @@ def main():
             wv = ai.make_workload(name, seed=0)
             rv = Runner(wv)
             msv = time_steps(rv, max(5, args.steps // 2), 3)
+            msc = time_cold(rv, 5)
             fv, bv = algorithmic_flops(wv), algorithmic_bytes(wv)
             tv = fv / (msv * 1e-3) / 1e12
-            ent = {"ms_per_step": round(msv, 5), "cold_ms_per_step": round(time_cold(rv, 5), 5),
+            ev, ev_at = sampled_error(rv)
+            ent = {"ms_per_step": round(msv, 5), "cold_ms_per_step": round(msc, 5),
                    "TFLOP/s": round(tv, 3),
-                   "frac_of_peak": round(tv / PEAK_TFLOPS[wv.dtype], 4), "dtype": wv.dtype,
-                   "GB/s": round(bv / (msv * 1e-3) / 1e9, 1),
-                   "max_abs_err_sampled": sampled_error(rv)}
+                   "frac_of_peak": round(tv / PEAK_TFLOPS[wv.dtype], 4),
+                   "frac_cold_of_peak": round(fv / (msc * 1e-3) / 1e12 / PEAK_TFLOPS[wv.dtype], 4),
+                   "dtype": wv.dtype, "GB/s": round(bv / (msv * 1e-3) / 1e9, 1),
+                   "max_abs_err_sampled": ev, "max_abs_err_sampled_at": ev_at}
+            if measured and wv.dtype == "bf16":
+                ent["frac_of_measured_peak"] = round(tv / measured, 4)
             if wv.cand2user is not None:
                 ent["GB/s_frac_of_hbm"] = round(ent["GB/s"] / PEAK_HBM_GBS, 4)
                 rep = 2 * wv.q.size * 2 + 2 * wv.cand2user.size * wv.k[0].size * 2
                 ent["replication_equivalent_GB/s"] = round(rep / (msv * 1e-3) / 1e9, 1)
-            variants[name] = ent
             del rv
             torch.cuda.empty_cache()
+            if not args.no_cpu_baseline:
+                ent["cpu_baseline"] = cpu_baseline(wv, name in CPU_FULL, budget_s=5.0)
+            variants[name] = ent
         for name in sorted(ai.LINEAR_WORKLOADS):
-            variants[name] = linear_variant(name, max(5, args.steps // 2))
+            ent = linear_variant(name, max(5, args.steps // 2))
+            if measured:
+                ent["frac_of_measured_peak"] = round(ent["TFLOP/s"] / measured, 4)
+            if not args.no_cpu_baseline:
+                ent["cpu_baseline"] = linear_cpu_baseline(name, budget_s=5.0)
+            variants[name] = ent
             torch.cuda.empty_cache()
         out["variants"] = variants
     print(json.dumps(out))
