@@ -64,9 +64,11 @@ typedef enum {
                              bf16 with (Lk + 64) * d * 2 > 2^31 - 1 bytes per K/V head
                              (jagged: (max_Lk + 64) * Hkv * d * 2) */
   ATTN_EUNSUPPORTED = -2, /* head dim d not in {64, 128}, or unknown dtype */
-  ATTN_ELAUNCH = -3       /* the HIP launch reported an error. An error left pending by an
+  ATTN_ELAUNCH = -3,      /* the HIP launch reported an error. An error left pending by an
                              earlier HIP call on the calling thread is cleared before each
                              launch, so this status is about this call's launches only */
+  ATTN_ESCRATCH = -4      /* attn_fwd_qknorm_noalloc: the normalised keys would not fit in
+                             its fixed workspace (B * Hkv * Lk * d * 2 > 32 MiB) */
 } attn_status;
 
 typedef enum { ATTN_F32 = 0, ATTN_BF16 = 1 } attn_dtype;
@@ -182,6 +184,31 @@ int attn_fwd_qknorm(const void* q, const void* k, const void* v, void* o,
                     int causal, const int32_t* kv_len, float scale, int dtype, void* stream);
 
 /*
+ * attn_fwd_qknorm without a caller workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation). The same arguments, results and checks
+ * as attn_fwd_qknorm, minus k_norm: the normalised keys go to a 32 MiB array
+ * the library defines in device memory, one per GPU, held from the first use
+ * on that GPU until the process ends. The call allocates nothing (no
+ * hipMalloc, hipFree or allocating library routine); its first call on a
+ * device looks the array up with hipGetSymbolAddress (ATTN_ELAUNCH if that
+ * fails).
+ * Limit: B * Hkv * Lk * d * 2 <= 32 MiB (the GQA workload B=1, Hkv=8,
+ * Lk=16384, d=128 fits exactly); larger problems return ATTN_ESCRATCH after
+ * every other check and before any HIP call.
+ * Concurrency: all calls on one GPU share that array. Calls whose work can
+ * overlap on one GPU (two host threads, or two streams not ordered against
+ * each other) race on it and give wrong results: serialise them, e.g. on one
+ * stream. Every call writes the keys it reads first, so nothing needs
+ * clearing between calls.
+ */
+int attn_fwd_qknorm_noalloc(const void* q, const void* k, const void* v, void* o,
+                            const float* gamma_q, const float* gamma_k, float eps,
+                            int B, int H, int Hkv, int Lq, int Lk, int d,
+                            int causal, const int32_t* kv_len, float scale, int dtype,
+                            void* stream);
+
+/*
  * In-kernel broadcast linear layer: one linear layer over the concatenated
  * features [x_user[cand2user[c]], x_cand[c]] of every candidate c, computed
  * without replicating the user features. "How We Built TLX" (Chinese
@@ -219,7 +246,7 @@ int ikbo_linear(const void* x_user, const void* x_cand, const void* w, const flo
 const char* attn_strerror(int status);
 
 /* ABI version: major * 100 + minor (101: attn_fwd_jagged; 102: attn_fwd_block_sparse;
- * 103: ikbo_linear; 104: attn_fwd_qknorm). */
+ * 103: ikbo_linear; 104: attn_fwd_qknorm; 105: attn_fwd_qknorm_noalloc). */
 int attn_version(void);
 
 #ifdef __cplusplus

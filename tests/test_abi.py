@@ -45,7 +45,8 @@ def lib():
 
 def test_header_declares_the_entry_points():
     assert declared_functions(HEADER) == ["attn_fwd", "attn_fwd_bcast", "attn_fwd_block_sparse",
-                                          "attn_fwd_jagged", "attn_fwd_qknorm", "attn_strerror",
+                                          "attn_fwd_jagged", "attn_fwd_qknorm",
+                                          "attn_fwd_qknorm_noalloc", "attn_strerror",
                                           "attn_version", "ikbo_linear"]
     assert declared_functions(os.path.join(INCLUDE, "attn_ceiling.h")) == [
         "attn_ceiling_copy", "attn_ceiling_exp2", "attn_ceiling_fma", "attn_ceiling_lds_read",
@@ -55,11 +56,11 @@ def test_header_declares_the_entry_points():
 def test_library_exports_every_declared_symbol(lib):
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert lib.attn_version() == 104
+    assert lib.attn_version() == 105
 
 
 def test_strerror_covers_every_status(lib):
-    for code in (0, -1, -2, -3):
+    for code in (0, -1, -2, -3, -4):
         assert taa.attn_strerror(code) not in ("", "unknown status")
     assert taa.attn_strerror(12345) == "unknown status"
 
@@ -242,3 +243,18 @@ def test_ceiling_probe_argument_checks(lib):
     assert lib.attn_ceiling_copy(FAKE, FAKE, 17, None) == -1                 # not 16-byte units
     assert lib.attn_ceiling_copy(MISALIGNED, FAKE, 16, None) == -1
     assert lib.attn_ceiling_copy(FAKE, FAKE, 0, None) == 0
+
+
+def test_qknorm_noalloc_checks_before_any_hip_call(lib):
+    """The allocation-free q/k-norm call runs attn_fwd_qknorm's argument checks, then its
+    workspace limit, before any HIP call."""
+    f = lib.attn_fwd_qknorm_noalloc
+    args = lambda B=1, H=2, Hkv=2, Lq=16, Lk=16, d=128, dtype=taa.ATTN_BF16, eps=1e-6: (  # noqa
+        FAKE, FAKE, FAKE, FAKE, None, None, eps, B, H, Hkv, Lq, Lk, d, 0, None, 0.0, dtype, None)
+    assert f(*args(dtype=taa.ATTN_F32)) == taa.ATTN_EUNSUPPORTED
+    assert f(*args(d=96)) == taa.ATTN_EUNSUPPORTED
+    assert f(*args(eps=-1.0)) == taa.ATTN_EINVAL
+    assert f(*args(H=3)) == taa.ATTN_EINVAL                     # H % Hkv != 0
+    assert f(*args(B=2, H=8, Hkv=8, Lk=16384)) == taa.ATTN_ESCRATCH   # 64 MiB of keys
+    assert f(*args(B=0)) == taa.ATTN_OK                         # empty: nothing to launch
+    assert taa.attn_strerror(taa.ATTN_ESCRATCH) not in ("", "unknown status")

@@ -18,7 +18,7 @@ import os
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libattn.so")
 
-ATTN_OK, ATTN_EINVAL, ATTN_EUNSUPPORTED, ATTN_ELAUNCH = 0, -1, -2, -3
+ATTN_OK, ATTN_EINVAL, ATTN_EUNSUPPORTED, ATTN_ELAUNCH, ATTN_ESCRATCH = 0, -1, -2, -3, -4
 ATTN_F32, ATTN_BF16 = 0, 1
 
 _lib = None
@@ -60,6 +60,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.attn_fwd_qknorm.argtypes = [vp, vp, vp, vp, vp, vp, f32, vp, i32, i32, i32, i32, i32,
                                     i32, i32, vp, f32, i32, vp]
     lib.attn_fwd_qknorm.restype = i32
+    lib.attn_fwd_qknorm_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, f32, i32, i32, i32, i32,
+                                            i32, i32, i32, vp, f32, i32, vp]
+    lib.attn_fwd_qknorm_noalloc.restype = i32
     lib.ikbo_linear.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp]
     lib.ikbo_linear.restype = i32
     lib.attn_strerror.argtypes = [i32]
@@ -287,6 +290,31 @@ def attn_fwd_qknorm(q, k, v, gamma_q=None, gamma_k=None, eps=1e-6, o=None, k_nor
                                float(eps), _ptr(k_norm), B, H, k.shape[1], Lq, k.shape[2], d,
                                int(bool(causal)), _ptr(kv_len), float(scale), _dtype_code(q),
                                _stream(stream)))
+    return o
+
+
+def attn_fwd_qknorm_noalloc(q, k, v, gamma_q=None, gamma_k=None, eps=1e-6, o=None, *,
+                            causal=False, kv_len=None, scale=0.0, stream=None):
+    """attn_fwd_qknorm with the normalised keys in the library's own device workspace
+    (32 MiB per GPU; no device memory is allocated by the library). Calls whose work
+    overlaps on one GPU share that workspace and must be serialised. Returns o (allocated
+    on `stream` when None: pass o for a call that allocates nothing at all)."""
+    import torch
+    lib = load_library()
+    o = _prep(q, k, v, o, {"kv_len": kv_len}, stream)
+    B, H, Lq, d = q.shape
+    if k.shape[0] != B:
+        raise ValueError("k/v batch must equal q batch")
+    if kv_len is not None and kv_len.numel() != B:
+        raise ValueError("kv_len must have one entry per batch element")
+    for name, g in (("gamma_q", gamma_q), ("gamma_k", gamma_k)):
+        if g is not None and (g.dtype != torch.float32 or not g.is_cuda or not g.is_contiguous()
+                              or g.numel() != d):
+            raise ValueError(f"{name} must be a contiguous float32 device tensor with d entries")
+    _check(lib.attn_fwd_qknorm_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(gamma_q),
+                                       _ptr(gamma_k), float(eps), B, H, k.shape[1], Lq,
+                                       k.shape[2], d, int(bool(causal)), _ptr(kv_len),
+                                       float(scale), _dtype_code(q), _stream(stream)))
     return o
 
 

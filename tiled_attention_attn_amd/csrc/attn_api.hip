@@ -5,6 +5,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "../../include/attn.h"
 #include "attn_params.h"
 #include "gemm_params.h"
@@ -18,9 +20,33 @@ hipError_t launch_f32(const Params& p, int D, bool causal, hipStream_t stream);
 bool plan_bf16(Params& p, int D, bool causal);
 }  // namespace attn
 
+// Workspace of the allocation-free entry point: the normalised keys of one
+// call, in a file-scope device array each GPU holds from module load until
+// the process ends. Host code never uses this name as an address: the
+// address is looked up per device (scratch_ptr) and passed to the kernels.
+constexpr int64_t kScratchBytes = (int64_t)32 << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
 namespace {
 
 constexpr int kF32Rows = 64;
+constexpr int kMaxDevices = 64;
+
+// Device address of `scratch` on the current device: looked up once per device
+// (with that device current) and kept. nullptr if the lookup fails.
+void* scratch_ptr() {
+  static std::mutex mu;
+  static void* ptrs[kMaxDevices] = {};
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  if (ptrs[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    ptrs[dev] = p;
+  }
+  return ptrs[dev];
+}
 
 bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15u) == 0; }
 
@@ -90,6 +116,30 @@ int check_and_launch(const void* q, const void* k, const void* v, void* o,
   return err == hipSuccess ? ATTN_OK : ATTN_ELAUNCH;
 }
 
+// Attention on RMS-normalised queries and keys (attn_fwd_qknorm). check_only:
+// run every argument check and return, launching nothing.
+int qknorm(const void* q, const void* k, const void* v, void* o, const float* gamma_q,
+           const float* gamma_k, float eps, void* k_norm, int B, int H, int Hkv, int Lq, int Lk,
+           int d, int causal, const int32_t* kv_len, float scale, int dtype, void* stream,
+           bool check_only) {
+  if (dtype != ATTN_BF16) return ATTN_EUNSUPPORTED;
+  if (d != 64 && d != 128) return ATTN_EUNSUPPORTED;
+  if (!isfinite(eps) || eps < 0.f) return ATTN_EINVAL;
+  if (!aligned16(gamma_q) || !aligned16(gamma_k) || !aligned16(k_norm)) return ATTN_EINVAL;
+  const bool keys = B > 0 && H > 0 && Lq > 0 && Lk > 0;   // keys to normalise
+  if (keys && (k_norm == nullptr || k == nullptr || k_norm == k)) return ATTN_EINVAL;
+  // Every other check (shared with attn_fwd) runs before the first launch.
+  const int pre = check_and_launch(q, k_norm, v, o, nullptr, B, B, H, Hkv, Lq, Lk, d, causal,
+                                   kv_len, scale, dtype, nullptr, nullptr, nullptr, nullptr, 0, 0,
+                                   gamma_q, 1, eps, /*check_only=*/true);
+  if (pre != ATTN_OK || check_only) return pre;
+  if (keys && attn::launch_rmsnorm_rows(k, k_norm, gamma_k, eps, (int64_t)B * Hkv * Lk, d,
+                                        (hipStream_t)stream) != hipSuccess)
+    return ATTN_ELAUNCH;
+  return check_and_launch(q, k_norm, v, o, nullptr, B, B, H, Hkv, Lq, Lk, d, causal, kv_len,
+                          scale, dtype, stream, nullptr, nullptr, nullptr, 0, 0, gamma_q, 1, eps);
+}
+
 }  // namespace
 
 extern "C" {
@@ -141,22 +191,29 @@ int attn_fwd_qknorm(const void* q, const void* k, const void* v, void* o, const 
                     const float* gamma_k, float eps, void* k_norm, int B, int H, int Hkv, int Lq,
                     int Lk, int d, int causal, const int32_t* kv_len, float scale, int dtype,
                     void* stream) {
-  if (dtype != ATTN_BF16) return ATTN_EUNSUPPORTED;
-  if (d != 64 && d != 128) return ATTN_EUNSUPPORTED;
-  if (!isfinite(eps) || eps < 0.f) return ATTN_EINVAL;
-  if (!aligned16(gamma_q) || !aligned16(gamma_k) || !aligned16(k_norm)) return ATTN_EINVAL;
-  const bool keys = B > 0 && H > 0 && Lq > 0 && Lk > 0;   // keys to normalise
-  if (keys && (k_norm == nullptr || k == nullptr || k_norm == k)) return ATTN_EINVAL;
-  // Every other check (shared with attn_fwd) runs before the first launch.
-  const int pre = check_and_launch(q, k_norm, v, o, nullptr, B, B, H, Hkv, Lq, Lk, d, causal,
-                                   kv_len, scale, dtype, nullptr, nullptr, nullptr, nullptr, 0, 0,
-                                   gamma_q, 1, eps, /*check_only=*/true);
+  return qknorm(q, k, v, o, gamma_q, gamma_k, eps, k_norm, B, H, Hkv, Lq, Lk, d, causal, kv_len,
+                scale, dtype, stream, false);
+}
+
+int attn_fwd_qknorm_noalloc(const void* q, const void* k, const void* v, void* o,
+                            const float* gamma_q, const float* gamma_k, float eps, int B, int H,
+                            int Hkv, int Lq, int Lk, int d, int causal, const int32_t* kv_len,
+                            float scale, int dtype, void* stream) {
+  const bool keys = B > 0 && H > 0 && Lq > 0 && Lk > 0;
+  // Every argument check of attn_fwd_qknorm runs first (an aligned stand-in
+  // for the workspace, never dereferenced: check_only launches nothing), then
+  // the size limit, and only then the one HIP call that finds the array.
+  const int pre = qknorm(q, k, v, o, gamma_q, gamma_k, eps, keys ? (void*)(uintptr_t)256 : nullptr,
+                         B, H, Hkv, Lq, Lk, d, causal, kv_len, scale, dtype, stream, true);
   if (pre != ATTN_OK) return pre;
-  if (keys && attn::launch_rmsnorm_rows(k, k_norm, gamma_k, eps, (int64_t)B * Hkv * Lk, d,
-                                        (hipStream_t)stream) != hipSuccess)
-    return ATTN_ELAUNCH;
-  return check_and_launch(q, k_norm, v, o, nullptr, B, B, H, Hkv, Lq, Lk, d, causal, kv_len,
-                          scale, dtype, stream, nullptr, nullptr, nullptr, 0, 0, gamma_q, 1, eps);
+  if (!keys)   // no key to normalise: the attention pass alone (zero rows when Lk == 0)
+    return qknorm(q, k, v, o, gamma_q, gamma_k, eps, nullptr, B, H, Hkv, Lq, Lk, d, causal,
+                  kv_len, scale, dtype, stream, false);
+  if ((int64_t)B * Hkv * Lk * d * 2 > kScratchBytes) return ATTN_ESCRATCH;
+  void* ws = scratch_ptr();
+  if (ws == nullptr) return ATTN_ELAUNCH;
+  return qknorm(q, k, v, o, gamma_q, gamma_k, eps, ws, B, H, Hkv, Lq, Lk, d, causal, kv_len,
+                scale, dtype, stream, false);
 }
 
 int ikbo_linear(const void* x_user, const void* x_cand, const void* w, const float* bias,
@@ -217,10 +274,12 @@ const char* attn_strerror(int status) {
     case ATTN_EINVAL: return "invalid argument";
     case ATTN_EUNSUPPORTED: return "unsupported head dimension or dtype";
     case ATTN_ELAUNCH: return "kernel launch failed";
+    case ATTN_ESCRATCH:
+      return "problem needs more than the allocation-free entry point's 32 MiB workspace";
     default: return "unknown status";
   }
 }
 
-int attn_version(void) { return 104; }
+int attn_version(void) { return 105; }
 
 }  // extern "C"
