@@ -189,13 +189,18 @@ def test_persistent_rounds_each_tile_config(lib, tmp_path, cfg):
     """Each tile configuration forced (ATTN_GEMM_CFG, child process) on a grid with more
     tiles than slots: workgroups run several tiles, interior and edge ones, and a tile's bf16
     output is stored behind the next tile's first loads. Candidate depths K_c = 0, 40, 128,
-    200 give 0, 1, 2 and 4 stages of K (40 and 200 cut the last one). Against the oracle."""
+    200 give 0, 1, 2 and 4 stages of K (40 and 200 cut the last one); with an even count the
+    last two stages of a tile load the next tile's first two and its row indices. The 2-stage
+    case maps some candidates to users out of range (NaN rows, set in the epilogue of tiles
+    that start from prefetched operands). Against the oracle."""
     import os
     import subprocess
     import sys
     B_c, N = PERSIST_CFGS[cfg]
     ws = [ai.make_linear(50, B_c, 64, K_c, N, shuffle=True, seed=51 + i)
           for i, K_c in enumerate((0, 40, 128, 200))]
+    bad = [3, B_c // 2, B_c - 300, B_c - 1]
+    ws[2].cand2user[bad] = [-1, 50, 1 << 30, -7]
     for i, w in enumerate(ws):
         np.savez(tmp_path / f"in{i}.npz", xu=w.x_user, xc=w.x_cand, w=w.w, c2u=w.cand2user,
                  b=w.bias)

@@ -23,9 +23,11 @@
 // sets the LDS reads per MFMA (128 x 64 reads 6 fragments per 8 MFMAs). K
 // advances 64 at a time through two LDS stages filled with direct-to-LDS
 // buffer loads; LDS rows are padded by one 16-byte chunk so that operand
-// reads are free of bank conflicts. With bf16 output, a tile's results wait
-// in registers until the next tile's first loads are issued and are stored
-// behind them, so that the stores drain while that tile computes.
+// reads are free of bank conflicts. On a persistent grid the last two
+// stages of a tile load the next tile's first two, so the K loop runs on
+// across tiles. With bf16 output, a tile's results wait in registers until
+// the next tile's addend loads are issued and are stored behind them, so
+// that the stores drain while that tile computes.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <stdlib.h>
@@ -46,9 +48,6 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 #define LDS_AS __attribute__((address_space(3)))
 
-constexpr int kBK = 64;                         // K per LDS stage
-constexpr int kRowChunks = kBK / 8;             // 16-byte chunks of one row in a stage
-constexpr int kPitch = kRowChunks + 1;          // LDS row pitch in chunks (one pad)
 // Word 3 of a raw buffer descriptor (gfx9 family): 32-bit data format, no
 // swizzle; with stride 0 an access is in range iff its offset is below
 // num_records, and out-of-range loads return zero.
@@ -86,19 +85,21 @@ __device__ __forceinline__ int xcd_tile(int w, int T) {
 // All keep the accumulators in architected VGPRs.
 template <int CFG>
 struct GemmShape {
-  static constexpr int TM = CFG == 0 ? 256 : 128;
-  static constexpr int TN = CFG == 0 ? 256 : CFG == 1 ? 128 : 64;
-  static constexpr int kWavesM = 2, kWavesN = CFG == 0 ? 4 : 2;
+  static constexpr bool kBig = CFG == 0;
+  static constexpr int TM = kBig ? 256 : 128;
+  static constexpr int TN = kBig ? 256 : CFG == 1 ? 128 : 64;
+  static constexpr int kWavesM = 2, kWavesN = kBig ? 4 : 2;
   static constexpr int kWaves = kWavesM * kWavesN;
   static constexpr int MB = TM / kWavesM / 32;     // 32 x 32 blocks per wave, rows
   static constexpr int NB = TN / kWavesN / 32;     // and columns
-  static constexpr int kPerCU = CFG == 0 || CFG == 3 ? 1 : 2;
+  static constexpr int kPerCU = kBig || CFG == 3 ? 1 : 2;
   static constexpr int kStages = CFG == 3 ? 4 : 2;
+  static constexpr int BK = 64;                    // K per LDS stage
   // Workgroups per CU for the register budget: 3 runs one (its LDS allows no
   // more) but takes the budget of two, 256 registers per wave. With the whole
   // file the compiler moves the accumulators to AGPRs and copies each addend
   // load into them behind its own wait.
-  static constexpr int kRegsPerCU = CFG == 0 ? 1 : 2;
+  static constexpr int kRegsPerCU = kBig ? 1 : 2;
 };
 
 template <int CFG, bool GATHER, bool OUT_F32>
@@ -107,6 +108,11 @@ ikbo_gemm_kernel(const GemmParams p) {
   using S = GemmShape<CFG>;
   constexpr int kWaves = S::kWaves, MB = S::MB, NB = S::NB, TM = S::TM, TN = S::TN;
   constexpr int WTM = MB * 32, WTN = NB * 32;     // wave tile
+  constexpr int kBK = S::BK;                      // K per LDS stage
+  constexpr int kRowChunks = kBK / 8;             // 16-byte chunks of one row in a stage
+  constexpr int kPitch = kRowChunks + 1;          // LDS row pitch in chunks (one pad)
+  constexpr int kSub = kBK / 16;                  // MFMA k-substeps per stage
+  static_assert(kSub % 2 == 0, "substeps alternate between two fragment slots");
   constexpr int kChunksA = TM * kPitch, kChunksB = TN * kPitch;   // chunks per stage
   constexpr int kLoadsA = kChunksA / 64, kLoadsB = kChunksB / 64; // wave-wide loads
   constexpr int kPerA = (kLoadsA + kWaves - 1) / kWaves;
@@ -130,15 +136,21 @@ ikbo_gemm_kernel(const GemmParams p) {
   // gridDim.x, a multiple of 8 whenever it is below the tile count, so the
   // workgroup stays on one XCD).
   // bf16 output with two stages: a whole tile's results wait in registers
-  // (converted and lane-swapped) until the next tile's addend and first two
-  // stages of loads are issued; its stores follow them and drain under that
-  // tile's first two stages. Edge tiles (rows past M or columns past N), and
+  // (converted and lane-swapped) until the next tile's addend loads (and its
+  // first two stages', unless the previous tile loaded them) are issued; its
+  // stores follow them and drain under that tile's first two stages. Edge tiles (rows past M or columns past N), and
   // the four-stage configuration (picked for grids of one round), store at
   // once. gfx9 counts loads and stores in one counter (vmcnt) and retires
   // them in issue order, so a wave waits for a stage with a count that leaves
   // the later stores outstanding; every store is therefore issued, whatever
   // the tile.
-  constexpr int kMinLoads = kLoadsA / kWaves + kLoadsB / kWaves;  // per wave and stage
+  // When A and B each leave half the waves one load short, B's loads start
+  // half a workgroup later, so every wave issues the same number per stage
+  // and the counted waits below are exact.
+  constexpr int kRotB =
+      (kLoadsA % kWaves == kWaves / 2 && kLoadsB % kWaves == kWaves / 2) ? kWaves / 2 : 0;
+  constexpr int kMinLoads = kRotB ? (kLoadsA + kLoadsB) / kWaves   // per wave and stage
+                                  : kLoadsA / kWaves + kLoadsB / kWaves;
   constexpr int kStores = MB * NB * 2;                            // 16-byte stores per wave
   constexpr bool kPend = !OUT_F32 && S::kStages == 2;
   u32x4 pend[MB][NB][2];
@@ -163,8 +175,78 @@ ikbo_gemm_kernel(const GemmParams p) {
           __builtin_amdgcn_raw_buffer_store_b128(pend[i][j][q], crs, svoff + (j * 32 + 16 * q) * 2,
                                                  (int)((uint32_t)(i * 32) * crow), 0);
   };
+  // Row block and column tile of the tile a workgroup runs at its step wl.
+  auto coords = [&](int wl, int& m0, int& n0) __attribute__((always_inline)) {
+    const int tile = xcd_tile(wl, p.tiles);
+    int rb, cb;
+    if constexpr (CFG == 3) {
+      // Column groups of 8 tiles, row blocks inside a group: an XCD's share of
+      // the tile order then spans fewer columns of B. On the user half of the
+      // broadcast layer (16 x 16 tiles) an XCD's 32 tiles read 4 row blocks of
+      // A and 8 column tiles of B, 2 + 2 MB, instead of 1 + 4.2 MB, within its
+      // 4 MB L2.
+      constexpr int kGW = 8;
+      const int nrb = p.tiles / p.tiles_n;
+      const int grp = tile / (kGW * nrb);
+      const int gcols = min(kGW, p.tiles_n - grp * kGW);
+      const int r = tile - grp * kGW * nrb;
+      rb = r / gcols;
+      cb = grp * kGW + r % gcols;
+    } else {
+      rb = tile / p.tiles_n;
+      cb = tile % p.tiles_n;
+    }
+    m0 = rb * TM;
+    n0 = cb * TN;
+  };
+  // Buffer descriptors start at the tile's first row and end with the last
+  // valid row's K-th element: chunks of rows past M (or N) read as zero.
+  const uint32_t a_row = (uint32_t)p.lda * 2, b_row = (uint32_t)p.ldb * 2;
+  auto a_rsrc = [&](int m0) __attribute__((always_inline)) {
+    return __builtin_amdgcn_make_buffer_rsrc(
+        (void*)((const char*)p.a + (size_t)m0 * a_row), (short)0,
+        (int)((uint32_t)(p.M - m0 - 1) * a_row + (uint32_t)p.K * 2), kBufferWord3);
+  };
+  auto b_rsrc = [&](int n0) __attribute__((always_inline)) {
+    return __builtin_amdgcn_make_buffer_rsrc(
+        (void*)((const char*)p.b + (size_t)n0 * b_row), (short)0,
+        (int)((uint32_t)(p.N - n0 - 1) * b_row + (uint32_t)p.K * 2), kBufferWord3);
+  };
+  const int nst = (p.K + kBK - 1) / kBK;
+  // Persistent two-stage ring with an even number of stages: the last two
+  // steps of a tile load the next tile's first two stages into the buffers
+  // they free, so that a tile starts with its operands in LDS; its gathered
+  // row indices come with its stage 0. The LDS buffers then alternate across
+  // tiles as they do inside one.
+  const bool xpre = kPend && nst >= 2 && (nst & 1) == 0;
+  // Gathered row indices go through LDS: each wave loads the zrow entries of
+  // its own WTM rows (consecutive) into a slot of its own with direct-to-LDS
+  // loads, and reads its lanes' entries from there. Loaded one tile ahead,
+  // they then never hold up a register a tile's early code might touch.
+  constexpr int kZLoads = WTM / 64;   // 4-byte loads per wave and tile
+  static_assert(WTM % 64 == 0, "row slots are whole wave loads");
+  __shared__ int zslot[GATHER ? kWaves * WTM : 1];
+  auto load_zrow = [&](int m0t) __attribute__((always_inline)) {
+    const int r0 = m0t + wm * WTM;
+    const __amdgpu_buffer_rsrc_t zrs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(p.zrow + r0), (short)0, max(p.M - r0, 0) * 4, kBufferWord3);
+#pragma unroll
+    for (int k = 0; k < kZLoads; ++k)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          zrs, (void LDS_AS*)(zslot + wave * WTM + k * 64), 4,
+          (uint32_t)(k * 64 + (threadIdx.x & 63)) * 4, 0, 0, 0);
+  };
+  if (GATHER && (int)blockIdx.x < p.tiles) {
+    int m0f, n0f;
+    coords(blockIdx.x, m0f, n0f);
+    load_zrow(m0f);
+    wait_vm();
+  }
   for (int wl = blockIdx.x; wl < p.tiles; wl += gridDim.x) {
-  const int tile = xcd_tile(wl, p.tiles);
+  const bool first = wl == (int)blockIdx.x;
+  const bool pre = xpre && !first;                 // stages 0 and 1 already loaded
+  const bool has_next = wl + (int)gridDim.x < p.tiles;
+  const bool load_next = xpre && has_next;        // this tile loads the next one's
   // Per-lane indices are recomputed every tile (the empty asm hides that
   // they are loop-invariant): hoisted out of the tile loop they would stay
   // live across the tile boundary, where the pending output needs the room.
@@ -172,41 +254,17 @@ ikbo_gemm_kernel(const GemmParams p) {
   asm volatile("" : "+v"(tid));
   const int lane = tid & 63;
   const int half = lane >> 5, col = lane & 31;
-  int rb, cb;
-  if constexpr (CFG == 3) {
-    // Column groups of 8 tiles, row blocks inside a group: an XCD's share of
-    // the tile order then spans fewer columns of B. On the user half of the
-    // broadcast layer (16 x 16 tiles) an XCD's 32 tiles read 4 row blocks of
-    // A and 8 column tiles of B, 2 + 2 MB, instead of 1 + 4.2 MB, within its
-    // 4 MB L2.
-    constexpr int kGW = 8;
-    const int nrb = p.tiles / p.tiles_n;
-    const int grp = tile / (kGW * nrb);
-    const int gcols = min(kGW, p.tiles_n - grp * kGW);
-    const int r = tile - grp * kGW * nrb;
-    rb = r / gcols;
-    cb = grp * kGW + r % gcols;
-  } else {
-    rb = tile / p.tiles_n;
-    cb = tile % p.tiles_n;
-  }
-  const int m0 = rb * TM;
-  const int n0 = cb * TN;
-
-  // Buffer descriptors start at the tile's first row and end with the last
-  // valid row's K-th element: chunks of rows past M (or N) read as zero.
-  const uint32_t a_row = (uint32_t)p.lda * 2, b_row = (uint32_t)p.ldb * 2;
-  const __amdgpu_buffer_rsrc_t arsrc = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)((const char*)p.a + (size_t)m0 * a_row), (short)0,
-      (int)((uint32_t)(p.M - m0 - 1) * a_row + (uint32_t)p.K * 2), kBufferWord3);
-  const __amdgpu_buffer_rsrc_t brsrc = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)((const char*)p.b + (size_t)n0 * b_row), (short)0,
-      (int)((uint32_t)(p.N - n0 - 1) * b_row + (uint32_t)p.K * 2), kBufferWord3);
+  int m0, n0, m0n = 0, n0n = 0;
+  coords(wl, m0, n0);
+  if (has_next) coords(wl + (int)gridDim.x, m0n, n0n);
+  const __amdgpu_buffer_rsrc_t arsrc = a_rsrc(m0), brsrc = b_rsrc(n0);
+  const __amdgpu_buffer_rsrc_t arsrc_n = a_rsrc(m0n), brsrc_n = b_rsrc(n0n);
 
   // Wave load n fills LDS chunks 64n .. 64n+63 of a stage; chunk q holds row
   // q / kPitch, column chunk q % kPitch (chunk kRowChunks is the pad).
   // The pad chunk of every row (column chunk kRowChunks) takes the
   // out-of-range offset: it reads as zero without a memory request.
+  const int wave_b = (wave + kRotB) % kWaves;
   uint32_t aoff[kPerA], boff[kPerB];
 #pragma unroll
   for (int j = 0; j < kPerA; ++j) {
@@ -216,7 +274,7 @@ ikbo_gemm_kernel(const GemmParams p) {
   }
 #pragma unroll
   for (int j = 0; j < kPerB; ++j) {
-    const int q = (wave + j * kWaves) * 64 + lane;
+    const int q = (wave_b + j * kWaves) * 64 + lane;
     const int c = q % kPitch;
     boff[j] = c < kRowChunks ? (uint32_t)(q / kPitch) * b_row + (uint32_t)c * 16 : kOutOfRange;
   }
@@ -224,7 +282,8 @@ ikbo_gemm_kernel(const GemmParams p) {
   // chunks past K take the out-of-range offset too.
   // (Offsets are passed as plain uint32_t values: in this template an
   // array-element argument made the host pass drop the kernel's stub.)
-  auto load_stage = [&](u32x4* adst, u32x4* bdst, int s) __attribute__((always_inline)) {
+  auto load_stage_from = [&](__amdgpu_buffer_rsrc_t ars, __amdgpu_buffer_rsrc_t brs, u32x4* adst,
+                             u32x4* bdst, int s) __attribute__((always_inline)) {
     const uint32_t koff = (uint32_t)s * (kBK * 2);
     const bool ragged = p.K - s * kBK < kBK;                  // chunks past K in this stage
     const int lim = min((p.K - s * kBK) >> 3, kRowChunks);   // valid column chunks
@@ -234,56 +293,65 @@ ikbo_gemm_kernel(const GemmParams p) {
       if (j < kPerA - 1 || n < kLoadsA) {
         uint32_t o = aoff[j] + koff;   // pad lanes stay out of range
         if (ragged && (n * 64 + lane) % kPitch >= lim) o = kOutOfRange;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(arsrc, (void LDS_AS*)(adst + n * 64), 16,
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ars, (void LDS_AS*)(adst + n * 64), 16,
                                                  (uint32_t)o, 0, 0, 0);
       }
     }
 #pragma unroll
     for (int j = 0; j < kPerB; ++j) {
-      const int n = wave + j * kWaves;
+      const int n = wave_b + j * kWaves;
       if (j < kPerB - 1 || n < kLoadsB) {
         uint32_t o = boff[j] + koff;
         if (ragged && (n * 64 + lane) % kPitch >= lim) o = kOutOfRange;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(brsrc, (void LDS_AS*)(bdst + n * 64), 16,
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(brs, (void LDS_AS*)(bdst + n * 64), 16,
                                                  (uint32_t)o, 0, 0, 0);
       }
     }
+  };
+  auto load_stage = [&](u32x4* adst, u32x4* bdst, int s) __attribute__((always_inline)) {
+    load_stage_from(arsrc, brsrc, adst, bdst, s);
   };
 
   // acc[i][j]: rows m0 + wm*WTM + i*32 .. +31 (one per lane) by columns
   // n0 + wn*WTN + j*32 .. +31 (in registers): register 4g + e holds column
   // j*32 + 8g + 4*half + e of the wave's block (the MFMA output row index).
   // The accumulators start from the row's addend (row zrow[m] of Z, or the
-  // bias), so the products are summed onto it and the epilogue only stores;
-  // these loads are issued before the first stage's and land with them. An
-  // out-of-range zrow starts the row at NaN, which the sum keeps. N is a
-  // multiple of 4: each run of 4 columns is wholly inside or outside.
-  f32x16 acc[MB][NB];
-  int zr[MB];   // the row indices first, so that their loads share one wait
-#pragma unroll
-  for (int i = 0; i < MB; ++i) {
-    const int m = m0 + wm * WTM + i * 32 + col;
-    zr[i] = GATHER && m < p.M ? p.zrow[m] : 0;
+  // bias), so the products are summed onto it and the epilogue only stores.
+  // Every lane issues the same loads whatever its row and columns (rows past
+  // M and columns past N, which are never stored, read a valid row and the
+  // last run of 4 columns), so that a wave's count of memory operations is
+  // fixed. With its first stages already in LDS, a tile does not wait for
+  // these loads before it starts: each MFMA waits only for its own
+  // accumulator. A row whose zrow is out of range gets NaN in the epilogue.
+  // N is a multiple of 4: each run of 4 columns is wholly inside or outside.
+  // A tile whose first two stages the previous one loaded waits here for its
+  // stage 0: what may still be in flight is stage 1's loads (at least
+  // kMinLoads per wave), issued after them.
+  if (pre) wait_vm_n<kMinLoads>();
+  // Without that, a tile after the first loads its row indices now.
+  if (GATHER && !xpre && !first) {
+    load_zrow(m0);
+    wait_vm();
   }
+  asm volatile("" ::: "memory");   // the row-index reads stay after these waits
+  f32x16 acc[MB][NB];
+  uint32_t badm = 0;   // bit i: row block i's zrow is out of range
 #pragma unroll
   for (int i = 0; i < MB; ++i) {
-    const float* src = nullptr;
-    bool bad = false;
+    const float* src = p.bias;
     if constexpr (GATHER) {
-      bad = zr[i] < 0 || zr[i] >= p.Mz;
-      const int zr_ = zr[i];
-      src = p.z + (size_t)(bad ? 0 : zr_) * p.N;
-    } else {
-      src = p.bias;
+      const int zr = zslot[wave * WTM + i * 32 + col];
+      const bool bad = zr < 0 || zr >= p.Mz;
+      badm |= (uint32_t)bad << i;
+      src = p.z + (size_t)(bad ? 0 : zr) * p.N;
     }
 #pragma unroll
     for (int j = 0; j < NB; ++j)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int n = n0 + wn * WTN + j * 32 + 8 * g + 4 * half;
+        const int n = min(n0 + wn * WTN + j * 32 + 8 * g + 4 * half, p.N - 4);
         f32x4 v = {0.f, 0.f, 0.f, 0.f};
-        if (src != nullptr && n < p.N) v = *(const f32x4*)(src + n);
-        if (bad) v = __builtin_nanf("");
+        if (GATHER || src != nullptr) v = *(const f32x4*)(src + n);
 #pragma unroll
         for (int e = 0; e < 4; ++e) acc[i][j][4 * g + e] = v[e];
       }
@@ -333,20 +401,17 @@ ikbo_gemm_kernel(const GemmParams p) {
     }
   };
   // One stage from buffer (ab, bb) whose substep 0 is already in slot 0:
-  // substeps 0..2 here; substep 3's MFMAs are left to after the barrier.
+  // substeps 0 .. kSub-2 here, each with the next one's reads; the last
+  // substep's MFMAs (slot 1) are left to after the barrier.
   auto stage = [&](const u32x4* ab, const u32x4* bb) __attribute__((always_inline)) {
-    read(ab, bb, 1, 1);
-    mfma(0);
-    interleave();
-    read(ab, bb, 2, 0);
-    mfma(1);
-    interleave();
-    read(ab, bb, 3, 1);
-    mfma(0);
-    interleave();
+#pragma unroll
+    for (int s = 1; s < kSub; ++s) {
+      read(ab, bb, s, s & 1);
+      mfma((s - 1) & 1);
+      interleave();
+    }
   };
 
-  const int nst = (p.K + kBK - 1) / kBK;
   // Workgroup barrier without __syncthreads()'s release fence, which would
   // wait for the pending stores too. Each wave has waited (vmcnt) for its own
   // loads of the stage about to be read and waits here for its LDS reads
@@ -359,15 +424,23 @@ ikbo_gemm_kernel(const GemmParams p) {
     asm volatile("" ::: "memory");
   };
   if constexpr (S::kStages == 2) {
-    if (nst > 0) load_stage(abuf0, bbuf0, 0);
-    if (nst > 1) load_stage(abuf1, bbuf1, 1);
+    if (!pre) {
+      if (nst > 0) load_stage(abuf0, bbuf0, 0);
+      if (nst > 1) load_stage(abuf1, bbuf1, 1);
+    }
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (kPend) store_pending(col, half);   // the previous tile's, after the loads
     __builtin_amdgcn_sched_barrier(0);
     // Wait for the addend and stage 0: what may remain is stage 1's loads (at
-    // least kMinLoads per wave) and the pending stores (kStores).
+    // least kMinLoads per wave) and the pending stores (kStores). A tile whose
+    // stage 0 the previous one loaded has waited for it already.
     if constexpr (kPend) {
-      if (nst > 1) wait_vm_n<kMinLoads + kStores>(); else wait_vm_n<kStores>();
+      if (pre) {
+      } else if (nst > 1) {
+        wait_vm_n<kMinLoads + kStores>();
+      } else {
+        wait_vm_n<kStores>();
+      }
     } else {
       if (nst > 1) wait_vm_n<kMinLoads>(); else wait_vm();
     }
@@ -387,6 +460,10 @@ ikbo_gemm_kernel(const GemmParams p) {
       lds_barrier();
       __builtin_amdgcn_sched_barrier(0);
       if (t + 2 < nst) load_stage(ab, bb, t + 2);
+      else if (load_next) {
+        load_stage_from(arsrc_n, brsrc_n, ab, bb, t + 2 - nst);
+        if (GATHER && t + 2 == nst) load_zrow(m0n);   // with stage 0, before stage 1
+      }
       read(nab, nbb, 0, 0);
       mfma(1);
     };
@@ -445,6 +522,15 @@ ikbo_gemm_kernel(const GemmParams p) {
     if (t + 2 < nst) step(abuf2, bbuf2, abuf3, bbuf3, t + 2);
   }
 
+  if constexpr (GATHER) {
+#pragma unroll
+    for (int i = 0; i < MB; ++i)
+      if ((badm >> i) & 1u)
+#pragma unroll
+        for (int j = 0; j < NB; ++j)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) acc[i][j][e] = __builtin_nanf("");
+  }
   // Epilogue. fp32 output: store the accumulators (rows past M and column
   // runs past N are skipped). bf16 output: convert them into the pending
   // registers.
@@ -511,7 +597,10 @@ ikbo_gemm_kernel(const GemmParams p) {
       }
     }
   }
-  __syncthreads();   // every wave is done with the LDS stages before the next tile loads
+  // Every wave is done with the LDS stages before the next tile loads into
+  // them; stores issued above need not have completed. A next tile whose
+  // first stages are already loaded writes LDS only after its first barrier.
+  if (!load_next) lds_barrier();
   }
   if constexpr (kPend) store_pending(threadIdx.x & 31, (threadIdx.x >> 5) & 1);
 }
