@@ -154,16 +154,21 @@ constexpr int kSchedMFMA = 0x008, kSchedDSRead = 0x100;
 // s_waitcnt vmcnt(0): wait for this wave's direct-to-LDS loads.
 __device__ __forceinline__ void wait_vm() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
-// W = 4: one 4-wave workgroup per SIMD pair (two workgroups per CU), the
-// software-pipelined loop; W = 8: one 8-wave workgroup per CU, the ping-pong
+// W = 4: 4-wave workgroups (one wave per SIMD), the software-pipelined loop,
+// two per CU at d = 128 and three at d = 64, whose 43 KB of LDS allow it and
+// whose registers fit the three-per-CU budget (168 VGPRs) without spills: a
+// third wave per SIMD hides more of the softmax, which at d = 64 weighs as
+// much as the MFMA work. W = 8: one 8-wave workgroup per CU, the ping-pong
 // loop (waves w and w+4 on one SIMD).
+template <int D, int W>
+constexpr int kGroupsPerCU = W == 4 ? (D == 64 ? 3 : 2) : 1;
 // Tensor layouts of the kernel instantiations.
 constexpr int kDense = 0, kJagged = 1, kSparse = 2;
 // Most key blocks a block-sparse query block may list (LDS list size).
 constexpr int kMaxKeyBlocks = 1024;
 
 template <int D, bool CAUSAL, int W, int LAYOUT>
-__global__ __launch_bounds__(W * 64, W == 4 ? 2 : 1) void attn_fwd_bf16_kernel(const Params p) {
+__global__ __launch_bounds__(W * 64, (kGroupsPerCU<D, W>)) void attn_fwd_bf16_kernel(const Params p) {
   using TL = Tile<D, W>;
   constexpr int kWaves = W;
   constexpr int BN = TL::BN, NC = TL::NC, KB = TL::KB, DB = TL::DB, QS = TL::QS, PS = TL::PS;
