@@ -237,7 +237,10 @@ __global__ __launch_bounds__(W * 64, (kGroupsPerCU<D, W>)) void attn_fwd_bf16_ke
     return min(max(off[b + 1] - off[b], 0), cap);
   };
 
-  // Every thread can derive the task of any wave (needed for shared loop bounds).
+  // Every thread can derive the task of any wave (needed for shared loop
+  // bounds). The loads read a clamped entry whatever the batch index, so
+  // that the tasks of all waves can be computed with their loads in flight
+  // together (one round trip rather than one per wave and use).
   auto task_of = [&](int w) __attribute__((always_inline)) -> WaveTask {
     WaveTask t;
     if (p.G == 1) {
@@ -247,14 +250,15 @@ __global__ __launch_bounds__(W * 64, (kGroupsPerCU<D, W>)) void attn_fwd_bf16_ke
       t.batch = bgrp * p.G + w / p.P;
       t.row0 = (w % p.P) * kRowsPerWave;
     }
-    t.lq = p.Lq;
-    if (jagged && t.batch < p.NB) t.lq = seq_len(p.q_offsets, t.batch, p.Lq);
+    const int bc = min(t.batch, p.NB - 1);
+    t.lq = jagged ? seq_len(p.q_offsets, bc, p.Lq) : p.Lq;
     t.valid = t.batch < p.NB && t.row0 < t.lq;
     t.kvb = t.batch;
     t.bad = false;
-    if (t.valid && p.cand2user != nullptr) {
-      t.kvb = p.cand2user[t.batch];
-      t.bad = (t.kvb < 0) || (t.kvb >= p.NKV);
+    if (p.cand2user != nullptr) {
+      const int u = p.cand2user[bc];
+      t.kvb = u;
+      t.bad = t.valid && ((u < 0) || (u >= p.NKV));
     }
     return t;
   };
@@ -287,6 +291,23 @@ __global__ __launch_bounds__(W * 64, (kGroupsPerCU<D, W>)) void attn_fwd_bf16_ke
 
   const float c = p.c;
 
+  // The tasks of all waves, and the pass leads: the first wave of each
+  // distinct K/V batch among the valid ones (one pass per lead; normally
+  // exactly one).
+  WaveTask tk[kWaves];
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) tk[w] = task_of(w);
+  uint32_t leads = 0;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    bool first = tk[w].valid && !tk[w].bad;
+#pragma unroll
+    for (int v = 0; v < w; ++v)
+      first = first && !(tk[v].valid && !tk[v].bad && tk[v].kvb == tk[w].kvb);
+    leads |= (uint32_t)first << w;
+  }
+  leads = __builtin_amdgcn_readfirstlane(leads);
+
   // Per-lane byte offsets, inside a K/V tile, of the chunks this lane loads:
   // wave load n writes LDS chunks 64n .. 64n+63 (lane i -> chunk 64n + i);
   // chunk q of the padded tile is row q / pitch, column q % pitch. Pad columns
@@ -307,17 +328,14 @@ __global__ __launch_bounds__(W * 64, (kGroupsPerCU<D, W>)) void attn_fwd_bf16_ke
     voff[j] = cc < NC ? (uint32_t)(r * (kv_rs * 2) + cc * 16) : kNoLoad;
   }
 
-  // One pass per distinct K/V batch among the waves (normally exactly one).
-  for (int lead = 0; lead < kWaves; ++lead) {
-    const WaveTask lt = task_of(lead);
-    if (!lt.valid || lt.bad) continue;
-    bool seen = false;
-    for (int w = 0; w < lead; ++w) {
-      const WaveTask tw = task_of(w);
-      if (tw.valid && !tw.bad && tw.kvb == lt.kvb) seen = true;
-    }
-    if (seen) continue;
-    const int kvb = lt.kvb;
+  // One pass per distinct K/V batch among the waves.
+  for (; leads != 0; leads &= leads - 1) {
+    const int lead = __builtin_ctz(leads);
+    int kvb = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w)
+      if (w == lead) kvb = tk[w].kvb;
+    kvb = __builtin_amdgcn_readfirstlane(kvb);
 
     int nvalid = jagged ? seq_len(p.kv_offsets, kvb, p.Lk) : p.Lk;
     if (p.kv_len != nullptr) nvalid = min(max(p.kv_len[kvb], 0), p.Lk);
@@ -336,7 +354,7 @@ __global__ __launch_bounds__(W * 64, (kGroupsPerCU<D, W>)) void attn_fwd_bf16_ke
     int tpb = 1;   // tiles per key block
     if constexpr (sparse) {
       tpb = p.blk / BN;
-      const int qblk = min(task_of(0).row0 / p.blk, p.nQB - 1);
+      const int qblk = min(tk[0].row0 / p.blk, p.nQB - 1);
       const int hm = p.mask_heads == 1 ? 0 : h;
       if (wave == 0) {
         const uint8_t* mrow = p.block_mask + ((size_t)hm * p.nQB + qblk) * p.nKB;
@@ -383,8 +401,9 @@ __global__ __launch_bounds__(W * 64, (kGroupsPerCU<D, W>)) void attn_fwd_bf16_ke
     };
 
     int ntiles = 0;
+#pragma unroll
     for (int w = 0; w < kWaves; ++w) {
-      const WaveTask t = task_of(w);
+      const WaveTask& t = tk[w];
       if (t.valid && !t.bad && t.kvb == kvb) ntiles = max(ntiles, tiles_touching(keys_needed(t)));
     }
     ntiles = __builtin_amdgcn_readfirstlane(ntiles);
@@ -469,6 +488,9 @@ __global__ __launch_bounds__(W * 64, (kGroupsPerCU<D, W>)) void attn_fwd_bf16_ke
         if (ok) x = *(const u32x4*)(qrow + 16 * s + 8 * half);
         qreg[qb][s] = __builtin_bit_cast(bf16x8, x);
       }
+    }
+#pragma unroll
+    for (int qb = 0; qb < kQB; ++qb) {
       // The softmax scale c = scale * log2(e) is folded into the query
       // operands (one bf16 rounding of c * q), so the score MFMAs produce
       // base-2 logits directly. RMS normalisation of the query row is fused
