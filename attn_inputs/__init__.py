@@ -119,10 +119,11 @@ def make_dense(B, H, Hkv, Lq, Lk, d, *, dtype="bf16", causal=False, seed=0,
 
 
 def make_bcast(B_c, B_u, H, Hkv, Lq, Lk, d, *, dtype="bf16", causal=False, seed=0,
-               cand2user=None, kv_len_range=None, scale=None) -> AttnInputs:
+               cand2user=None, kv_len_range=None, scale=None, shuffle=False) -> AttnInputs:
     """Broadcast problem: B_c candidates' queries, B_u users' keys/values.
 
-    cand2user defaults to the contiguous grouping c -> c // (B_c // B_u).
+    cand2user defaults to the contiguous grouping c -> c // (B_c // B_u); shuffle=True
+    permutes that map on its own stream (candidates of one user no longer adjacent).
     """
     q = _draw((B_c, H, Lq, d), dtype, seed, STREAM_Q)
     k = _draw((B_u, Hkv, Lk, d), dtype, seed, STREAM_K)
@@ -130,6 +131,8 @@ def make_bcast(B_c, B_u, H, Hkv, Lq, Lk, d, *, dtype="bf16", causal=False, seed=
     if cand2user is None:
         per = max(1, B_c // B_u)
         cand2user = np.minimum(np.arange(B_c) // per, B_u - 1)
+        if shuffle:
+            cand2user = _gen(seed, STREAM_MAP).permutation(cand2user)
     cand2user = np.asarray(cand2user, dtype=np.int32)
     kv_len = None
     if kv_len_range is not None:
@@ -231,6 +234,10 @@ WORKLOADS = {
                                dtype="bf16", causal=True),
     "bcast_Bc1024_Bu32": dict(kind="bcast", B_c=1024, B_u=32, H=8, Hkv=8, Lq=64, Lk=1024,
                               d=128, dtype="bf16", causal=False),
+    # the same with the candidate -> user map shuffled (a user's candidates not adjacent)
+    "bcast_Bc1024_Bu32_shuffled": dict(kind="bcast", B_c=1024, B_u=32, H=8, Hkv=8, Lq=64,
+                                       Lk=1024, d=128, dtype="bf16", causal=False,
+                                       shuffle=True),
     "masked_kvlen_L4096_d64": dict(kind="dense", B=8, H=16, Hkv=16, Lq=4096, Lk=4096, d=64,
                                    dtype="bf16", causal=False, kv_len_range=(2048, 4096)),
     "gqa_causal_L16384": dict(kind="dense", B=1, H=32, Hkv=8, Lq=16384, Lk=16384, d=128,

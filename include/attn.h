@@ -106,6 +106,44 @@ int attn_fwd_bcast(const void* q, const void* k, const void* v, void* o,
                    int dtype, void* stream);
 
 /*
+ * attn_fwd_bcast with the candidates packed in a given order. For short
+ * query lengths the bf16 kernel packs several candidates into one workgroup,
+ * which shares each K/V tile read among them ("How We Built TLX", Chinese
+ * translation, "Case study 2: in-kernel broadcast optimisation for RecSys":
+ * K/V read once per user); packed candidates of different users take one
+ * pass each, with the other candidates' waves idle. Here workgroup slot s
+ * holds candidate order[s], so an order that keeps each user's candidates
+ * together (attn_bcast_group) restores one pass per workgroup for any
+ * cand2user map.
+ *   order [B_c] int32 in device memory: a permutation of 0 .. B_c-1 (not
+ *         checked; a slot whose entry is out of range computes nothing, so an
+ *         order that is not a permutation leaves rows unwritten)
+ * Everything else as attn_fwd_bcast; the result is bit-identical to it (a
+ * candidate's arithmetic does not depend on its slot). The fp32 path, which
+ * does not pack candidates, ignores the order. Status codes as attn_fwd.
+ */
+int attn_fwd_bcast_grouped(const void* q, const void* k, const void* v, void* o,
+                           const int32_t* cand2user, const int32_t* order, int B_c, int B_u,
+                           int H, int Hkv, int Lq, int Lk, int d, int causal,
+                           const int32_t* kv_len, float scale, int dtype, void* stream);
+
+/*
+ * Candidate grouping for attn_fwd_bcast_grouped: writes order[0 .. B_c-1], a
+ * permutation of the candidates in which each user's candidates form one run
+ * (users in increasing order; candidates whose user is out of [0, B_u) last,
+ * and within a run in no fixed order). A counting sort in one workgroup,
+ * enqueued on `stream`.
+ *   cand2user [B_c] int32, device memory (read)
+ *   order     [B_c] int32, device memory (written)
+ *   work      [B_u + 1] int32, device memory: workspace, overwritten; it must
+ *             not be in use by other work on the stream at the same time
+ * Returns ATTN_OK (B_c = 0: nothing is enqueued), ATTN_EINVAL (B_c < 0,
+ * B_u < 1 or B_u = INT_MAX, or a NULL pointer), ATTN_ELAUNCH.
+ */
+int attn_bcast_group(const int32_t* cand2user, int B_c, int B_u, int32_t* order, int32_t* work,
+                     void* stream);
+
+/*
  * Jagged (variable-length) attention forward: B sequences of different
  * lengths packed token by token, each attending over its own keys only.
  * The pages give this operation only as an article title ("Meta 造了个 Triton
@@ -246,7 +284,8 @@ int ikbo_linear(const void* x_user, const void* x_cand, const void* w, const flo
 const char* attn_strerror(int status);
 
 /* ABI version: major * 100 + minor (101: attn_fwd_jagged; 102: attn_fwd_block_sparse;
- * 103: ikbo_linear; 104: attn_fwd_qknorm; 105: attn_fwd_qknorm_noalloc). */
+ * 103: ikbo_linear; 104: attn_fwd_qknorm; 105: attn_fwd_qknorm_noalloc;
+ * 106: attn_fwd_bcast_grouped, attn_bcast_group). */
 int attn_version(void);
 
 #ifdef __cplusplus

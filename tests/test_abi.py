@@ -44,7 +44,8 @@ def lib():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions(HEADER) == ["attn_fwd", "attn_fwd_bcast", "attn_fwd_block_sparse",
+    assert declared_functions(HEADER) == ["attn_bcast_group", "attn_fwd", "attn_fwd_bcast",
+                                          "attn_fwd_bcast_grouped", "attn_fwd_block_sparse",
                                           "attn_fwd_jagged", "attn_fwd_qknorm",
                                           "attn_fwd_qknorm_noalloc", "attn_strerror",
                                           "attn_version", "ikbo_linear"]
@@ -56,7 +57,7 @@ def test_header_declares_the_entry_points():
 def test_library_exports_every_declared_symbol(lib):
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert lib.attn_version() == 105
+    assert lib.attn_version() == 106
 
 
 def test_strerror_covers_every_status(lib):
@@ -119,6 +120,37 @@ def test_attn_fwd_argument_checks(lib, kwargs, status):
 ])
 def test_attn_fwd_bcast_argument_checks(lib, kwargs, status):
     assert bcast(lib, **kwargs) == status
+
+
+def bcast_grouped(lib, c2u=FAKE, order=FAKE, B_c=4, B_u=2, H=2, Hkv=2, Lq=16, Lk=16, d=128,
+                  dtype=taa.ATTN_BF16):
+    return lib.attn_fwd_bcast_grouped(FAKE, FAKE, FAKE, FAKE, c2u, order, B_c, B_u, H, Hkv, Lq,
+                                      Lk, d, 0, None, 0.0, dtype, None)
+
+
+@pytest.mark.parametrize("kwargs,status", [
+    (dict(B_u=0), taa.ATTN_EINVAL),
+    (dict(c2u=None), taa.ATTN_EINVAL),
+    (dict(order=None), taa.ATTN_EINVAL),
+    (dict(d=32), taa.ATTN_EUNSUPPORTED),
+    (dict(H=4, Hkv=3), taa.ATTN_EINVAL),
+    (dict(B_c=0, c2u=None, order=None), taa.ATTN_OK),
+])
+def test_attn_fwd_bcast_grouped_argument_checks(lib, kwargs, status):
+    assert bcast_grouped(lib, **kwargs) == status
+
+
+@pytest.mark.parametrize("args,status", [
+    ((FAKE, -1, 2, FAKE, FAKE), taa.ATTN_EINVAL),
+    ((FAKE, 4, 0, FAKE, FAKE), taa.ATTN_EINVAL),
+    ((FAKE, 4, 2147483647, FAKE, FAKE), taa.ATTN_EINVAL),
+    ((None, 4, 2, FAKE, FAKE), taa.ATTN_EINVAL),
+    ((FAKE, 4, 2, None, FAKE), taa.ATTN_EINVAL),
+    ((FAKE, 4, 2, FAKE, None), taa.ATTN_EINVAL),
+    ((None, 0, 2, None, None), taa.ATTN_OK),     # nothing to group: nothing enqueued
+])
+def test_attn_bcast_group_argument_checks(lib, args, status):
+    assert lib.attn_bcast_group(*args, None) == status
 
 
 def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):

@@ -51,6 +51,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.attn_fwd_bcast.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32,
                                    vp, f32, i32, vp]
     lib.attn_fwd_bcast.restype = i32
+    lib.attn_fwd_bcast_grouped.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
+                                           i32, i32, vp, f32, i32, vp]
+    lib.attn_fwd_bcast_grouped.restype = i32
+    lib.attn_bcast_group.argtypes = [vp, i32, i32, vp, vp, vp]
+    lib.attn_bcast_group.restype = i32
     lib.attn_fwd_jagged.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
                                     f32, i32, vp]
     lib.attn_fwd_jagged.restype = i32
@@ -174,24 +179,59 @@ def attn_fwd(q, k, v, o=None, *, causal=False, kv_len=None, scale=0.0, stream=No
 
 
 def attn_fwd_bcast(q, k, v, cand2user, o=None, *, causal=False, kv_len=None, scale=0.0,
-                   stream=None):
+                   order=None, stream=None):
     """In-kernel broadcast attention: candidate c uses user cand2user[c]'s K/V.
 
     q [B_c,H,Lq,d], k/v [B_u,Hkv,Lk,d], cand2user int32 [B_c] device tensor,
     kv_len int32 [B_u] device tensor or None. Returns o [B_c,H,Lq,d].
+    order: optional int32 [B_c] device tensor, the order in which candidates are packed
+    into workgroups (a permutation, e.g. from bcast_group); calls attn_fwd_bcast_grouped.
     """
     lib = load_library()
-    o = _prep(q, k, v, o, {"cand2user": cand2user, "kv_len": kv_len}, stream)
+    o = _prep(q, k, v, o, {"cand2user": cand2user, "kv_len": kv_len, "order": order}, stream)
     B_c, H, Lq, d = q.shape
     B_u = k.shape[0]
     if cand2user.numel() != B_c:
         raise ValueError("cand2user must have one entry per candidate")
     if kv_len is not None and kv_len.numel() != B_u:
         raise ValueError("kv_len must have one entry per user")
-    _check(lib.attn_fwd_bcast(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(cand2user), B_c, B_u, H,
-                              k.shape[1], Lq, k.shape[2], d, int(bool(causal)), _ptr(kv_len),
-                              float(scale), _dtype_code(q), _stream(stream)))
+    if order is None:
+        _check(lib.attn_fwd_bcast(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(cand2user), B_c, B_u,
+                                  H, k.shape[1], Lq, k.shape[2], d, int(bool(causal)),
+                                  _ptr(kv_len), float(scale), _dtype_code(q), _stream(stream)))
+        return o
+    if order.numel() != B_c:
+        raise ValueError("order must have one entry per candidate")
+    _check(lib.attn_fwd_bcast_grouped(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(cand2user),
+                                      _ptr(order), B_c, B_u, H, k.shape[1], Lq, k.shape[2], d,
+                                      int(bool(causal)), _ptr(kv_len), float(scale),
+                                      _dtype_code(q), _stream(stream)))
     return o
+
+
+def bcast_group(cand2user, B_u, order=None, *, work=None, stream=None):
+    """A permutation of the candidates that keeps each user's candidates together (users
+    in increasing order, out-of-range users last), computed on the device
+    (attn_bcast_group). Returns order, an int32 [B_c] device tensor. work: optional
+    int32 device tensor of at least B_u + 1 entries (allocated here if None)."""
+    import torch
+    lib = load_library()
+    if cand2user.dtype != torch.int32 or not cand2user.is_cuda or not cand2user.is_contiguous():
+        raise ValueError("cand2user must be a contiguous int32 device tensor")
+    B_c = cand2user.numel()
+    if order is None:
+        order = _on(stream, lambda: torch.empty(B_c, dtype=torch.int32, device=cand2user.device))
+    elif order.numel() != B_c or order.dtype != torch.int32 or not order.is_contiguous():
+        raise ValueError("order must be a contiguous int32 device tensor with B_c entries")
+    if work is None:
+        work = _on(stream, lambda: torch.empty(int(B_u) + 1, dtype=torch.int32,
+                                               device=cand2user.device))
+    elif (work.numel() < int(B_u) + 1 or work.dtype != torch.int32 or not work.is_cuda
+          or not work.is_contiguous()):
+        raise ValueError("work must be a contiguous int32 device tensor of B_u + 1 entries")
+    _check(lib.attn_bcast_group(_ptr(cand2user), B_c, int(B_u), _ptr(order), _ptr(work),
+                                _stream(stream)))
+    return order
 
 
 def attn_fwd_jagged(q, k, v, q_offsets, kv_offsets, max_lq, max_lk, o=None, *, causal=False,

@@ -15,8 +15,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OBJDIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libattn.so")
-SOURCES = ["attn_api.hip", "attn_bf16.hip", "attn_f32.hip", "ikbo_gemm.hip", "rmsnorm.hip",
-           "ceiling.hip"]
+SOURCES = ["attn_api.hip", "attn_bf16.hip", "attn_f32.hip", "bcast_group.hip", "ikbo_gemm.hip",
+           "rmsnorm.hip", "ceiling.hip"]
 ARCH = "gfx950"
 
 # Packed fp32 VALU ops are turned off for every HIP translation unit.

@@ -17,6 +17,8 @@ hipError_t launch_rmsnorm_rows(const void* x, void* y, const float* gamma, float
                                int D, hipStream_t stream);
 hipError_t launch_bf16(const Params& p, int D, bool causal, hipStream_t stream);
 hipError_t launch_f32(const Params& p, int D, bool causal, hipStream_t stream);
+hipError_t launch_bcast_group(const int32_t* cand2user, int B_c, int B_u, int32_t* order,
+                              int32_t* work, hipStream_t stream);
 bool plan_bf16(Params& p, int D, bool causal);
 }  // namespace attn
 
@@ -57,7 +59,8 @@ int check_and_launch(const void* q, const void* k, const void* v, void* o,
                      void* stream, const int32_t* q_offsets = nullptr,
                      const int32_t* kv_offsets = nullptr, const uint8_t* block_mask = nullptr,
                      int blk = 0, int mask_heads = 0, const float* gamma_q = nullptr,
-                     int qnorm = 0, float eps = 0.f, bool check_only = false) {
+                     int qnorm = 0, float eps = 0.f, bool check_only = false,
+                     const int32_t* cand_order = nullptr) {
   if (dtype != ATTN_F32 && dtype != ATTN_BF16) return ATTN_EUNSUPPORTED;
   if (d != 64 && d != 128) return ATTN_EUNSUPPORTED;
   if (NB < 0 || NKV < 0 || H < 0 || Lq < 0 || Lk < 0 || Hkv < 1) return ATTN_EINVAL;
@@ -79,6 +82,7 @@ int check_and_launch(const void* q, const void* k, const void* v, void* o,
   p.o = o;
   p.kv_len = kv_len;
   p.cand2user = cand2user;
+  p.cand_order = cand_order;
   p.q_offsets = q_offsets;
   p.kv_offsets = kv_offsets;
   p.block_mask = block_mask;
@@ -159,6 +163,29 @@ int attn_fwd_bcast(const void* q, const void* k, const void* v, void* o,
   if (B_c > 0 && H > 0 && Lq > 0 && cand2user == nullptr) return ATTN_EINVAL;
   return check_and_launch(q, k, v, o, cand2user, B_c, B_u, H, Hkv, Lq, Lk, d, causal, kv_len,
                           scale, dtype, stream);
+}
+
+int attn_fwd_bcast_grouped(const void* q, const void* k, const void* v, void* o,
+                           const int32_t* cand2user, const int32_t* order, int B_c, int B_u,
+                           int H, int Hkv, int Lq, int Lk, int d, int causal,
+                           const int32_t* kv_len, float scale, int dtype, void* stream) {
+  if (B_c > 0 && B_u < 1) return ATTN_EINVAL;
+  if (B_c > 0 && H > 0 && Lq > 0 && (cand2user == nullptr || order == nullptr))
+    return ATTN_EINVAL;
+  return check_and_launch(q, k, v, o, cand2user, B_c, B_u, H, Hkv, Lq, Lk, d, causal, kv_len,
+                          scale, dtype, stream, nullptr, nullptr, nullptr, 0, 0, nullptr, 0,
+                          0.f, false, order);
+}
+
+int attn_bcast_group(const int32_t* cand2user, int B_c, int B_u, int32_t* order, int32_t* work,
+                     void* stream) {
+  if (B_c < 0 || B_u < 1 || B_u == 0x7fffffff) return ATTN_EINVAL;
+  if (B_c == 0) return ATTN_OK;
+  if (cand2user == nullptr || order == nullptr || work == nullptr) return ATTN_EINVAL;
+  return attn::launch_bcast_group(cand2user, B_c, B_u, order, work, (hipStream_t)stream) ==
+                 hipSuccess
+             ? ATTN_OK
+             : ATTN_ELAUNCH;
 }
 
 int attn_fwd_block_sparse(const void* q, const void* k, const void* v, void* o,
@@ -280,6 +307,6 @@ const char* attn_strerror(int status) {
   }
 }
 
-int attn_version(void) { return 105; }
+int attn_version(void) { return 106; }
 
 }  // extern "C"

@@ -250,13 +250,19 @@ __global__ __launch_bounds__(W * 64, (kGroupsPerCU<D, W>)) void attn_fwd_bf16_ke
       t.batch = bgrp * p.G + w / p.P;
       t.row0 = (w % p.P) * kRowsPerWave;
     }
+    // (broadcast with a slot order: the slot's candidate, out of range = no rows)
     const int bc = min(t.batch, p.NB - 1);
+    bool in_range = t.batch < p.NB;
+    if (p.cand_order != nullptr) {
+      t.batch = p.cand_order[bc];
+      in_range = in_range && (unsigned)t.batch < (unsigned)p.NB;
+    }
     t.lq = jagged ? seq_len(p.q_offsets, bc, p.Lq) : p.Lq;
-    t.valid = t.batch < p.NB && t.row0 < t.lq;
+    t.valid = in_range && t.row0 < t.lq;
     t.kvb = t.batch;
     t.bad = false;
     if (p.cand2user != nullptr) {
-      const int u = p.cand2user[bc];
+      const int u = p.cand2user[p.cand_order != nullptr ? (in_range ? t.batch : 0) : bc];
       t.kvb = u;
       t.bad = t.valid && ((u < 0) || (u >= p.NKV));
     }
@@ -274,7 +280,7 @@ __global__ __launch_bounds__(W * 64, (kGroupsPerCU<D, W>)) void attn_fwd_bf16_ke
   me.valid = __builtin_amdgcn_readfirstlane((int)me.valid) != 0;
   me.bad = __builtin_amdgcn_readfirstlane((int)me.bad) != 0;
   // element offset of row 0 of this wave's (sequence, head)
-  size_t q_base = ((size_t)me.batch * p.H + h) * (size_t)p.Lq * D;
+  size_t q_base = ((size_t)(me.valid ? me.batch : 0) * p.H + h) * (size_t)p.Lq * D;
   if (jagged) q_base = me.valid ? (size_t)p.q_offsets[me.batch] * q_rs + (size_t)h * D : 0;
   const __bf16* __restrict__ qg = (const __bf16*)p.q + q_base;
   __bf16* __restrict__ og = (__bf16*)p.o + q_base;

@@ -18,6 +18,7 @@ struct Params {
   void* o;                   // [NB, H, Lq, D]    (jagged: [total_q, H, D])
   const int32_t* kv_len;     // [NKV] or nullptr
   const int32_t* cand2user;  // [NB] or nullptr
+  const int32_t* cand_order; // [NB] or nullptr: the candidate each packed slot holds (broadcast)
   const int32_t* q_offsets;  // [NB + 1] or nullptr (dense layout)
   const int32_t* kv_offsets; // [NB + 1], set iff q_offsets is
   const uint8_t* block_mask; // [mask_heads, nQB, nKB] or nullptr (no block sparsity)
