@@ -22,6 +22,10 @@ launches per step, 2 FLOPs per multiply-add of the decomposed products, with
 torch's hipBLASLt products and gather on the same inputs timed beside it for
 context). A step of the q/k-normalised workload is both of its launches (key
 normalisation, then the attention pass with the query normalisation fused).
+Each variant's timed steps follow at least 100 ms of untimed GPU work, so that
+the clocks, which drop while the CPU baselines run, have ramped up again. The
+shuffled broadcast variant is also timed through the grouped path (device
+grouping of the candidates by user, then the attention with that packing).
 """
 from __future__ import annotations
 
@@ -43,6 +47,8 @@ METRIC = "attention fwd TFLOP/s (bf16) and % of MFMA peak; broadcast-path GB/s"
 HEADLINE = "gqa_causal_L16384"
 PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}   # MI355X dense MFMA / fp32 matrix peaks
 PEAK_HBM_GBS = 8000.0
+# Untimed GPU time spent before each variant's timed steps (clock ramp after CPU work).
+WARM_MS = 100.0
 KERNEL_SOURCE = os.path.join(ROOT, "tiled_attention_attn_amd", "csrc", "attn_bf16.hip")
 LINEAR_SOURCE = os.path.join(ROOT, "tiled_attention_attn_amd", "csrc", "ikbo_gemm.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
@@ -184,11 +190,23 @@ class Runner:
                                     causal=self.w.causal, kv_len=self.kv)
 
 
-def time_steps(fn, steps: int, warmup: int) -> float:
-    """Average milliseconds per step, from HIP events on the launch stream."""
+def time_steps(fn, steps: int, warmup: int, warm_ms: float = 0.0) -> float:
+    """Average milliseconds per step, from HIP events on the launch stream. After the
+    `warmup` steps, further untimed steps run until at least `warm_ms` of GPU time has
+    been spent warming up: after seconds of CPU work (the oracle baselines) the GPU
+    clocks are down, and a short timed region would otherwise start before they ramp."""
     import torch
     for _ in range(warmup):
         fn()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    done = 0.0
+    while done < warm_ms:
+        a.record()
+        for _ in range(4):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        done += a.elapsed_time(b)
     torch.cuda.synchronize()
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     start.record()
@@ -436,7 +454,7 @@ CPU_FULL = {"fp32_tiny", "dense_causal_L2048", "bcast_Bc1024_Bu32", "bcast_Bc102
             "masked_kvlen_L4096_d64"}
 
 
-def linear_variant(name: str, steps: int, warmup: int = 3) -> dict:
+def linear_variant(name: str, steps: int, warmup: int = 3, warm_ms: float = WARM_MS) -> dict:
     """Time the in-kernel broadcast linear layer on its workload (both launches: the
     user half, then the candidate half with the gathered user rows), with sampled
     rows checked against the float64 oracle."""
@@ -453,7 +471,7 @@ def linear_variant(name: str, steps: int, warmup: int = 3) -> dict:
     y = torch.empty((B_c, N), dtype=torch.bfloat16, device="cuda")
     z = torch.empty((B_u, N), dtype=torch.float32, device="cuda")
     step = lambda: taa.ikbo_linear(xu, xc, w, c2u, bias, y, z)  # noqa: E731
-    ms = time_steps(step, steps, warmup)
+    ms = time_steps(step, steps, warmup, warm_ms=warm_ms)
     ms_cold = time_cold(step)
     flops = 2 * (B_u * K_u + B_c * K_c) * N
     nbytes = (2 * (wl.x_user.size + wl.x_cand.size + wl.w.size) + 4 * N + 4 * B_c
@@ -469,7 +487,7 @@ def linear_variant(name: str, steps: int, warmup: int = 3) -> dict:
     bias_t = torch.zeros(N, device="cuda") if bias is None else bias
     ms_torch = time_steps(
         lambda: torch.mm(xc, wc_t) + (torch.mm(xu, wu_t).float() + bias_t)[c2u_l].bfloat16(),
-        max(5, steps // 2), 3)
+        max(5, steps // 2), 3, warm_ms=warm_ms)
     tf = flops / (ms * 1e-3) / 1e12
     return {"ms_per_step": round(ms, 5), "cold_ms_per_step": round(ms_cold, 5),
             "TFLOP/s": round(tf, 3),
@@ -488,7 +506,7 @@ def linear_variant(name: str, steps: int, warmup: int = 3) -> dict:
 
 def linear_main(args) -> None:
     """The linear layer as the measured workload: one JSON line, as for attention."""
-    ent = linear_variant(args.workload, args.steps, warmup=args.warmup)
+    ent = linear_variant(args.workload, args.steps, warmup=args.warmup, warm_ms=0.0)
     cfg = ent.pop("config")
     tf = ent["TFLOP/s"]
     out = {
@@ -645,7 +663,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--workload", default=HEADLINE,
                     choices=sorted(ai.WORKLOADS) + sorted(ai.LINEAR_WORKLOADS))
     ap.add_argument("--no-variants", action="store_true")
@@ -741,7 +759,7 @@ def main():
                 continue
             wv = ai.make_workload(name, seed=0)
             rv = Runner(wv)
-            msv = time_steps(rv, max(5, args.steps // 2), 3)
+            msv = time_steps(rv, max(5, args.steps // 2), 3, warm_ms=WARM_MS)
             msc = time_cold(rv, 5)
             fv, bv = algorithmic_flops(wv), algorithmic_bytes(wv)
             tv = fv / (msv * 1e-3) / 1e12
@@ -757,7 +775,7 @@ def main():
             if wv.cand2user is not None and name.endswith("_shuffled"):
                 # the same inputs through the grouped path (grouping included in each step)
                 rg = Runner(wv, grouped=True)
-                msg = time_steps(rg, max(5, args.steps // 2), 3)
+                msg = time_steps(rg, max(5, args.steps // 2), 3, warm_ms=WARM_MS)
                 eg, eg_at = sampled_error(rg)
                 ent["grouped"] = {"ms_per_step": round(msg, 5),
                                   "TFLOP/s": round(fv / (msg * 1e-3) / 1e12, 3),
