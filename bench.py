@@ -663,7 +663,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=60)
     ap.add_argument("--workload", default=HEADLINE,
                     choices=sorted(ai.WORKLOADS) + sorted(ai.LINEAR_WORKLOADS))
     ap.add_argument("--no-variants", action="store_true")
