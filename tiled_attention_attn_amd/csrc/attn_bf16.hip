@@ -442,18 +442,20 @@ __global__ __launch_bounds__(W * 64, (kGroupsPerCU<D, W>)) void attn_fwd_bf16_ke
 
     // Direct-to-LDS buffer loads of tile t. Each tile gets its own buffer
     // descriptor: the base is the tile's first row and the range is the bytes
-    // of this (batch, head)'s valid rows from there on (none for a tile past
-    // the end). A lane's only offset is its own chunk offset, so the range
-    // check is the plain per-lane one: chunks of rows past the end read as
-    // zero (those keys are masked or never read), and so do the pad lanes.
-    // (jagged: the range ends with the last row of this head, so later rows,
-    // which belong to other heads or sequences, read as zero too)
+    // of this (batch, head)'s valid rows (the first nvalid: Lk, kv_len or the
+    // sequence's length) from there on (none for a tile past the end). A
+    // lane's only offset is its own chunk offset, so the range check is the
+    // plain per-lane one: chunks of rows past the last valid one read as zero,
+    // and so do the pad lanes. Those keys are masked, and their zero V rows
+    // keep P = 0 times V at zero whatever the memory there holds (padding past
+    // kv_len may be uninitialised: 0 * NaN would poison the row). The range
+    // ends with the last valid row's own D elements, so later rows (other
+    // heads or sequences in the jagged layout) are never read either.
     // The pass's K/V base addresses and valid byte range are wave-uniform:
     // kept in scalar registers, the per-tile descriptor is scalar arithmetic
     // (a descriptor the compiler cannot prove uniform costs a loop per load).
     const uint32_t kv_bytes = __builtin_amdgcn_readfirstlane(
-        jagged ? (nvalid > 0 ? (uint32_t)(nvalid - 1) * (kv_rs * 2) + D * 2 : 0u)
-               : (uint32_t)p.Lk * (D * 2));
+        nvalid > 0 ? (uint32_t)(nvalid - 1) * (kv_rs * 2) + D * 2 : 0u);
     const uint64_t kaddr = uniform_u64((uint64_t)(uintptr_t)kg);
     const uint64_t vaddr = uniform_u64((uint64_t)(uintptr_t)vg);
     auto load_tile = [&](uint64_t base, u32x4* dst, int t, const uint32_t* off, auto per_c,

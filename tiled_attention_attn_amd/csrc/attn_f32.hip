@@ -54,8 +54,11 @@ __global__ __launch_bounds__(kF32Rows) void attn_fwd_f32_kernel(const Params p) 
   }
   int nvalid = jagged ? min(max(p.kv_offsets[b + 1] - p.kv_offsets[b], 0), p.Lk) : p.Lk;
   if (p.kv_len != nullptr) nvalid = min(max(p.kv_len[kvb], 0), p.Lk);
-  // keys that may be read: a jagged sequence must not read its neighbours
-  const int kread = jagged ? nvalid : p.Lk;
+  // keys that may be read: a jagged sequence must not read its neighbours;
+  // keys past the valid ones are masked; they are not read either (zero K and
+  // V), so that uninitialised padding past kv_len cannot reach the output
+  // through 0 * NaN
+  const int kread = nvalid;
   int nkeys = nvalid;
   if (CAUSAL) nkeys = min(nkeys, min(mt * kF32Rows + kF32Rows, lq));
   const int ntiles = (nkeys + kF32Keys - 1) / kF32Keys;
