@@ -237,42 +237,76 @@ __global__ __launch_bounds__(W * 64, (kGroupsPerCU<D, W>)) void attn_fwd_bf16_ke
     return min(max(off[b + 1] - off[b], 0), cap);
   };
 
-  // Every thread can derive the task of any wave (needed for shared loop
-  // bounds). The loads read a clamped entry whatever the batch index, so
-  // that the tasks of all waves can be computed with their loads in flight
-  // together (one round trip rather than one per wave and use).
-  auto task_of = [&](int w) __attribute__((always_inline)) -> WaveTask {
-    WaveTask t;
+  // The tasks of all waves, computed together (every thread derives every
+  // wave's task: the pass loop bounds are shared). Each level of indirection
+  // (the slot order, the jagged offsets, cand2user) loads the entries of all
+  // waves before any is used, so the chain costs one round trip per level
+  // rather than one per wave and level. Indices are clamped, so the loads stay
+  // in bounds whatever the batch index.
+  WaveTask tk[kWaves];
+  int bcl[kWaves];
+  bool in_range[kWaves];
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
     if (p.G == 1) {
-      t.batch = bgrp;
-      t.row0 = (mt * kWaves + w) * kRowsPerWave;
+      tk[w].batch = bgrp;
+      tk[w].row0 = (mt * kWaves + w) * kRowsPerWave;
     } else {
-      t.batch = bgrp * p.G + w / p.P;
-      t.row0 = (w % p.P) * kRowsPerWave;
+      tk[w].batch = bgrp * p.G + w / p.P;
+      tk[w].row0 = (w % p.P) * kRowsPerWave;
     }
-    // (broadcast with a slot order: the slot's candidate, out of range = no rows)
-    const int bc = min(t.batch, p.NB - 1);
-    bool in_range = t.batch < p.NB;
-    if (p.cand_order != nullptr) {
-      t.batch = p.cand_order[bc];
-      in_range = in_range && (unsigned)t.batch < (unsigned)p.NB;
+    bcl[w] = min(tk[w].batch, p.NB - 1);
+    in_range[w] = tk[w].batch < p.NB;
+  }
+  if (p.cand_order != nullptr) {
+    // broadcast with a slot order: the slot's candidate (out of range: no rows)
+    int cand[kWaves];
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) cand[w] = p.cand_order[bcl[w]];
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      tk[w].batch = cand[w];
+      in_range[w] = in_range[w] && (unsigned)cand[w] < (unsigned)p.NB;
     }
-    t.lq = jagged ? seq_len(p.q_offsets, bc, p.Lq) : p.Lq;
-    t.valid = in_range && t.row0 < t.lq;
-    t.kvb = t.batch;
-    t.bad = false;
-    if (p.cand2user != nullptr) {
-      const int u = p.cand2user[p.cand_order != nullptr ? (in_range ? t.batch : 0) : bc];
-      t.kvb = u;
-      t.bad = t.valid && ((u < 0) || (u >= p.NKV));
+  }
+  if constexpr (jagged) {
+    int lo[kWaves], hi[kWaves];
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      lo[w] = p.q_offsets[bcl[w]];
+      hi[w] = p.q_offsets[bcl[w] + 1];
     }
-    return t;
-  };
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) tk[w].lq = min(max(hi[w] - lo[w], 0), p.Lq);
+  } else {
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) tk[w].lq = p.Lq;
+  }
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    tk[w].valid = in_range[w] && tk[w].row0 < tk[w].lq;
+    tk[w].kvb = tk[w].batch;
+    tk[w].bad = false;
+  }
+  if (p.cand2user != nullptr) {
+    int u[kWaves];
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w)
+      u[w] = p.cand2user[p.cand_order != nullptr ? (in_range[w] ? tk[w].batch : 0) : bcl[w]];
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      tk[w].kvb = u[w];
+      tk[w].bad = tk[w].valid && ((u[w] < 0) || (u[w] >= p.NKV));
+    }
+  }
 
   // The wave's own task is wave-uniform; moving it to scalar registers lets
   // the compiler treat everything derived from it (loop bounds, buffer
   // descriptors) as uniform.
-  WaveTask me = task_of(wave);
+  WaveTask me = tk[0];
+#pragma unroll
+  for (int w = 1; w < kWaves; ++w)
+    if (wave == w) me = tk[w];
   me.batch = __builtin_amdgcn_readfirstlane(me.batch);
   me.row0 = __builtin_amdgcn_readfirstlane(me.row0);
   me.lq = __builtin_amdgcn_readfirstlane(me.lq);
@@ -297,12 +331,8 @@ __global__ __launch_bounds__(W * 64, (kGroupsPerCU<D, W>)) void attn_fwd_bf16_ke
 
   const float c = p.c;
 
-  // The tasks of all waves, and the pass leads: the first wave of each
-  // distinct K/V batch among the valid ones (one pass per lead; normally
-  // exactly one).
-  WaveTask tk[kWaves];
-#pragma unroll
-  for (int w = 0; w < kWaves; ++w) tk[w] = task_of(w);
+  // The pass leads: the first wave of each distinct K/V batch among the valid
+  // ones (one pass per lead; normally exactly one).
   uint32_t leads = 0;
 #pragma unroll
   for (int w = 0; w < kWaves; ++w) {
