@@ -22,6 +22,10 @@
  *   - kv_len != NULL: key j is allowed iff j < clamp(kv_len[kv batch], 0, Lk);
  *     it masks keys only, every query row is computed;
  *   - the two combine by AND. A row with no allowed key is written as 0.
+ * Keys are processed in tiles of 64. A masked key inside a tile that a row
+ * reads still has its zero probability multiplied by its V row, so a
+ * non-finite V value there (0 * Inf = NaN) reaches that row; tiles a row
+ * does not read, and keys at or past kv_len, never do.
  *
  * Layout. Every tensor is contiguous row-major [batch, heads, seq, d], d
  * fastest (the PyTorch SDPA layout). q/k/v/o all have the element type

@@ -86,3 +86,27 @@ def test_nan_past_user_kv_len_in_the_broadcast_variant(lib):
     ref = oracle.attention_bcast(qf, kf, vf, w.cand2user, kv_len=w.kv_len)
     assert not np.isnan(got).any()
     assert max_err(got, ref) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("L", [2000, 4200])   # 4-wave and 8-wave schedules
+def test_inf_in_v_stays_out_of_tiles_that_do_not_hold_it(lib, L):
+    """Causal: V row 100 (key tile 1) holds +Inf. Rows 0..63 need key tile 0 only, so they
+    must stay finite and match the oracle: no product of theirs may multiply that row, not
+    even by a zero probability (0 * Inf = NaN), including the 8-wave schedule's first, empty
+    PV product. (Rows 64..99 share the tile with key 100 and are masked against it; their
+    zero probabilities still multiply it, as the header documents.)"""
+    import torch
+    B, H, Hkv, d = 1, 2, 2, 128
+    w = ai.make_dense(B, H, Hkv, L, L, d, causal=True, seed=93)
+    v = w.v.copy()
+    v[:, :, 100, :] = np.uint16(0x7F80)     # bf16 +Inf
+    q, k = to_dev(w.q, "bf16"), to_dev(w.k, "bf16")
+    o = lib.attn_fwd(q, k, to_dev(v, "bf16"), causal=True)
+    torch.cuda.synchronize()
+    got = from_dev(o)[:, :, :64]
+    assert np.isfinite(got).all(), "a row whose tiles do not hold the Inf key went non-finite"
+    qf, kf, vf = w.f64()
+    rows = np.arange(64)
+    for h in range(H):
+        ref = oracle.attention_rows(qf, kf, vf, 0, h, rows, causal=True)
+        assert max_err(got[0, h], ref) <= TOL["bf16"]

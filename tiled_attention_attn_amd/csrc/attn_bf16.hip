@@ -778,7 +778,7 @@ __global__ __launch_bounds__(W * 64, (kGroupsPerCU<D, W>)) void attn_fwd_bf16_ke
     f32x16 sacc[kQB][KB];
     auto mfma_phase = [&](int t, const u32x4* kb, const u32x4* vb) __attribute__((always_inline)) {
       // One instruction stream for every tile up to my_total: at t = 0 the
-      // PV half multiplies the zeroed P by finite V data (a no-op), and at
+      // PV half multiplies the zeroed P by the zeroed V buffer (a no-op), and at
       // t = my_total the QK half computes a score tile nobody reads. A
       // branch per product costs more (registers at the join) than these
       // 32 MFMAs per pass.
@@ -839,12 +839,13 @@ __global__ __launch_bounds__(W * 64, (kGroupsPerCU<D, W>)) void attn_fwd_bf16_ke
         half_step(g_c, std::integral_constant<int, 3>{}, h + 3);
       }
     };
-    // K(0), plus V(0) in the buffer the first (empty) PV half reads, so
-    // that it multiplies the zeroed P by finite values.
+    // K(0), and zeros in the V buffer the first (empty) PV half reads: it
+    // multiplies the zeroed P by them, and V data there (0 * Inf = NaN for a
+    // key some rows never see) could change those rows.
 #pragma unroll
     for (int ps = 0; ps < PS; ++ps) pprev[0][ps] = bf16x8{};
     load_k(kbuf0, tile_of(0));
-    load_v(vbuf1, tile_of(0));
+    for (int i = tid; i < TL::VCHUNKS; i += kWaves * 64) vbuf1[i] = u32x4{0u, 0u, 0u, 0u};
     wait_vm();
     __syncthreads();
     if (grp_id == 0) run_group(std::integral_constant<int, 0>{});
