@@ -52,6 +52,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 #define LDS_AS __attribute__((address_space(3)))
@@ -68,19 +69,30 @@ struct Tile {
   static constexpr int DB = D / 32;                  // 32-wide d blocks of O^T
   static constexpr int QS = D / 16;                  // k-steps of the QK^T product
   static constexpr int PS = BN / 16;                 // k-steps of the PV product
-  // LDS row pitches in 16-byte chunks (LDS: 64 banks x 4 bytes). K is read
-  // 16 bytes per lane with consecutive lanes on consecutive rows: one pad
-  // chunk staggers the rows by 4 banks, so 16 lanes cover all 64 banks. V is
-  // read by the transposing load, where a half-wave touches 4 consecutive
-  // rows x 64 bytes: four pad chunks put those rows 64 bytes apart modulo
-  // 256. Either way every operand address is a per-lane base plus an
+  // LDS layouts (LDS: 64 banks x 4 bytes; a chunk is 16 bytes). K rows are
+  // KPITCH chunks apart: K is read 16 bytes per lane with consecutive lanes on
+  // consecutive rows, and one pad chunk staggers the rows by 4 banks, so 16
+  // lanes cover all 64 banks. V is stored in 1 KB windows of VROWS whole rows
+  // (one wave load each, reading VROWS contiguous rows of memory); inside a
+  // window the rows are split into d-blocks of 32 columns, block-major:
+  // window offset = block * VROWS * 64 + (row % VROWS) * 64 + byte. The
+  // transposing read of a half-wave touches 4 consecutive rows x 64 bytes of
+  // one block: 256 contiguous bytes, every bank once, with no pad chunks to
+  // load. Either way every operand address is a per-lane base plus an
   // immediate.
   static constexpr int KPITCH = NC + 1;
-  static constexpr int VPITCH = NC + 4;
+  static constexpr int VROWS = 64 / NC;              // V rows per 1 KB window
+  static_assert(VROWS == 4 || VROWS == 8, "a V read's 16-row step spans whole windows");
   // Buffers are whole wave loads (64 chunks); chunks past the last row land
   // in the allocation's tail and are never read.
   static constexpr int KCHUNKS = (BN * KPITCH + 63) / 64 * 64;
-  static constexpr int VCHUNKS = (BN * VPITCH + 63) / 64 * 64;
+  static constexpr int VCHUNKS = BN * NC;
+  static_assert(VCHUNKS % 64 == 0, "V tile is whole wave loads");
+  // Unused chunks after each V buffer at d = 128. Measured: with a workgroup
+  // LDS size of exactly 66 KB the two-per-CU 4-wave kernels ran the L = 2048
+  // causal workload 4-5% slower than with any of 66 KB + 32 B, 68, 70, 72,
+  // 74, 78 or 80 KB (same host, interleaved runs); the cause is not known.
+  static constexpr int VSLACK = D == 128 ? 64 : 0;
   static constexpr int KLOADS = KCHUNKS / 64;        // wave-wide loads per K tile
   static constexpr int VLOADS = VCHUNKS / 64;
   static constexpr int KPER = (KLOADS + W - 1) / W;  // loads per wave (upper bound)
@@ -153,6 +165,13 @@ constexpr int kSchedMFMA = 0x008, kSchedDSRead = 0x100;
 
 // s_waitcnt vmcnt(0): wait for this wave's direct-to-LDS loads.
 __device__ __forceinline__ void wait_vm() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// s_waitcnt vmcnt(N): wait until at most N of this wave's loads are in
+// flight (they complete in issue order).
+template <int N>
+__device__ __forceinline__ void wait_vm_n() {
+  static_assert(N >= 0 && N < 64, "vmcnt is six bits");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
 
 // W = 4: 4-wave workgroups (one wave per SIMD), the software-pipelined loop,
 // two per CU at d = 128 and three at d = 64, whose 43 KB of LDS allow it and
@@ -172,14 +191,14 @@ __global__ __launch_bounds__(W * 64, (kGroupsPerCU<D, W>)) void attn_fwd_bf16_ke
   using TL = Tile<D, W>;
   constexpr int kWaves = W;
   constexpr int BN = TL::BN, NC = TL::NC, KB = TL::KB, DB = TL::DB, QS = TL::QS, PS = TL::PS;
-  constexpr int KPITCH = TL::KPITCH, VPITCH = TL::VPITCH;
+  constexpr int KPITCH = TL::KPITCH, VROWS = TL::VROWS;
 
   // Four distinct LDS objects, so the compiler can tell that the loads in
   // flight into one buffer never alias reads of another.
   __shared__ u32x4 kbuf0[TL::KCHUNKS];
   __shared__ u32x4 kbuf1[TL::KCHUNKS];
-  __shared__ u32x4 vbuf0[TL::VCHUNKS];
-  __shared__ u32x4 vbuf1[TL::VCHUNKS];
+  __shared__ u32x4 vbuf0[TL::VCHUNKS + TL::VSLACK];
+  __shared__ u32x4 vbuf1[TL::VCHUNKS + TL::VSLACK];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -345,10 +364,13 @@ __global__ __launch_bounds__(W * 64, (kGroupsPerCU<D, W>)) void attn_fwd_bf16_ke
   leads = __builtin_amdgcn_readfirstlane(leads);
 
   // Per-lane byte offsets, inside a K/V tile, of the chunks this lane loads:
-  // wave load n writes LDS chunks 64n .. 64n+63 (lane i -> chunk 64n + i);
-  // chunk q of the padded tile is row q / pitch, column q % pitch. Pad columns
-  // get an offset past any buffer range (ranges stay below 2^31 bytes), so
-  // those lanes make no memory request. Wave w issues loads w, w+W, ...
+  // wave load n writes LDS chunks 64n .. 64n+63 (lane i -> chunk 64n + i).
+  // K: chunk q of the padded tile is row q / KPITCH, column q % KPITCH; pad
+  // columns get an offset past any buffer range (ranges stay below 2^31
+  // bytes), so those lanes make no memory request. V: load n fills window n,
+  // rows n * VROWS .. n * VROWS + VROWS - 1; lane i takes d-block
+  // i / (4 VROWS), row n * VROWS + (i / 4) % VROWS, column chunk
+  // 4 * block + i % 4. Wave w issues loads w, w+W, ...
   constexpr uint32_t kNoLoad = 0x80000000u;
   uint32_t koff[TL::KPER], voff[TL::VPER];
 #pragma unroll
@@ -360,8 +382,9 @@ __global__ __launch_bounds__(W * 64, (kGroupsPerCU<D, W>)) void attn_fwd_bf16_ke
 #pragma unroll
   for (int j = 0; j < TL::VPER; ++j) {
     const int q = (wave + j * kWaves) * 64 + lane;
-    const int r = q / VPITCH, cc = q % VPITCH;
-    voff[j] = cc < NC ? (uint32_t)(r * (kv_rs * 2) + cc * 16) : kNoLoad;
+    const int i = q % 64;
+    const int r = (q / 64) * VROWS + (i / 4) % VROWS, cc = (i / (4 * VROWS)) * 4 + i % 4;
+    voff[j] = (uint32_t)(r * (kv_rs * 2) + cc * 16);
   }
 
   // One pass per distinct K/V batch among the waves.
@@ -527,6 +550,10 @@ __global__ __launch_bounds__(W * 64, (kGroupsPerCU<D, W>)) void attn_fwd_bf16_ke
         qreg[qb][s] = __builtin_bit_cast(bf16x8, x);
       }
     }
+    // Scaling (or normalising) the queries waits for their loads; each
+    // schedule calls this after issuing its first K/V tile loads, so that the
+    // query and K/V round trips overlap.
+    auto prep_q = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int qb = 0; qb < kQB; ++qb) {
       // The softmax scale c = scale * log2(e) is folded into the query
@@ -550,15 +577,29 @@ __global__ __launch_bounds__(W * 64, (kGroupsPerCU<D, W>)) void attn_fwd_bf16_ke
           }
         ss = halves_sum(ss);
         const float r = 1.0f / sqrtf(ss * (1.0f / D) + p.eps);
+        // gamma_q (16-byte aligned) in 16-byte loads, all issued before any
+        // is used; one branch for the whole row
+        const float* __restrict__ gq = p.gamma_q;
+        f32x4 g[QS][2];
+        if (gq != nullptr) {
+#pragma unroll
+          for (int s = 0; s < QS; ++s)
+#pragma unroll
+            for (int k4 = 0; k4 < 2; ++k4) g[s][k4] = *(const f32x4*)(gq + 16 * s + 8 * half + 4 * k4);
+        } else {
+#pragma unroll
+          for (int s = 0; s < QS; ++s)
+#pragma unroll
+            for (int k4 = 0; k4 < 2; ++k4) g[s][k4] = f32x4{1.f, 1.f, 1.f, 1.f};
+        }
 #pragma unroll
         for (int s = 0; s < QS; ++s)
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float gam = p.gamma_q != nullptr ? p.gamma_q[16 * s + 8 * half + e] : 1.0f;
-            qreg[qb][s][e] = (__bf16)((float)qreg[qb][s][e] * r * (gam * c));
-          }
+          for (int e = 0; e < 8; ++e)
+            qreg[qb][s][e] = (__bf16)((float)qreg[qb][s][e] * r * (g[s][e >> 2][e & 3] * c));
       }
     }
+    };
 
     f32x16 oacc[kQB][DB];
 #pragma unroll
@@ -594,7 +635,8 @@ __global__ __launch_bounds__(W * 64, (kGroupsPerCU<D, W>)) void attn_fwd_bf16_ke
     // V^T operands come through the transposing LDS read: source role il
     // addresses V[row][dcol .. dcol+3], result lane il then holds
     // V[key0 + s][dbase + il] for s = 0..3.
-    const int vlane = (half * 4 + (il >> 2)) * (VPITCH * 16) + ((grp & 1) * 16 + 4 * (il & 3)) * 2;
+    const int vrow = half * 4 + (il >> 2);
+    const int vlane = (vrow / VROWS) * 1024 + (vrow % VROWS) * 64 + ((grp & 1) * 16 + 4 * (il & 3)) * 2;
     // Both products of one step in a single instruction stream: first
     // O += P(t-1) V(t-1), then S(t) = K(t) Q^T, so P(t-1) is dead before S(t)
     // is born. Operand reads run two MFMAs ahead through the whole stream
@@ -613,10 +655,10 @@ __global__ __launch_bounds__(W * 64, (kGroupsPerCU<D, W>)) void attn_fwd_bf16_ke
       if constexpr (PV) {
 #pragma unroll
         for (int step = 0; step < NV; ++step) {
-          const int o1 = ((step / DB) * 16) * (VPITCH * 16) + (step % DB) * 64;
+          const int o1 = ((step / DB) * 16 / VROWS) * 1024 + (step % DB) * (VROWS * 64);
           const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)(vb + o1));
           const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-              (LDS_AS bf16x4*)(vb + o1 + 8 * (VPITCH * 16)));
+              (LDS_AS bf16x4*)(vb + o1 + (8 / VROWS) * 1024));
           va[step] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
         }
 #pragma unroll
@@ -846,6 +888,7 @@ __global__ __launch_bounds__(W * 64, (kGroupsPerCU<D, W>)) void attn_fwd_bf16_ke
     for (int ps = 0; ps < PS; ++ps) pprev[0][ps] = bf16x8{};
     load_k(kbuf0, tile_of(0));
     for (int i = tid; i < TL::VCHUNKS; i += kWaves * 64) vbuf1[i] = u32x4{0u, 0u, 0u, 0u};
+    prep_q();
     wait_vm();
     __syncthreads();
     if (grp_id == 0) run_group(std::integral_constant<int, 0>{});
@@ -870,8 +913,10 @@ __global__ __launch_bounds__(W * 64, (kGroupsPerCU<D, W>)) void attn_fwd_bf16_ke
       u32x4* knext = PAR ? kbuf0 : kbuf1;
       u32x4* vprev = PAR ? vbuf0 : vbuf1;
       u32x4* vcur = PAR ? vbuf1 : vbuf0;
-      if (t + 1 < ntiles) load_k(knext, tile_of(t + 1));
-      if (t < ntiles) load_v(vcur, tile_of(t));
+      if (t > 0) {   // the prologue issued iteration 0's loads
+        if (t + 1 < ntiles) load_k(knext, tile_of(t + 1));
+        if (t < ntiles) load_v(vcur, tile_of(t));
+      }
       if constexpr (MODE != 0) {
         // Priority for the MFMA stream at d = 64 only: measured with two
         // workgroups per SIMD pair, it helps d = 64 and slows d = 128 (the
@@ -900,8 +945,17 @@ __global__ __launch_bounds__(W * 64, (kGroupsPerCU<D, W>)) void attn_fwd_bf16_ke
     using First = std::integral_constant<int, 1>;
     using Both = std::integral_constant<int, 2>;
     using Last = std::integral_constant<int, 3>;
+    // The prologue issues K(0) and iteration 0's loads, V(0) and K(1), right
+    // behind the queries', so that their round trips overlap. It waits for
+    // the queries and K(0) only: V(0) and K(1), issued last, may still be in
+    // flight (every wave issues at least VLOADS / W and KLOADS / W of them),
+    // and iteration 0 waits for them.
     load_k(kbuf0, tile_of(0));
-    wait_vm();
+    load_v(vbuf0, tile_of(0));
+    if (1 < ntiles) load_k(kbuf1, tile_of(1));
+    prep_q();
+    if (1 < ntiles) wait_vm_n<TL::VLOADS / W + TL::KLOADS / W>();
+    else wait_vm_n<TL::VLOADS / W>();
     __syncthreads();
     int t = 0;
     const int n = active ? my_total : 0;   // tiles this wave computes
