@@ -372,20 +372,22 @@ __global__ __launch_bounds__(W * 64, (kGroupsPerCU<D, W>)) void attn_fwd_bf16_ke
   // i / (4 VROWS), row n * VROWS + (i / 4) % VROWS, column chunk
   // 4 * block + i % 4. Wave w issues loads w, w+W, ...
   constexpr uint32_t kNoLoad = 0x80000000u;
+  // (Unsigned arithmetic throughout: it compiles to shifts and one
+  // multiply-high per K entry rather than signed-division fixups.)
   uint32_t koff[TL::KPER], voff[TL::VPER];
+  const uint32_t row_bytes = (uint32_t)kv_rs * 2u;
+  const uint32_t ulane = (uint32_t)lane;
 #pragma unroll
   for (int j = 0; j < TL::KPER; ++j) {
-    const int q = (wave + j * kWaves) * 64 + lane;
-    const int r = q / KPITCH, cc = q % KPITCH;
-    koff[j] = cc < NC ? (uint32_t)(r * (kv_rs * 2) + cc * 16) : kNoLoad;
+    const uint32_t q = (uint32_t)(wave + j * kWaves) * 64u + ulane;
+    const uint32_t r = q / (uint32_t)KPITCH, cc = q % (uint32_t)KPITCH;
+    koff[j] = cc < (uint32_t)NC ? r * row_bytes + cc * 16u : kNoLoad;
   }
+  const uint32_t vpart = ((ulane / 4u) % (uint32_t)VROWS) * row_bytes +
+                         ((ulane / (4u * VROWS)) * 4u + ulane % 4u) * 16u;
 #pragma unroll
-  for (int j = 0; j < TL::VPER; ++j) {
-    const int q = (wave + j * kWaves) * 64 + lane;
-    const int i = q % 64;
-    const int r = (q / 64) * VROWS + (i / 4) % VROWS, cc = (i / (4 * VROWS)) * 4 + i % 4;
-    voff[j] = (uint32_t)(r * (kv_rs * 2) + cc * 16);
-  }
+  for (int j = 0; j < TL::VPER; ++j)
+    voff[j] = (uint32_t)(wave + j * kWaves) * ((uint32_t)VROWS * row_bytes) + vpart;
 
   // One pass per distinct K/V batch among the waves.
   for (; leads != 0; leads &= leads - 1) {
