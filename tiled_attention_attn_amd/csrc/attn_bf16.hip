@@ -69,23 +69,26 @@ struct Tile {
   static constexpr int DB = D / 32;                  // 32-wide d blocks of O^T
   static constexpr int QS = D / 16;                  // k-steps of the QK^T product
   static constexpr int PS = BN / 16;                 // k-steps of the PV product
-  // LDS layouts (LDS: 64 banks x 4 bytes; a chunk is 16 bytes). K rows are
-  // KPITCH chunks apart: K is read 16 bytes per lane with consecutive lanes on
-  // consecutive rows, and one pad chunk staggers the rows by 4 banks, so 16
-  // lanes cover all 64 banks. V is stored in 1 KB windows of VROWS whole rows
-  // (one wave load each, reading VROWS contiguous rows of memory); inside a
-  // window the rows are split into d-blocks of 32 columns, block-major:
+  // LDS layouts (LDS: 64 banks x 4 bytes; a chunk is 16 bytes). Each wave
+  // load fills one 1 KB window with 64 / NC whole rows of K or V, so that it
+  // reads whole rows of memory, and neither layout has pad chunks to load.
+  // K: window w holds rows w, w + NWIN, w + 2 NWIN, ... row-major, and the
+  // windows start KWIN = 65 chunks apart: (row r, chunk c) is at chunk
+  // (r % NWIN) * KWIN + (r / NWIN) * NC + c. A K operand read has 16 lanes on
+  // 16 consecutive rows at one chunk; the one-chunk stagger of the windows
+  // (and, at d = 64, the row offset inside a window) puts them on 16
+  // distinct 16-byte bank groups. V: window n holds rows n * VROWS ..
+  // n * VROWS + VROWS - 1, split into d-blocks of 32 columns, block-major:
   // window offset = block * VROWS * 64 + (row % VROWS) * 64 + byte. The
   // transposing read of a half-wave touches 4 consecutive rows x 64 bytes of
-  // one block: 256 contiguous bytes, every bank once, with no pad chunks to
-  // load. Either way every operand address is a per-lane base plus an
-  // immediate.
-  static constexpr int KPITCH = NC + 1;
+  // one block: 256 contiguous bytes, every bank once. Either way every
+  // operand address is a per-lane base plus an immediate.
+  static constexpr int NWIN = BN * NC / 64;          // K windows (= wave loads) per tile
+  static constexpr int KWIN = 65;                    // chunks between K window starts
+  static_assert(32 % NWIN == 0, "a 32-key block spans whole rounds of K windows");
   static constexpr int VROWS = 64 / NC;              // V rows per 1 KB window
   static_assert(VROWS == 4 || VROWS == 8, "a V read's 16-row step spans whole windows");
-  // Buffers are whole wave loads (64 chunks); chunks past the last row land
-  // in the allocation's tail and are never read.
-  static constexpr int KCHUNKS = (BN * KPITCH + 63) / 64 * 64;
+  static constexpr int KCHUNKS = NWIN * KWIN;
   static constexpr int VCHUNKS = BN * NC;
   static_assert(VCHUNKS % 64 == 0, "V tile is whole wave loads");
   // Unused chunks after each V buffer at d = 128. Measured: with a workgroup
@@ -93,7 +96,7 @@ struct Tile {
   // causal workload 4-5% slower than with any of 66 KB + 32 B, 68, 70, 72,
   // 74, 78 or 80 KB (same host, interleaved runs); the cause is not known.
   static constexpr int VSLACK = D == 128 ? 64 : 0;
-  static constexpr int KLOADS = KCHUNKS / 64;        // wave-wide loads per K tile
+  static constexpr int KLOADS = NWIN;                // wave-wide loads per K tile
   static constexpr int VLOADS = VCHUNKS / 64;
   static constexpr int KPER = (KLOADS + W - 1) / W;  // loads per wave (upper bound)
   static constexpr int VPER = (VLOADS + W - 1) / W;
@@ -191,7 +194,7 @@ __global__ __launch_bounds__(W * 64, (kGroupsPerCU<D, W>)) void attn_fwd_bf16_ke
   using TL = Tile<D, W>;
   constexpr int kWaves = W;
   constexpr int BN = TL::BN, NC = TL::NC, KB = TL::KB, DB = TL::DB, QS = TL::QS, PS = TL::PS;
-  constexpr int KPITCH = TL::KPITCH, VROWS = TL::VROWS;
+  constexpr int NWIN = TL::NWIN, KWIN = TL::KWIN, VROWS = TL::VROWS;
 
   // Four distinct LDS objects, so the compiler can tell that the loads in
   // flight into one buffer never alias reads of another.
@@ -363,26 +366,18 @@ __global__ __launch_bounds__(W * 64, (kGroupsPerCU<D, W>)) void attn_fwd_bf16_ke
   }
   leads = __builtin_amdgcn_readfirstlane(leads);
 
-  // Per-lane byte offsets, inside a K/V tile, of the chunks this lane loads:
-  // wave load n writes LDS chunks 64n .. 64n+63 (lane i -> chunk 64n + i).
-  // K: chunk q of the padded tile is row q / KPITCH, column q % KPITCH; pad
-  // columns get an offset past any buffer range (ranges stay below 2^31
-  // bytes), so those lanes make no memory request. V: load n fills window n,
-  // rows n * VROWS .. n * VROWS + VROWS - 1; lane i takes d-block
+  // Per-lane byte offsets, inside a K/V tile, of the chunks this lane loads
+  // (wave load n fills window n, lane i its 16-byte slot i). K: lane i takes
+  // row n + NWIN * (i / NC), column chunk i % NC. V: lane i takes d-block
   // i / (4 VROWS), row n * VROWS + (i / 4) % VROWS, column chunk
-  // 4 * block + i % 4. Wave w issues loads w, w+W, ...
-  constexpr uint32_t kNoLoad = 0x80000000u;
-  // (Unsigned arithmetic throughout: it compiles to shifts and one
-  // multiply-high per K entry rather than signed-division fixups.)
+  // 4 * block + i % 4. Wave w issues loads w, w+W, ... (Unsigned arithmetic:
+  // it compiles to shifts and adds.)
   uint32_t koff[TL::KPER], voff[TL::VPER];
   const uint32_t row_bytes = (uint32_t)kv_rs * 2u;
   const uint32_t ulane = (uint32_t)lane;
+  const uint32_t kpart = (ulane / (uint32_t)NC) * (uint32_t)NWIN * row_bytes + (ulane % (uint32_t)NC) * 16u;
 #pragma unroll
-  for (int j = 0; j < TL::KPER; ++j) {
-    const uint32_t q = (uint32_t)(wave + j * kWaves) * 64u + ulane;
-    const uint32_t r = q / (uint32_t)KPITCH, cc = q % (uint32_t)KPITCH;
-    koff[j] = cc < (uint32_t)NC ? r * row_bytes + cc * 16u : kNoLoad;
-  }
+  for (int j = 0; j < TL::KPER; ++j) koff[j] = (uint32_t)(wave + j * kWaves) * row_bytes + kpart;
   const uint32_t vpart = ((ulane / 4u) % (uint32_t)VROWS) * row_bytes +
                          ((ulane / (4u * VROWS)) * 4u + ulane % 4u) * 16u;
 #pragma unroll
@@ -500,8 +495,8 @@ __global__ __launch_bounds__(W * 64, (kGroupsPerCU<D, W>)) void attn_fwd_bf16_ke
     // of this (batch, head)'s valid rows (the first nvalid: Lk, kv_len or the
     // sequence's length) from there on (none for a tile past the end). A
     // lane's only offset is its own chunk offset, so the range check is the
-    // plain per-lane one: chunks of rows past the last valid one read as zero,
-    // and so do the pad lanes. Those keys are masked, and their zero V rows
+    // plain per-lane one: chunks of rows past the last valid one read as zero.
+    // Those keys are masked, and their zero V rows
     // keep P = 0 times V at zero whatever the memory there holds (padding past
     // kv_len may be uninitialised: 0 * NaN would poison the row). The range
     // ends with the last valid row's own D elements, so later rows (other
@@ -514,8 +509,9 @@ __global__ __launch_bounds__(W * 64, (kGroupsPerCU<D, W>)) void attn_fwd_bf16_ke
     const uint64_t kaddr = uniform_u64((uint64_t)(uintptr_t)kg);
     const uint64_t vaddr = uniform_u64((uint64_t)(uintptr_t)vg);
     auto load_tile = [&](uint64_t base, u32x4* dst, int t, const uint32_t* off, auto per_c,
-                         auto nloads_c) __attribute__((always_inline)) {
+                         auto nloads_c, auto stride_c) __attribute__((always_inline)) {
       constexpr int PER = decltype(per_c)::value, NLOADS = decltype(nloads_c)::value;
+      constexpr int STRIDE = decltype(stride_c)::value;   // chunks between windows
       const uint32_t tile_off = (uint32_t)t * (uint32_t)(BN * kv_rs * 2);
       // both below 2^31: a signed max, which has a scalar instruction (an
       // unsigned saturating subtract would go to a vector register)
@@ -526,17 +522,17 @@ __global__ __launch_bounds__(W * 64, (kGroupsPerCU<D, W>)) void attn_fwd_bf16_ke
       for (int j = 0; j < PER; ++j) {
         const int n = wave + j * kWaves;
         if (j < PER - 1 || n < NLOADS)
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (void LDS_AS*)(dst + n * 64), 16, off[j],
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (void LDS_AS*)(dst + n * STRIDE), 16, off[j],
                                                    0, 0, 0);
       }
     };
     auto load_k = [&](u32x4* dst, int t) __attribute__((always_inline)) {
       load_tile(kaddr, dst, t, koff, std::integral_constant<int, TL::KPER>{},
-                std::integral_constant<int, TL::KLOADS>{});
+                std::integral_constant<int, TL::KLOADS>{}, std::integral_constant<int, KWIN>{});
     };
     auto load_v = [&](u32x4* dst, int t) __attribute__((always_inline)) {
       load_tile(vaddr, dst, t, voff, std::integral_constant<int, TL::VPER>{},
-                std::integral_constant<int, TL::VLOADS>{});
+                std::integral_constant<int, TL::VLOADS>{}, std::integral_constant<int, 64>{});
     };
     // Q^T operands: block qb, lane holds query row0+32qb+col, d = 16*s + 8*half + 0..7.
     bf16x8 qreg[kQB][QS];
@@ -650,7 +646,7 @@ __global__ __launch_bounds__(W * 64, (kGroupsPerCU<D, W>)) void attn_fwd_bf16_ke
                     auto qk_c) __attribute__((always_inline)) {
       static_assert(kQB == 1, "one query block per wave");
       constexpr bool PV = decltype(pv_c)::value, QK = decltype(qk_c)::value;
-      const u32x4* kl = kb + col * KPITCH + half;
+      const u32x4* kl = kb + (col % NWIN) * KWIN + (col / NWIN) * NC + half;
       const LDS_AS char* vb = (const LDS_AS char*)vb32 + vlane;
       constexpr int NK = QS * KB, NV = PS * DB;
       bf16x8 ka[QS][KB], va[NV];
@@ -680,7 +676,7 @@ __global__ __launch_bounds__(W * 64, (kGroupsPerCU<D, W>)) void attn_fwd_bf16_ke
         for (int s = 0; s < QS; ++s)
 #pragma unroll
           for (int kbk = 0; kbk < KB; ++kbk)
-            ka[s][kbk] = __builtin_bit_cast(bf16x8, kl[kbk * 32 * KPITCH + 2 * s]);
+            ka[s][kbk] = __builtin_bit_cast(bf16x8, kl[kbk * (32 / NWIN) * NC + 2 * s]);
 #pragma unroll
         for (int s = 0; s < QS; ++s)
 #pragma unroll
