@@ -22,7 +22,8 @@
 // lane holds one output row and runs of 4 consecutive columns. The wave tile
 // sets the LDS reads per MFMA (128 x 64 reads 6 fragments per 8 MFMAs). K
 // advances 64 at a time through two LDS stages filled with direct-to-LDS
-// buffer loads; LDS rows are padded by one 16-byte chunk so that operand
+// buffer loads, each filling one 1 KB LDS window with 8 whole rows of the
+// stage; the windows are staggered by one 16-byte chunk so that operand
 // reads are free of bank conflicts. On a persistent grid the last two
 // stages of a tile load the next tile's first two, so the K loop runs on
 // across tiles. With bf16 output, a tile's results wait in registers until
@@ -110,14 +111,23 @@ ikbo_gemm_kernel(const GemmParams p) {
   constexpr int WTM = MB * 32, WTN = NB * 32;     // wave tile
   constexpr int kBK = S::BK;                      // K per LDS stage
   constexpr int kRowChunks = kBK / 8;             // 16-byte chunks of one row in a stage
-  constexpr int kPitch = kRowChunks + 1;          // LDS row pitch in chunks (one pad)
   constexpr int kSub = kBK / 16;                  // MFMA k-substeps per stage
   static_assert(kSub % 2 == 0, "substeps alternate between two fragment slots");
-  constexpr int kChunksA = TM * kPitch, kChunksB = TN * kPitch;   // chunks per stage
-  constexpr int kLoadsA = kChunksA / 64, kLoadsB = kChunksB / 64; // wave-wide loads
+  // Stage layout: wave load n fills window n, 1 KB holding rows n, n + NW,
+  // n + 2 NW, ... (NW = rows / 8 windows) row-major; windows start kWin = 65
+  // chunks apart. Row r, column chunk c is at chunk
+  // (r % NW) * kWin + (r / NW) * kRowChunks + c. An operand read has 16 lanes
+  // on 16 consecutive rows at one chunk: the one-chunk stagger of the windows
+  // (and the 128-byte row offset inside a window) puts them on distinct
+  // 16-byte bank groups, and every load reads whole rows with no idle lane.
+  static_assert(kRowChunks == 8, "eight rows per 1 KB window");
+  constexpr int kWin = 65;
+  constexpr int kNWA = TM / 8, kNWB = TN / 8;     // windows (= wave loads) per stage
+  static_assert(32 % kNWA == 0 && 32 % kNWB == 0, "row blocks of 32 span whole window rounds");
+  constexpr int kChunksA = kNWA * kWin, kChunksB = kNWB * kWin;   // chunks per stage
+  constexpr int kLoadsA = kNWA, kLoadsB = kNWB;                   // wave-wide loads
   constexpr int kPerA = (kLoadsA + kWaves - 1) / kWaves;
   constexpr int kPerB = (kLoadsB + kWaves - 1) / kWaves;
-  static_assert(kChunksA % 64 == 0 && kChunksB % 64 == 0, "a stage is whole wave loads");
   // Separate arrays per stage buffer: the compiler then knows that reads of
   // one buffer do not wait for direct-to-LDS loads still landing in another.
   constexpr int kRingA = S::kStages > 2 ? kChunksA : 1, kRingB = S::kStages > 2 ? kChunksB : 1;
@@ -260,24 +270,17 @@ ikbo_gemm_kernel(const GemmParams p) {
   const __amdgpu_buffer_rsrc_t arsrc = a_rsrc(m0), brsrc = b_rsrc(n0);
   const __amdgpu_buffer_rsrc_t arsrc_n = a_rsrc(m0n), brsrc_n = b_rsrc(n0n);
 
-  // Wave load n fills LDS chunks 64n .. 64n+63 of a stage; chunk q holds row
-  // q / kPitch, column chunk q % kPitch (chunk kRowChunks is the pad).
-  // The pad chunk of every row (column chunk kRowChunks) takes the
-  // out-of-range offset: it reads as zero without a memory request.
+  // Wave load n fills window n of a stage: lane i takes row n + NW * (i / 8),
+  // column chunk i % 8.
   const int wave_b = (wave + kRotB) % kWaves;
+  const uint32_t lrow = (uint32_t)lane / kRowChunks, lchunk = (uint32_t)lane % kRowChunks;
   uint32_t aoff[kPerA], boff[kPerB];
 #pragma unroll
-  for (int j = 0; j < kPerA; ++j) {
-    const int q = (wave + j * kWaves) * 64 + lane;
-    const int c = q % kPitch;
-    aoff[j] = c < kRowChunks ? (uint32_t)(q / kPitch) * a_row + (uint32_t)c * 16 : kOutOfRange;
-  }
+  for (int j = 0; j < kPerA; ++j)
+    aoff[j] = ((uint32_t)(wave + j * kWaves) + lrow * kNWA) * a_row + lchunk * 16;
 #pragma unroll
-  for (int j = 0; j < kPerB; ++j) {
-    const int q = (wave_b + j * kWaves) * 64 + lane;
-    const int c = q % kPitch;
-    boff[j] = c < kRowChunks ? (uint32_t)(q / kPitch) * b_row + (uint32_t)c * 16 : kOutOfRange;
-  }
+  for (int j = 0; j < kPerB; ++j)
+    boff[j] = ((uint32_t)(wave_b + j * kWaves) + lrow * kNWB) * b_row + lchunk * 16;
   // Stage s covers K columns 64s .. 64s+63; in a last stage cut by K, the
   // chunks past K take the out-of-range offset too.
   // (Offsets are passed as plain uint32_t values: in this template an
@@ -291,9 +294,9 @@ ikbo_gemm_kernel(const GemmParams p) {
     for (int j = 0; j < kPerA; ++j) {
       const int n = wave + j * kWaves;
       if (j < kPerA - 1 || n < kLoadsA) {
-        uint32_t o = aoff[j] + koff;   // pad lanes stay out of range
-        if (ragged && (n * 64 + lane) % kPitch >= lim) o = kOutOfRange;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(ars, (void LDS_AS*)(adst + n * 64), 16,
+        uint32_t o = aoff[j] + koff;
+        if (ragged && (int)lchunk >= lim) o = kOutOfRange;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ars, (void LDS_AS*)(adst + n * kWin), 16,
                                                  (uint32_t)o, 0, 0, 0);
       }
     }
@@ -302,8 +305,8 @@ ikbo_gemm_kernel(const GemmParams p) {
       const int n = wave_b + j * kWaves;
       if (j < kPerB - 1 || n < kLoadsB) {
         uint32_t o = boff[j] + koff;
-        if (ragged && (n * 64 + lane) % kPitch >= lim) o = kOutOfRange;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(brs, (void LDS_AS*)(bdst + n * 64), 16,
+        if (ragged && (int)lchunk >= lim) o = kOutOfRange;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(brs, (void LDS_AS*)(bdst + n * kWin), 16,
                                                  (uint32_t)o, 0, 0, 0);
       }
     }
@@ -369,14 +372,18 @@ ikbo_gemm_kernel(const GemmParams p) {
   bf16x8 av[2][MB], bv[2][NB];
   auto read = [&](const u32x4* ab, const u32x4* bb, int s, int slot)
                   __attribute__((always_inline)) {
+    // row wm*WTM + i*32 + col: window col % NW, row (wm*WTM + i*32) / NW +
+    // col / NW inside it (NW divides 32)
+    const int abase = (col % kNWA) * kWin + (col / kNWA) * kRowChunks + half;
+    const int bbase = (col % kNWB) * kWin + (col / kNWB) * kRowChunks + half;
 #pragma unroll
     for (int i = 0; i < MB; ++i)
-      av[slot][i] =
-          __builtin_bit_cast(bf16x8, ab[(wm * WTM + i * 32 + col) * kPitch + 2 * s + half]);
+      av[slot][i] = __builtin_bit_cast(
+          bf16x8, ab[abase + ((wm * WTM + i * 32) / kNWA) * kRowChunks + 2 * s]);
 #pragma unroll
     for (int j = 0; j < NB; ++j)
-      bv[slot][j] =
-          __builtin_bit_cast(bf16x8, bb[(wn * WTN + j * 32 + col) * kPitch + 2 * s + half]);
+      bv[slot][j] = __builtin_bit_cast(
+          bf16x8, bb[bbase + ((wn * WTN + j * 32) / kNWB) * kRowChunks + 2 * s]);
   };
   auto mfma = [&](int slot) __attribute__((always_inline)) {
 #pragma unroll
