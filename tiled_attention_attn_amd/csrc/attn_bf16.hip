@@ -521,7 +521,7 @@ __global__ __launch_bounds__(W * 64, (kGroupsPerCU<D, W>)) void attn_fwd_bf16_ke
 #pragma unroll
       for (int j = 0; j < PER; ++j) {
         const int n = wave + j * kWaves;
-        if (j < PER - 1 || n < NLOADS)
+        if (j < PER - 1 || NLOADS % kWaves == 0 || n < NLOADS)
           __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (void LDS_AS*)(dst + n * STRIDE), 16, off[j],
                                                    0, 0, 0);
       }
