@@ -177,7 +177,7 @@ __device__ __forceinline__ void wait_vm_n() {
 }
 
 // W = 4: 4-wave workgroups (one wave per SIMD), the software-pipelined loop,
-// two per CU at d = 128 and three at d = 64, whose 43 KB of LDS allow it and
+// two per CU at d = 128 and three at d = 64, whose 33 KB of LDS allow it and
 // whose registers fit the three-per-CU budget (168 VGPRs) without spills: a
 // third wave per SIMD hides more of the softmax, which at d = 64 weighs as
 // much as the MFMA work. W = 8: one 8-wave workgroup per CU, the ping-pong
