@@ -392,6 +392,23 @@ __global__ __launch_bounds__(W * 64, (kGroupsPerCU<D, W>)) void attn_fwd_bf16_ke
     for (int w = 0; w < kWaves; ++w)
       if (w == lead) kvb = tk[w].kvb;
     kvb = __builtin_amdgcn_readfirstlane(kvb);
+    const bool active = __builtin_amdgcn_readfirstlane(me.valid && !me.bad && me.kvb == kvb) != 0;
+    // The query rows first: they depend on nothing below, so their round trip
+    // overlaps the pass setup.
+    // Q^T operands: block qb, lane holds query row0+32qb+col, d = 16*s + 8*half + 0..7.
+    bf16x8 qreg[kQB][QS];
+#pragma unroll
+    for (int qb = 0; qb < kQB; ++qb) {
+      const int row = me.row0 + 32 * qb + col;
+      const bool ok = active && row < me.lq;
+      const __bf16* qrow = qg + (size_t)(ok ? row : 0) * q_rs;
+#pragma unroll
+      for (int s = 0; s < QS; ++s) {
+        u32x4 x = {0u, 0u, 0u, 0u};
+        if (ok) x = *(const u32x4*)(qrow + 16 * s + 8 * half);
+        qreg[qb][s] = __builtin_bit_cast(bf16x8, x);
+      }
+    }
 
     int nvalid = jagged ? seq_len(p.kv_offsets, kvb, p.Lk) : p.Lk;
     if (p.kv_len != nullptr) nvalid = min(max(p.kv_len[kvb], 0), p.Lk);
@@ -463,7 +480,6 @@ __global__ __launch_bounds__(W * 64, (kGroupsPerCU<D, W>)) void attn_fwd_bf16_ke
       if (t.valid && !t.bad && t.kvb == kvb) ntiles = max(ntiles, tiles_touching(keys_needed(t)));
     }
     ntiles = __builtin_amdgcn_readfirstlane(ntiles);
-    const bool active = __builtin_amdgcn_readfirstlane(me.valid && !me.bad && me.kvb == kvb) != 0;
     if (ntiles == 0) {
       if (active) {
         const int row = me.row0 + col;  // no valid key: output rows are 0
@@ -534,20 +550,6 @@ __global__ __launch_bounds__(W * 64, (kGroupsPerCU<D, W>)) void attn_fwd_bf16_ke
       load_tile(vaddr, dst, t, voff, std::integral_constant<int, TL::VPER>{},
                 std::integral_constant<int, TL::VLOADS>{}, std::integral_constant<int, 64>{});
     };
-    // Q^T operands: block qb, lane holds query row0+32qb+col, d = 16*s + 8*half + 0..7.
-    bf16x8 qreg[kQB][QS];
-#pragma unroll
-    for (int qb = 0; qb < kQB; ++qb) {
-      const int row = me.row0 + 32 * qb + col;
-      const bool ok = active && row < me.lq;
-      const __bf16* qrow = qg + (size_t)(ok ? row : 0) * q_rs;
-#pragma unroll
-      for (int s = 0; s < QS; ++s) {
-        u32x4 x = {0u, 0u, 0u, 0u};
-        if (ok) x = *(const u32x4*)(qrow + 16 * s + 8 * half);
-        qreg[qb][s] = __builtin_bit_cast(bf16x8, x);
-      }
-    }
     // Scaling (or normalising) the queries waits for their loads; each
     // schedule calls this after issuing its first K/V tile loads, so that the
     // query and K/V round trips overlap.
