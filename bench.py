@@ -616,15 +616,28 @@ def ceiling(reps: int = 3) -> dict:
     iters = 20000
     ms = timed(lambda: b.ceiling_exp2(sink, wg, iters))
     n = wg * 256 * iters * 16
+    exp_per_ms = n / ms
     out["v_exp_f32"] = {"G/s": round(n / (ms * 1e-3) / 1e9, 1),
                         "per_CU_per_clk_at_2.4GHz": round(n / (ms * 1e-3) / 256 / 2.4e9, 2),
                         "ms": round(ms, 3)}
     iters = 65536
     ms = timed(lambda: b.ceiling_fma(sink, wg, iters))
     n = wg * 256 * iters * 16
+    fma_per_ms = n / ms
     out["v_fma_f32"] = {"TFLOP/s": round(2 * n / (ms * 1e-3) / 1e12, 2),
                         "per_CU_per_clk_at_2.4GHz": round(n / (ms * 1e-3) / 256 / 2.4e9, 2),
                         "ms": round(ms, 3)}
+    # One exponential between every four FMAs, against the time each part takes alone
+    # at the rates above: about 1 of their sum if the exponential takes FMA issue
+    # slots, about 1 of the larger part if it runs beside them.
+    iters = 16384
+    ms = timed(lambda: b.ceiling_exp2_fma(sink, wg, iters))
+    t_exp = wg * 256 * iters * 8 / exp_per_ms
+    t_fma = wg * 256 * iters * 32 / fma_per_ms
+    out["v_exp_f32_between_fmas"] = {"ms": round(ms, 3), "exp_part_alone_ms": round(t_exp, 3),
+                                     "fma_part_alone_ms": round(t_fma, 3),
+                                     "over_sum_of_parts": round(ms / (t_exp + t_fma), 3),
+                                     "over_larger_part": round(ms / max(t_exp, t_fma), 3)}
     wg, iters = 512, 32768
     for name, tr, nb in (("lds_read_b128", 0, 16), ("lds_read_b64_tr_b16", 1, 8)):
         ms = timed(lambda: b.ceiling_lds_read(sink, wg, iters, tr))

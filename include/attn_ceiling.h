@@ -54,6 +54,17 @@ int attn_ceiling_exp2(float* out, int workgroups, int iters, void* stream);
 int attn_ceiling_fma(float* out, int workgroups, int iters, void* stream);
 
 /*
+ * Exponentials and FMAs together: 256 threads per workgroup, 8 independent
+ * exponential chains and 32 independent FMA chains per thread, one v_exp_f32
+ * issued between every four v_fma_f32. Exponentials = workgroups * 256 * iters
+ * * 8, FMAs = workgroups * 256 * iters * 32. Timed beside the two probes above,
+ * it tells whether the exponential runs beside the FMAs (time = the larger
+ * part) or takes their issue slots (time = the sum of the parts).
+ *   out  workgroups x 256 floats (written)
+ */
+int attn_ceiling_exp2_fma(float* out, int workgroups, int iters, void* stream);
+
+/*
  * LDS read bandwidth: 512 threads per workgroup (64 KiB of LDS each), 8 reads
  * per thread and iteration, bank-conflict-free. transposed = 0: ds_read_b128
  * (16 bytes per lane); transposed != 0: ds_read_b64_tr_b16 (8 bytes per lane).

@@ -50,8 +50,8 @@ def test_header_declares_the_entry_points():
                                           "attn_fwd_qknorm_noalloc", "attn_strerror",
                                           "attn_version", "ikbo_linear"]
     assert declared_functions(os.path.join(INCLUDE, "attn_ceiling.h")) == [
-        "attn_ceiling_copy", "attn_ceiling_exp2", "attn_ceiling_fma", "attn_ceiling_lds_read",
-        "attn_ceiling_mfma_bf16"]
+        "attn_ceiling_copy", "attn_ceiling_exp2", "attn_ceiling_exp2_fma", "attn_ceiling_fma",
+        "attn_ceiling_lds_read", "attn_ceiling_mfma_bf16"]
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -271,6 +271,8 @@ def test_ceiling_probe_argument_checks(lib):
     assert lib.attn_ceiling_exp2(None, 1, 1, None) == -1
     assert lib.attn_ceiling_exp2(FAKE, 0, 1, None) == -1
     assert lib.attn_ceiling_fma(FAKE, 1, 0, None) == -1                      # no iterations
+    assert lib.attn_ceiling_exp2_fma(None, 1, 1, None) == -1
+    assert lib.attn_ceiling_exp2_fma(FAKE, 1, 0, None) == -1
     assert lib.attn_ceiling_lds_read(None, 1, 1, 0, None) == -1
     assert lib.attn_ceiling_copy(FAKE, FAKE, 17, None) == -1                 # not 16-byte units
     assert lib.attn_ceiling_copy(MISALIGNED, FAKE, 16, None) == -1

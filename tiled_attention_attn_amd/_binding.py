@@ -78,9 +78,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.attn_ceiling_mfma_bf16.argtypes = [vp, i64, vp, i32, i32, i32, vp]
     lib.attn_ceiling_exp2.argtypes = [vp, i32, i32, vp]
     lib.attn_ceiling_fma.argtypes = [vp, i32, i32, vp]
+    lib.attn_ceiling_exp2_fma.argtypes = [vp, i32, i32, vp]
     lib.attn_ceiling_lds_read.argtypes = [vp, i32, i32, i32, vp]
     lib.attn_ceiling_copy.argtypes = [vp, vp, i64, vp]
     for fn in (lib.attn_ceiling_mfma_bf16, lib.attn_ceiling_exp2, lib.attn_ceiling_fma,
+               lib.attn_ceiling_exp2_fma,
                lib.attn_ceiling_lds_read, lib.attn_ceiling_copy):
         fn.restype = i32
     _lib = lib
@@ -435,6 +437,14 @@ def ceiling_fma(out, workgroups, iters, stream=None):
         raise ValueError("ceiling_fma: out too small")
     _probe_check(load_library().attn_ceiling_fma(_ptr(out), int(workgroups), int(iters),
                                                  _stream(stream)), "attn_ceiling_fma")
+
+
+def ceiling_exp2_fma(out, workgroups, iters, stream=None):
+    """Enqueue the mixed probe: workgroups*256*iters*8 exponentials and 4x as many FMAs."""
+    if out.numel() < workgroups * 256:
+        raise ValueError("ceiling_exp2_fma: out too small")
+    _probe_check(load_library().attn_ceiling_exp2_fma(_ptr(out), int(workgroups), int(iters),
+                                                      _stream(stream)), "attn_ceiling_exp2_fma")
 
 
 def ceiling_lds_read(out, workgroups, iters, transposed, stream=None):

@@ -9,6 +9,10 @@
 //          attention inputs do; constant data does not)
 //   exp2   v_exp_f32, sixteen independent chains per lane (x <- 2^-x)
 //   fma    v_fma_f32, sixteen independent chains per lane
+//   mix    eight exponential chains and 32 FMA chains per lane, one v_exp_f32
+//          issued between every four FMAs: if the exponential ran in a unit of
+//          its own beside the FMAs, the time would be the larger of the two
+//          parts, not their sum
 //   lds    ds_read_b128, or the transposing ds_read_b64_tr_b16, from a 64 KiB
 //          LDS buffer, conflict-free addresses
 //   copy   HBM to HBM, 16-byte loads and stores, four in flight per thread
@@ -89,6 +93,33 @@ __global__ __launch_bounds__(256) void fma_kernel(float* __restrict__ out, int i
   float s = 0.f;
 #pragma unroll
   for (int j = 0; j < kChains; ++j) s += x[j];
+  out[(int64_t)blockIdx.x * 256 + threadIdx.x] = s;
+}
+
+constexpr int kMixExp = 8, kMixFma = 32;   // chains per lane of the mixed probe
+
+__global__ __launch_bounds__(256) void exp2_fma_kernel(float* __restrict__ out, int iters) {
+  float e[kMixExp], f[kMixFma];
+#pragma unroll
+  for (int j = 0; j < kMixExp; ++j) e[j] = 0.5f + 0.01f * j + 1e-5f * threadIdx.x;
+#pragma unroll
+  for (int j = 0; j < kMixFma; ++j) f[j] = 0.5f + 0.01f * j + 1e-5f * threadIdx.x;
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int j = 0; j < kMixExp; ++j) {
+      e[j] = __builtin_amdgcn_exp2f(-e[j]);
+#pragma unroll
+      for (int i = 0; i < kMixFma / kMixExp; ++i) {
+        const int k = j * (kMixFma / kMixExp) + i;
+        f[k] = __builtin_fmaf(f[k], 0.999f, 0.0005f);
+      }
+    }
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int j = 0; j < kMixExp; ++j) s += e[j];
+#pragma unroll
+  for (int j = 0; j < kMixFma; ++j) s += f[j];
   out[(int64_t)blockIdx.x * 256 + threadIdx.x] = s;
 }
 
@@ -188,6 +219,14 @@ int attn_ceiling_fma(float* out, int workgroups, int iters, void* stream) {
   if (out == nullptr || workgroups < 1 || iters < 1) return -1;
   (void)hipGetLastError();
   hipLaunchKernelGGL(fma_kernel, dim3(workgroups), dim3(256), 0, (hipStream_t)stream, out, iters);
+  return launched();
+}
+
+int attn_ceiling_exp2_fma(float* out, int workgroups, int iters, void* stream) {
+  if (out == nullptr || workgroups < 1 || iters < 1) return -1;
+  (void)hipGetLastError();
+  hipLaunchKernelGGL(exp2_fma_kernel, dim3(workgroups), dim3(256), 0, (hipStream_t)stream, out,
+                     iters);
   return launched();
 }
 
