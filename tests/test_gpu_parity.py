@@ -81,7 +81,31 @@ DENSE_CASES = [
 ]
 
 
-@pytest.mark.parametrize("case", DENSE_CASES, ids=lambda c: "-".join(map(str, c[:8])))
+def _random_dense_cases(n_short=24, n_long=4, seed=2026):
+    """Seeded shapes beyond the hand-picked ones: any (B, H, Hkv, Lq, Lk) in small
+    ranges, both head dims, both mask kinds, a few fp32; and some d=128 problems with
+    Lk >= 4096 (the 8-wave schedule), kept short in Lq for the oracle's sake."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n_short + n_long):
+        long = i >= n_short
+        Hkv = int(rng.integers(1, 4))
+        H = Hkv * int(rng.choice([1, 2, 4]))
+        B = int(rng.integers(1, 4))
+        d = 128 if long else int(rng.choice([64, 128]))
+        Lq = int(rng.integers(1, 120 if long else 400))
+        Lk = int(rng.integers(4096, 6000)) if long else int(rng.integers(1, 600))
+        dtype = "f32" if (not long and rng.random() < 0.2) else "bf16"
+        causal = bool(rng.random() < 0.5)
+        if long:
+            causal = bool(i % 2)   # half of them run the whole key range
+        kvr = (int(rng.integers(0, Lk)), Lk) if rng.random() < 0.4 else None
+        cases.append((B, H, Hkv, Lq, Lk, d, dtype, causal, kvr))
+    return cases
+
+
+@pytest.mark.parametrize("case", DENSE_CASES + _random_dense_cases(),
+                         ids=lambda c: "-".join(map(str, c[:8])))
 def test_dense_matches_oracle(lib, case):
     B, H, Hkv, Lq, Lk, d, dtype, causal, kvr = case
     w = ai.make_dense(B, H, Hkv, Lq, Lk, d, dtype=dtype, causal=causal, seed=11,
@@ -147,6 +171,26 @@ BCAST_CASES = [
     (8, 2, 2, 2, 64, 8200, 128, "bf16", False, "shuffled"),   # 8-wave schedule
     (5, 2, 4, 2, 40, 8300, 128, "bf16", True, "contiguous"),
 ]
+
+
+def _random_bcast_cases(n=10, seed=2027):
+    """Seeded broadcast shapes: any candidate and user counts, query and key lengths
+    in small ranges, both head dims, contiguous or shuffled maps."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for _ in range(n):
+        Hkv = int(rng.integers(1, 3))
+        H = Hkv * int(rng.choice([1, 2]))
+        B_u = int(rng.integers(1, 6))
+        B_c = int(rng.integers(1, 21))
+        d = int(rng.choice([64, 128]))
+        cases.append((B_c, B_u, H, Hkv, int(rng.integers(1, 130)), int(rng.integers(1, 400)), d,
+                      "bf16", bool(rng.random() < 0.5),
+                      "shuffled" if rng.random() < 0.5 else "contiguous"))
+    return cases
+
+
+BCAST_CASES += _random_bcast_cases()
 
 
 def _map(kind, B_c, B_u, seed=0):
