@@ -49,6 +49,26 @@ SPARSE_CASES = [
 ]
 
 
+def _random_sparse_cases(n=5, seed=2029):
+    """Seeded block-sparse problems: block sizes of 128-512, random masks per head or
+    shared, ragged edges, both head dims, with or without kv_len."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for _ in range(n):
+        Hkv = int(rng.integers(1, 3))
+        H = Hkv * int(rng.choice([1, 2]))
+        blk = 128 * int(rng.integers(1, 5))
+        Lq, Lk = int(rng.integers(1, 1500)), int(rng.integers(1, 1500))
+        kvr = (int(rng.integers(0, Lk)), Lk) if rng.random() < 0.4 else None
+        cases.append((int(rng.integers(1, 3)), H, Hkv, Lq, Lk, int(rng.choice([64, 128])), "bf16",
+                      bool(rng.random() < 0.5), blk, int(rng.choice([1, H])),
+                      float(rng.uniform(0.2, 0.8)), kvr))
+    return cases
+
+
+SPARSE_CASES += _random_sparse_cases()
+
+
 @pytest.mark.parametrize("case", SPARSE_CASES,
                          ids=lambda c: f"{c[6]}-d{c[5]}-c{int(c[7])}-L{c[3]}x{c[4]}-blk{c[8]}")
 def test_block_sparse_matches_oracle(lib, case):

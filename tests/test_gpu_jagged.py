@@ -50,6 +50,24 @@ JAGGED_CASES = [
 ]
 
 
+def _random_jagged_cases(n=6, seed=2028):
+    """Seeded packed batches: 1-7 sequences of 0-600 tokens (keys the same lengths or
+    drawn apart), both head dims, GQA or not, causal or not."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for _ in range(n):
+        Hkv = int(rng.integers(1, 3))
+        nb = int(rng.integers(1, 8))
+        lq = [int(x) if rng.random() > 0.15 else 0 for x in rng.integers(1, 600, size=nb)]
+        lk = None if rng.random() < 0.5 else [int(x) for x in rng.integers(0, 600, size=nb)]
+        cases.append((Hkv * int(rng.choice([1, 2])), Hkv, int(rng.choice([64, 128])), "bf16",
+                      bool(rng.random() < 0.5), lq, lk))
+    return cases
+
+
+JAGGED_CASES += _random_jagged_cases()
+
+
 @pytest.mark.parametrize("case", JAGGED_CASES, ids=lambda c: f"{c[3]}-d{c[2]}-c{int(c[4])}-"
                          f"{'_'.join(map(str, c[5]))}")
 def test_jagged_matches_oracle(lib, case):

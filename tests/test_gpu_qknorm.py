@@ -49,6 +49,23 @@ QKNORM_CASES = [
 ]
 
 
+def _random_qknorm_cases(n=4, seed=2030):
+    """Seeded q/k-normalised problems in small ranges, both head dims."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for _ in range(n):
+        Hkv = int(rng.integers(1, 3))
+        Lk = int(rng.integers(1, 500))
+        kvr = (int(rng.integers(0, Lk)), Lk) if rng.random() < 0.4 else None
+        cases.append((int(rng.integers(1, 3)), Hkv * int(rng.choice([1, 2, 4])), Hkv,
+                      int(rng.integers(1, 400)), Lk, int(rng.choice([64, 128])),
+                      bool(rng.random() < 0.5), kvr, bool(rng.random() < 0.7), 1e-6))
+    return cases
+
+
+QKNORM_CASES += _random_qknorm_cases()
+
+
 @pytest.mark.parametrize("case", QKNORM_CASES,
                          ids=lambda c: f"d{c[5]}-c{int(c[6])}-L{c[3]}x{c[4]}-g{int(c[8])}-e{c[9]}")
 def test_qknorm_matches_oracle(lib, case):
