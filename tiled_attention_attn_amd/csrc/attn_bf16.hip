@@ -310,6 +310,40 @@ __global__ __launch_bounds__(W * 64, (kGroupsPerCU<D, W>)) void attn_fwd_bf16_ke
     tk[w].kvb = tk[w].batch;
     tk[w].bad = false;
   }
+  // The wave's own rows are wave-uniform; moving them to scalar registers lets
+  // the compiler treat everything derived from them (loop bounds, buffer
+  // descriptors) as uniform.
+  WaveTask me = tk[0];
+#pragma unroll
+  for (int w = 1; w < kWaves; ++w)
+    if (wave == w) me = tk[w];
+  me.batch = __builtin_amdgcn_readfirstlane(me.batch);
+  me.row0 = __builtin_amdgcn_readfirstlane(me.row0);
+  me.lq = __builtin_amdgcn_readfirstlane(me.lq);
+  me.valid = __builtin_amdgcn_readfirstlane((int)me.valid) != 0;
+  // element offset of row 0 of this wave's (sequence, head)
+  size_t q_base = ((size_t)(me.valid ? me.batch : 0) * p.H + h) * (size_t)p.Lq * D;
+  if (jagged) q_base = me.valid ? (size_t)p.q_offsets[me.batch] * q_rs + (size_t)h * D : 0;
+  const __bf16* __restrict__ qg = (const __bf16*)p.q + q_base;
+  __bf16* __restrict__ og = (__bf16*)p.o + q_base;
+
+  // The query rows next: they need no K/V index, so their round trip overlaps
+  // the user lookup and the pass setup. A wave computes in exactly one pass.
+  // Q^T operands: block qb, lane holds query row0+32qb+col, d = 16*s + 8*half + 0..7.
+  bf16x8 qreg[kQB][QS];
+#pragma unroll
+  for (int qb = 0; qb < kQB; ++qb) {
+    const int row = me.row0 + 32 * qb + col;
+    const bool ok = me.valid && row < me.lq;
+    const __bf16* qrow = qg + (size_t)(ok ? row : 0) * q_rs;
+#pragma unroll
+    for (int s = 0; s < QS; ++s) {
+      u32x4 x = {0u, 0u, 0u, 0u};
+      if (ok) x = *(const u32x4*)(qrow + 16 * s + 8 * half);
+      qreg[qb][s] = __builtin_bit_cast(bf16x8, x);
+    }
+  }
+
   if (p.cand2user != nullptr) {
     int u[kWaves];
 #pragma unroll
@@ -322,24 +356,16 @@ __global__ __launch_bounds__(W * 64, (kGroupsPerCU<D, W>)) void attn_fwd_bf16_ke
     }
   }
 
-  // The wave's own task is wave-uniform; moving it to scalar registers lets
-  // the compiler treat everything derived from it (loop bounds, buffer
-  // descriptors) as uniform.
-  WaveTask me = tk[0];
+  // the wave's K/V batch and user check, once the map is read
+  {
+    int kvb_me = tk[0].kvb;
+    bool bad_me = tk[0].bad;
 #pragma unroll
-  for (int w = 1; w < kWaves; ++w)
-    if (wave == w) me = tk[w];
-  me.batch = __builtin_amdgcn_readfirstlane(me.batch);
-  me.row0 = __builtin_amdgcn_readfirstlane(me.row0);
-  me.lq = __builtin_amdgcn_readfirstlane(me.lq);
-  me.kvb = __builtin_amdgcn_readfirstlane(me.kvb);
-  me.valid = __builtin_amdgcn_readfirstlane((int)me.valid) != 0;
-  me.bad = __builtin_amdgcn_readfirstlane((int)me.bad) != 0;
-  // element offset of row 0 of this wave's (sequence, head)
-  size_t q_base = ((size_t)(me.valid ? me.batch : 0) * p.H + h) * (size_t)p.Lq * D;
-  if (jagged) q_base = me.valid ? (size_t)p.q_offsets[me.batch] * q_rs + (size_t)h * D : 0;
-  const __bf16* __restrict__ qg = (const __bf16*)p.q + q_base;
-  __bf16* __restrict__ og = (__bf16*)p.o + q_base;
+    for (int w = 1; w < kWaves; ++w)
+      if (wave == w) { kvb_me = tk[w].kvb; bad_me = tk[w].bad; }
+    me.kvb = __builtin_amdgcn_readfirstlane(kvb_me);
+    me.bad = __builtin_amdgcn_readfirstlane((int)bad_me) != 0;
+  }
 
   // Candidates with an out-of-range user index get NaN rows.
   if (me.valid && me.bad) {
@@ -385,7 +411,18 @@ __global__ __launch_bounds__(W * 64, (kGroupsPerCU<D, W>)) void attn_fwd_bf16_ke
     voff[j] = (uint32_t)(wave + j * kWaves) * ((uint32_t)VROWS * row_bytes) + vpart;
 
   // One pass per distinct K/V batch among the waves.
-  for (; leads != 0; leads &= leads - 1) {
+  // A pass after the first reloads its query rows, and the registers are
+  // declared undefined at the end of each pass (an empty asm that writes
+  // them), so the rows are not kept live through a pass's epilogue for a
+  // later pass.
+  auto forget_q = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int qb = 0; qb < kQB; ++qb)
+#pragma unroll
+      for (int s = 0; s < QS; ++s) asm volatile("" : "=v"(qreg[qb][s]));
+  };
+  bool first_pass = true;
+  for (; leads != 0; forget_q(), first_pass = false, leads &= leads - 1) {
     const int lead = __builtin_ctz(leads);
     int kvb = 0;
 #pragma unroll
@@ -393,20 +430,18 @@ __global__ __launch_bounds__(W * 64, (kGroupsPerCU<D, W>)) void attn_fwd_bf16_ke
       if (w == lead) kvb = tk[w].kvb;
     kvb = __builtin_amdgcn_readfirstlane(kvb);
     const bool active = __builtin_amdgcn_readfirstlane(me.valid && !me.bad && me.kvb == kvb) != 0;
-    // The query rows first: they depend on nothing below, so their round trip
-    // overlaps the pass setup.
-    // Q^T operands: block qb, lane holds query row0+32qb+col, d = 16*s + 8*half + 0..7.
-    bf16x8 qreg[kQB][QS];
+    if (!first_pass) {
 #pragma unroll
-    for (int qb = 0; qb < kQB; ++qb) {
-      const int row = me.row0 + 32 * qb + col;
-      const bool ok = active && row < me.lq;
-      const __bf16* qrow = qg + (size_t)(ok ? row : 0) * q_rs;
+      for (int qb = 0; qb < kQB; ++qb) {
+        const int row = me.row0 + 32 * qb + col;
+        const bool ok = active && row < me.lq;
+        const __bf16* qrow = qg + (size_t)(ok ? row : 0) * q_rs;
 #pragma unroll
-      for (int s = 0; s < QS; ++s) {
-        u32x4 x = {0u, 0u, 0u, 0u};
-        if (ok) x = *(const u32x4*)(qrow + 16 * s + 8 * half);
-        qreg[qb][s] = __builtin_bit_cast(bf16x8, x);
+        for (int s = 0; s < QS; ++s) {
+          u32x4 x = {0u, 0u, 0u, 0u};
+          if (ok) x = *(const u32x4*)(qrow + 16 * s + 8 * half);
+          qreg[qb][s] = __builtin_bit_cast(bf16x8, x);
+        }
       }
     }
 
