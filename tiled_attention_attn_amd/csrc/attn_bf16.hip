@@ -759,16 +759,18 @@ __global__ __launch_bounds__(W * 64, (kGroupsPerCU<D, W>)) void attn_fwd_bf16_ke
     // and returns the rescale factor of O.
     auto softmax = [&](f32x16 (&sacc)[KB], int qb, int tile, bool masked, bf16x8 (&pout)[PS]) __attribute__((always_inline)) -> float {
       if (masked) {
-        const int key0 = tile * BN;
+        // Element (kbk, i) holds key tile*BN + half*4 + off with a compile-time
+        // off; it is dead (past kv_len, or after the row's own position when
+        // causal) iff off >= lim. lim depends on the tile, so no comparison is
+        // hoisted out of the tile loop as a loop-invariant mask.
         const int qrow = me.row0 + 32 * qb + col;
+        const int lim = (CAUSAL ? min(nvalid, qrow + 1) : nvalid) - (tile * BN + half * 4);
 #pragma unroll
         for (int kbk = 0; kbk < KB; ++kbk)
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
-            const int key = key0 + kbk * 32 + (i >> 2) * 8 + half * 4 + (i & 3);
-            bool dead = key >= nvalid;
-            if (CAUSAL) dead = dead || key > qrow;
-            if (dead) sacc[kbk][i] = -INFINITY;
+            const int off = kbk * 32 + (i >> 2) * 8 + (i & 3);
+            if (off >= lim) sacc[kbk][i] = -INFINITY;
           }
       }
       // Exponentials 2^(sacc - d), rounded to bf16 as the next PV operand;
