@@ -569,12 +569,21 @@ __global__ __launch_bounds__(W * 64, (kGroupsPerCU<D, W>)) void attn_fwd_bf16_ke
       const int left = max((int)kv_bytes - (int)tile_off, 0);
       const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
           (void*)(uintptr_t)(base + tile_off), (short)0, left, kBufferWord3);
+      // LDS destination of load j: the buffer's address plus this wave's
+      // window offset plus a compile-time step. The wave offset passes through
+      // an empty asm on every call, so the sum is one scalar add here rather
+      // than one loop-invariant register per (buffer, j) pair, which the
+      // compiler spilled to VGPR lanes and read back in the loops.
+      uint32_t wofs = (uint32_t)wave * (uint32_t)(STRIDE * 16);
+      asm volatile("" : "+s"(wofs));
+      const uint32_t d0 = (uint32_t)(uintptr_t)((void LDS_AS*)dst) + wofs;
 #pragma unroll
       for (int j = 0; j < PER; ++j) {
         const int n = wave + j * kWaves;
         if (j < PER - 1 || NLOADS % kWaves == 0 || n < NLOADS)
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (void LDS_AS*)(dst + n * STRIDE), 16, off[j],
-                                                   0, 0, 0);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(
+              rsrc, (void LDS_AS*)(uintptr_t)(d0 + (uint32_t)(j * kWaves * STRIDE * 16)), 16, off[j],
+              0, 0, 0);
       }
     };
     auto load_k = [&](u32x4* dst, int t) __attribute__((always_inline)) {
