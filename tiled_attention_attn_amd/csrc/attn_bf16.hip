@@ -53,6 +53,7 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 #define LDS_AS __attribute__((address_space(3)))
@@ -73,7 +74,7 @@ struct Tile {
   // load fills one 1 KB window with 64 / NC whole rows of K or V, so that it
   // reads whole rows of memory, and neither layout has pad chunks to load.
   // K: window w holds rows w, w + NWIN, w + 2 NWIN, ... row-major, and the
-  // windows start KWIN = 65 chunks apart: (row r, chunk c) is at chunk
+  // windows start KWIN chunks apart: (row r, chunk c) is at chunk
   // (r % NWIN) * KWIN + (r / NWIN) * NC + c. A K operand read has 16 lanes on
   // 16 consecutive rows at one chunk; the one-chunk stagger of the windows
   // (and, at d = 64, the row offset inside a window) puts them on 16
@@ -84,7 +85,13 @@ struct Tile {
   // one block: 256 contiguous bytes, every bank once. Either way every
   // operand address is a per-lane base plus an immediate.
   static constexpr int NWIN = BN * NC / 64;          // K windows (= wave loads) per tile
-  static constexpr int KWIN = 65;                    // chunks between K window starts
+  // chunks between K window starts: 65 for the 32 x 32 operand reads, 66 for
+  // the 16 x 16 ones of the 8-wave d = 128 schedule. A 16-byte operand read
+  // is served 32 lanes at a time over 512 bytes of banks (measured: a
+  // pattern whose lane groups 0 and 1 sat 16 bytes apart had four conflict
+  // cycles per read). There, lanes l and l + 16 read one row 16 bytes apart,
+  // so consecutive rows must sit 32 bytes apart modulo 512: 66 chunks.
+  static constexpr int KWIN = (W == 8 && D == 128) ? 66 : 65;
   static_assert(32 % NWIN == 0, "a 32-key block spans whole rounds of K windows");
   static constexpr int VROWS = 64 / NC;              // V rows per 1 KB window
   static_assert(VROWS == 4 || VROWS == 8, "a V read's 16-row step spans whole windows");
@@ -145,6 +152,19 @@ __device__ __forceinline__ float halves_sum(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
+// The same over the four 16-lane rows (lanes l, l^16, l^32, l^48 hold one
+// query in the 16 x 16 tiles of v_mfma_f32_16x16x32_bf16): after the
+// half exchange, one row-pair swap (rows 0 <-> 1, 2 <-> 3).
+__device__ __forceinline__ float rowpair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return vmax(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float rowpair_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float quarters_max(float x) { return rowpair_max(halves_max(x)); }
+__device__ __forceinline__ float quarters_sum(float x) { return rowpair_sum(halves_sum(x)); }
 
 // Lazy rescaling: the reference r used for the exponent 2^(u - r) moves to
 // the row max on a row's first unmasked tile and then stays put while every
@@ -193,7 +213,30 @@ template <int D, bool CAUSAL, int W, int LAYOUT>
 __global__ __launch_bounds__(W * 64, (kGroupsPerCU<D, W>)) void attn_fwd_bf16_kernel(const Params p) {
   using TL = Tile<D, W>;
   constexpr int kWaves = W;
-  constexpr int BN = TL::BN, NC = TL::NC, KB = TL::KB, DB = TL::DB, QS = TL::QS, PS = TL::PS;
+  constexpr int BN = TL::BN, NC = TL::NC;
+  // Matrix-core shape. The 8-wave d = 128 schedule runs both products on
+  // v_mfma_f32_16x16x32_bf16: on this chip, at the power limit, it sustains
+  // about 1.5 times the rate of v_mfma_f32_32x32x16_bf16 on the same operand
+  // data (half the accumulator traffic per FLOP). Its 16 x 16 tiles put a
+  // wave's 32 queries in two blocks of 16 (lane l holds query l % 16 of each)
+  // and a tile's keys in blocks of 16 (lane l holds keys 4 (l / 16) .. +3 of
+  // each); the other schedules keep the 32 x 32 tiles: one block of 32
+  // queries (lane l holds query l % 32) and keys in blocks of 32.
+  constexpr bool M16 = W == 8 && D == 128;
+  constexpr int QB = M16 ? 2 : kQB;               // query blocks per wave
+  constexpr int QR = M16 ? 16 : 32;               // queries per block
+  constexpr int KB = M16 ? BN / 16 : TL::KB;      // key blocks per tile
+  constexpr int DB = M16 ? D / 16 : TL::DB;       // d blocks of O^T
+  constexpr int QS = M16 ? D / 32 : TL::QS;       // k-steps of the QK^T product
+  constexpr int PS = M16 ? BN / 32 : TL::PS;      // k-steps of the PV product
+  constexpr int AE = M16 ? 4 : 16;                // accumulator floats per lane
+  using Acc = std::conditional_t<M16, f32x4, f32x16>;
+  // Chunks between V window starts. The 16 x 16 transposing reads of lane
+  // groups 0 and 1 (and 2 and 3) fall on consecutive windows, so the windows
+  // are staggered by 32 bytes there (within the slack of the V buffers), which
+  // puts the two groups of a read cycle on different banks.
+  constexpr int VWIN = M16 ? 66 : 64;
+  static_assert(TL::VLOADS * VWIN <= TL::VCHUNKS + TL::VSLACK, "staggered V windows fit the buffer");
   constexpr int NWIN = TL::NWIN, KWIN = TL::KWIN, VROWS = TL::VROWS;
 
   // Four distinct LDS objects, so the compiler can tell that the loads in
@@ -210,6 +253,8 @@ __global__ __launch_bounds__(W * 64, (kGroupsPerCU<D, W>)) void attn_fwd_bf16_ke
   const int col = lane & 31;    // the query this lane owns
   const int il = lane & 15;     // index inside a 16-lane group (transposing read)
   const int grp = lane >> 4;    // 16-lane group
+  const int qcol = M16 ? il : col;   // the query of a block this lane holds
+  const int qgrp = M16 ? grp : half; // which keys of a key block it holds
 
   // ---- decode the logical tile --------------------------------------------
   const int L = xcd_remap(blockIdx.x, p.T, p.chunk);
@@ -330,16 +375,18 @@ __global__ __launch_bounds__(W * 64, (kGroupsPerCU<D, W>)) void attn_fwd_bf16_ke
   // The query rows next: they need no K/V index, so their round trip overlaps
   // the user lookup and the pass setup. A wave computes in exactly one pass.
   // Q^T operands: block qb, lane holds query row0+32qb+col, d = 16*s + 8*half + 0..7.
-  bf16x8 qreg[kQB][QS];
+  // (16 x 16 tiles: lane l holds query row0+16qb+l%16, d = 32*s + 8*(l/16) + 0..7.)
+  bf16x8 qreg[QB][QS];
+  constexpr int QSTEP = M16 ? 32 : 16;   // d per k-step
 #pragma unroll
-  for (int qb = 0; qb < kQB; ++qb) {
-    const int row = me.row0 + 32 * qb + col;
+  for (int qb = 0; qb < QB; ++qb) {
+    const int row = me.row0 + QR * qb + qcol;
     const bool ok = me.valid && row < me.lq;
     const __bf16* qrow = qg + (size_t)(ok ? row : 0) * q_rs;
 #pragma unroll
     for (int s = 0; s < QS; ++s) {
       u32x4 x = {0u, 0u, 0u, 0u};
-      if (ok) x = *(const u32x4*)(qrow + 16 * s + 8 * half);
+      if (ok) x = *(const u32x4*)(qrow + QSTEP * s + 8 * qgrp);
       qreg[qb][s] = __builtin_bit_cast(bf16x8, x);
     }
   }
@@ -417,7 +464,7 @@ __global__ __launch_bounds__(W * 64, (kGroupsPerCU<D, W>)) void attn_fwd_bf16_ke
   // later pass.
   auto forget_q = [&]() __attribute__((always_inline)) {
 #pragma unroll
-    for (int qb = 0; qb < kQB; ++qb)
+    for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
       for (int s = 0; s < QS; ++s) asm volatile("" : "=v"(qreg[qb][s]));
   };
@@ -432,14 +479,14 @@ __global__ __launch_bounds__(W * 64, (kGroupsPerCU<D, W>)) void attn_fwd_bf16_ke
     const bool active = __builtin_amdgcn_readfirstlane(me.valid && !me.bad && me.kvb == kvb) != 0;
     if (!first_pass) {
 #pragma unroll
-      for (int qb = 0; qb < kQB; ++qb) {
-        const int row = me.row0 + 32 * qb + col;
+      for (int qb = 0; qb < QB; ++qb) {
+        const int row = me.row0 + QR * qb + qcol;
         const bool ok = active && row < me.lq;
         const __bf16* qrow = qg + (size_t)(ok ? row : 0) * q_rs;
 #pragma unroll
         for (int s = 0; s < QS; ++s) {
           u32x4 x = {0u, 0u, 0u, 0u};
-          if (ok) x = *(const u32x4*)(qrow + 16 * s + 8 * half);
+          if (ok) x = *(const u32x4*)(qrow + QSTEP * s + 8 * qgrp);
           qreg[qb][s] = __builtin_bit_cast(bf16x8, x);
         }
       }
@@ -592,14 +639,14 @@ __global__ __launch_bounds__(W * 64, (kGroupsPerCU<D, W>)) void attn_fwd_bf16_ke
     };
     auto load_v = [&](u32x4* dst, int t) __attribute__((always_inline)) {
       load_tile(vaddr, dst, t, voff, std::integral_constant<int, TL::VPER>{},
-                std::integral_constant<int, TL::VLOADS>{}, std::integral_constant<int, 64>{});
+                std::integral_constant<int, TL::VLOADS>{}, std::integral_constant<int, VWIN>{});
     };
     // Scaling (or normalising) the queries waits for their loads; each
     // schedule calls this after issuing its first K/V tile loads, so that the
     // query and K/V round trips overlap.
     auto prep_q = [&]() __attribute__((always_inline)) {
 #pragma unroll
-    for (int qb = 0; qb < kQB; ++qb) {
+    for (int qb = 0; qb < QB; ++qb) {
       // The softmax scale c = scale * log2(e) is folded into the query
       // operands (one bf16 rounding of c * q), so the score MFMAs produce
       // base-2 logits directly. RMS normalisation of the query row is fused
@@ -619,7 +666,7 @@ __global__ __launch_bounds__(W * 64, (kGroupsPerCU<D, W>)) void attn_fwd_bf16_ke
             const float v = (float)qreg[qb][s][e];
             ss = __builtin_fmaf(v, v, ss);
           }
-        ss = halves_sum(ss);
+        ss = M16 ? quarters_sum(ss) : halves_sum(ss);
         const float r = 1.0f / sqrtf(ss * (1.0f / D) + p.eps);
         // gamma_q (16-byte aligned) in 16-byte loads, all issued before any
         // is used; one branch for the whole row
@@ -629,7 +676,7 @@ __global__ __launch_bounds__(W * 64, (kGroupsPerCU<D, W>)) void attn_fwd_bf16_ke
 #pragma unroll
           for (int s = 0; s < QS; ++s)
 #pragma unroll
-            for (int k4 = 0; k4 < 2; ++k4) g[s][k4] = *(const f32x4*)(gq + 16 * s + 8 * half + 4 * k4);
+            for (int k4 = 0; k4 < 2; ++k4) g[s][k4] = *(const f32x4*)(gq + QSTEP * s + 8 * qgrp + 4 * k4);
         } else {
 #pragma unroll
           for (int s = 0; s < QS; ++s)
@@ -645,13 +692,13 @@ __global__ __launch_bounds__(W * 64, (kGroupsPerCU<D, W>)) void attn_fwd_bf16_ke
     }
     };
 
-    f32x16 oacc[kQB][DB];
+    Acc oacc[QB][DB];
 #pragma unroll
-    for (int qb = 0; qb < kQB; ++qb)
+    for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
       for (int b = 0; b < DB; ++b)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) oacc[qb][b][i] = 0.f;
+        for (int i = 0; i < AE; ++i) oacc[qb][b][i] = 0.f;
     // Online-softmax state of the lane's query row, in base-2 logit units u
     // (the queries carry the scale): the reference r (scores are
     // exponentiated as 2^(u - r)), this lane's partial row sum, and pen =
@@ -664,23 +711,27 @@ __global__ __launch_bounds__(W * 64, (kGroupsPerCU<D, W>)) void attn_fwd_bf16_ke
     // product, into registers that hold nothing live at that point.
     constexpr bool kSeed = true;
     constexpr bool kKeepSeed = W == 4;
-    float r_ref[kQB], l_run[kQB], pen[kQB];
-    f32x16 neg_r[kQB];
+    float r_ref[QB], l_run[QB], pen[QB];
+    Acc neg_r[QB];
 #pragma unroll
-    for (int qb = 0; qb < kQB; ++qb) {
+    for (int qb = 0; qb < QB; ++qb) {
       r_ref[qb] = 0.f;
       l_run[qb] = 0.f;
       pen[qb] = INFINITY;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) neg_r[qb][i] = 0.f;
+      for (int i = 0; i < AE; ++i) neg_r[qb][i] = 0.f;
     }
-    bf16x8 pprev[kQB][PS];          // probabilities of the previous tile (PV operand)
+    bf16x8 pprev[QB][PS];          // probabilities of the previous tile (PV operand)
 
     // V^T operands come through the transposing LDS read: source role il
     // addresses V[row][dcol .. dcol+3], result lane il then holds
     // V[key0 + s][dbase + il] for s = 0..3.
-    const int vrow = half * 4 + (il >> 2);
-    const int vlane = (vrow / VROWS) * 1024 + (vrow % VROWS) * 64 + ((grp & 1) * 16 + 4 * (il & 3)) * 2;
+    // 32 x 32 tiles: group grp reads keys half*4 (+8) at d-columns (grp&1)*16 of
+    // a 32-wide block. 16 x 16 tiles: group grp reads keys 4 grp (+16) at
+    // d-columns 0..15 of a 16-wide block (V window grp, VROWS = 4).
+    const int vrow = M16 ? 4 * grp + (il >> 2) : half * 4 + (il >> 2);
+    const int vlane = M16 ? (vrow / VROWS) * (VWIN * 16) + (vrow % VROWS) * 64 + (il & 3) * 8
+                          : (vrow / VROWS) * 1024 + (vrow % VROWS) * 64 + ((grp & 1) * 16 + 4 * (il & 3)) * 2;
     // Both products of one step in a single instruction stream: first
     // O += P(t-1) V(t-1), then S(t) = K(t) Q^T, so P(t-1) is dead before S(t)
     // is born. Operand reads run two MFMAs ahead through the whole stream
@@ -688,10 +739,89 @@ __global__ __launch_bounds__(W * 64, (kGroupsPerCU<D, W>)) void attn_fwd_bf16_ke
     // not wait at the seam between the products. PV_C / QK_C (compile time)
     // drop one of the products: the first tile of a pass has no PV product
     // and the step after the last tile no QK product.
-    auto pvqk = [&](f32x16 (&sacc)[kQB][KB], const u32x4* kb, const u32x4* vb32, auto pv_c,
+    auto pvqk = [&](Acc (&sacc)[QB][KB], const u32x4* kb, const u32x4* vb32, auto pv_c,
                     auto qk_c) __attribute__((always_inline)) {
-      static_assert(kQB == 1, "one query block per wave");
       constexpr bool PV = decltype(pv_c)::value, QK = decltype(qk_c)::value;
+      if constexpr (M16) {
+        static_assert(VROWS == 4 && NWIN == 16 && NC == 16, "16 x 16 tiles: d = 128 layouts");
+        // K operand (key block kt, k-step s): lane l reads key kt*16 + l%16
+        // (window l%16), chunk 4 s + l/16.
+        const u32x4* kl = kb + il * KWIN + grp;
+        const LDS_AS char* vb = (const LDS_AS char*)vb32 + vlane;
+        constexpr int NK = QS * KB, NV = PS * DB;
+        bf16x8 ka[QS][KB], va[NV];
+        if constexpr (PV) {
+          // V^T operand (32-key step c, 16-wide d block db): keys 32c + 4 grp
+          // + 0..3 (lo) and 32c + 16 + 4 grp + 0..3 (hi) at d = 16 db + l%16,
+          // matching the probabilities' k order.
+#pragma unroll
+          for (int step = 0; step < NV; ++step) {
+            const int c = step / DB, db = step % DB;
+            const int o1 = (c * 8) * (VWIN * 16) + (db / 2) * (VROWS * 64) + (db % 2) * 32;
+            const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)(vb + o1));
+            const bf16x4 hi =
+                __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)(vb + o1 + 4 * (VWIN * 16)));
+            va[step] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+          }
+#pragma unroll
+          for (int step = 0; step < NV; ++step)
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb)
+              oacc[qb][step % DB] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                  va[step], pprev[qb][step / DB], oacc[qb][step % DB], 0, 0, 0);
+        }
+        if constexpr (QK) {
+          Acc seed[QB];
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+            for (int i = 0; i < AE; ++i) seed[qb][i] = -r_ref[qb];
+#pragma unroll
+          for (int s = 0; s < QS; ++s)
+#pragma unroll
+            for (int kt = 0; kt < KB; ++kt) ka[s][kt] = __builtin_bit_cast(bf16x8, kl[kt * NC + 4 * s]);
+#pragma unroll
+          for (int s = 0; s < QS; ++s)
+#pragma unroll
+            for (int kt = 0; kt < KB; ++kt)
+#pragma unroll
+              for (int qb = 0; qb < QB; ++qb)
+                sacc[qb][kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    ka[s][kt], qreg[qb][s], s > 0 ? sacc[qb][kt] : seed[qb], 0, 0, 0);
+        }
+        // operand reads two MFMA pairs ahead, as below
+        if constexpr (PV && QK) {
+          __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 4, 0);
+#pragma unroll
+          for (int i = 0; i < NV - 2; ++i) {
+            __builtin_amdgcn_sched_group_barrier(kSchedMFMA, QB, 0);
+            __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 2, 0);
+          }
+#pragma unroll
+          for (int i = 0; i < NK; ++i) {
+            __builtin_amdgcn_sched_group_barrier(kSchedMFMA, QB, 0);
+            __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 1, 0);
+          }
+          __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 2 * QB, 0);
+        } else if constexpr (PV) {
+          __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 4, 0);
+#pragma unroll
+          for (int i = 0; i < NV - 2; ++i) {
+            __builtin_amdgcn_sched_group_barrier(kSchedMFMA, QB, 0);
+            __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 2, 0);
+          }
+          __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 2 * QB, 0);
+        } else if constexpr (QK) {
+          __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 2, 0);
+#pragma unroll
+          for (int i = 0; i < NK - 2; ++i) {
+            __builtin_amdgcn_sched_group_barrier(kSchedMFMA, QB, 0);
+            __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 1, 0);
+          }
+          __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 2 * QB, 0);
+        }
+      } else {
+      static_assert(QB == 1, "one query block per wave");
       const u32x4* kl = kb + (col % NWIN) * KWIN + (col / NWIN) * NC + half;
       const LDS_AS char* vb = (const LDS_AS char*)vb32 + vlane;
       constexpr int NK = QS * KB, NV = PS * DB;
@@ -760,25 +890,28 @@ __global__ __launch_bounds__(W * 64, (kGroupsPerCU<D, W>)) void attn_fwd_bf16_ke
         }
         __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 2, 0);
       }
+      }
     };
     using kOn = std::true_type;
     using kOff = std::false_type;
     // Online softmax of block qb for tile t: sacc holds u - r, the base-2
     // logits relative to the row's reference; produces the next PV operand
     // and returns the rescale factor of O.
-    auto softmax = [&](f32x16 (&sacc)[KB], int qb, int tile, bool masked, bf16x8 (&pout)[PS]) __attribute__((always_inline)) -> float {
+    auto softmax = [&](Acc (&sacc)[KB], int qb, int tile, bool masked, bf16x8 (&pout)[PS]) __attribute__((always_inline)) -> float {
       if (masked) {
         // Element (kbk, i) holds key tile*BN + half*4 + off with a compile-time
         // off; it is dead (past kv_len, or after the row's own position when
         // causal) iff off >= lim. lim depends on the tile, so no comparison is
         // hoisted out of the tile loop as a loop-invariant mask.
-        const int qrow = me.row0 + 32 * qb + col;
-        const int lim = (CAUSAL ? min(nvalid, qrow + 1) : nvalid) - (tile * BN + half * 4);
+        const int qrow = me.row0 + QR * qb + qcol;
+        const int lim = (CAUSAL ? min(nvalid, qrow + 1) : nvalid) - (tile * BN + qgrp * 4);
 #pragma unroll
         for (int kbk = 0; kbk < KB; ++kbk)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int off = kbk * 32 + (i >> 2) * 8 + (i & 3);
+          for (int i = 0; i < AE; ++i) {
+            // 32 x 32: key 32 kbk + 8 (i / 4) + 4 half + i % 4;
+            // 16 x 16: key 16 kbk + 4 grp + i
+            const int off = M16 ? kbk * 16 + i : kbk * 32 + (i >> 2) * 8 + (i & 3);
             if (off >= lim) sacc[kbk][i] = -INFINITY;
           }
       }
@@ -790,7 +923,9 @@ __global__ __launch_bounds__(W * 64, (kGroupsPerCU<D, W>)) void attn_fwd_bf16_ke
         for (int ps = 0; ps < PS; ++ps)
 #pragma unroll
           for (int j = 0; j < 8; ++j) {
-            float x = sacc[ps >> 1][(ps & 1) * 8 + j];
+            // the PV operand's k order: 32 x 32, keys of step ps from block ps/2;
+            // 16 x 16, slots 0-3 from key block 2 ps, 4-7 from 2 ps + 1
+            float x = M16 ? sacc[2 * ps + (j >> 2)][j & 3] : sacc[ps >> 1][(ps & 1) * 8 + j];
             if constexpr (decltype(shifted_c)::value) x -= d;
             const float e = __builtin_amdgcn_exp2f(x);
             ps4[j & 3] += e;
@@ -816,15 +951,16 @@ __global__ __launch_bounds__(W * 64, (kGroupsPerCU<D, W>)) void attn_fwd_bf16_ke
       // between the lane halves). The reference moves up to the row max, or,
       // on a row's first unmasked tile, to it from wherever it was.
       float pm[8];
+      constexpr int NE = KB * AE;   // the lane's scores of the row (32 either way)
 #pragma unroll
-      for (int j = 0; j < 8; ++j) pm[j] = vmax(sacc[0][2 * j], sacc[0][2 * j + 1]);
+      for (int j = 0; j < 8; ++j)
+        pm[j] = vmax(sacc[(2 * j) / AE][(2 * j) % AE], sacc[(2 * j + 1) / AE][(2 * j + 1) % AE]);
 #pragma unroll
-      for (int kbk = 1; kbk < KB; ++kbk)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) pm[j] = vmax(pm[j], vmax(sacc[kbk][2 * j], sacc[kbk][2 * j + 1]));
+      for (int e = 16; e < NE; e += 2)
+        pm[(e / 2) % 8] = vmax(pm[(e / 2) % 8], vmax(sacc[e / AE][e % AE], sacc[(e + 1) / AE][(e + 1) % AE]));
       float mx = vmax(vmax(vmax(pm[0], pm[1]), vmax(pm[2], pm[3])),
                       vmax(vmax(pm[4], pm[5]), vmax(pm[6], pm[7])));
-      mx = halves_max(mx) - shift;   // row max of u - r
+      mx = (M16 ? quarters_max(mx) : halves_max(mx)) - shift;   // row max of u - r
       const bool seen = pen[qb] == 0.f;
       // d: how far the reference moves (0 while a row has no unmasked key)
       const float d = seen ? vmax(mx, 0.f) : (mx == -INFINITY ? 0.f : mx);
@@ -833,7 +969,7 @@ __global__ __launch_bounds__(W * 64, (kGroupsPerCU<D, W>)) void attn_fwd_bf16_ke
       r_ref[qb] += d;
       if constexpr (kKeepSeed) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) neg_r[qb][i] = -r_ref[qb];
+        for (int i = 0; i < AE; ++i) neg_r[qb][i] = -r_ref[qb];
       }
       if (mx != -INFINITY) pen[qb] = 0.f;
       const float rs = exps(std::true_type{}, shift + d, 0.f);
@@ -845,7 +981,7 @@ __global__ __launch_bounds__(W * 64, (kGroupsPerCU<D, W>)) void attn_fwd_bf16_ke
 #pragma unroll
         for (int b = 0; b < DB; ++b)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) oacc[qb][b][i] *= alpha;
+          for (int i = 0; i < AE; ++i) oacc[qb][b][i] *= alpha;
       }
     };
 
@@ -863,7 +999,7 @@ __global__ __launch_bounds__(W * 64, (kGroupsPerCU<D, W>)) void attn_fwd_bf16_ke
     // unrolled by four half-steps so that every access names one fixed LDS
     // buffer.
     const int grp_id = wave / kGroupWaves;
-    f32x16 sacc[kQB][KB];
+    Acc sacc[QB][KB];
     auto mfma_phase = [&](int t, const u32x4* kb, const u32x4* vb) __attribute__((always_inline)) {
       // One instruction stream for every tile up to my_total: at t = 0 the
       // PV half multiplies the zeroed P by the zeroed V buffer (a no-op), and at
@@ -880,7 +1016,7 @@ __global__ __launch_bounds__(W * 64, (kGroupsPerCU<D, W>)) void attn_fwd_bf16_ke
       if (t >= 0 && t < my_total) {
         const bool masked = t >= my_full;
 #pragma unroll
-        for (int qb = 0; qb < kQB; ++qb) {
+        for (int qb = 0; qb < QB; ++qb) {
           bf16x8 pnew[PS];
           const float alpha = softmax(sacc[qb], qb, tile_of(t), masked, pnew);
           rescale(qb, alpha);
@@ -931,9 +1067,11 @@ __global__ __launch_bounds__(W * 64, (kGroupsPerCU<D, W>)) void attn_fwd_bf16_ke
     // multiplies the zeroed P by them, and V data there (0 * Inf = NaN for a
     // key some rows never see) could change those rows.
 #pragma unroll
-    for (int ps = 0; ps < PS; ++ps) pprev[0][ps] = bf16x8{};
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+      for (int ps = 0; ps < PS; ++ps) pprev[qb][ps] = bf16x8{};
     load_k(kbuf0, tile_of(0));
-    for (int i = tid; i < TL::VCHUNKS; i += kWaves * 64) vbuf1[i] = u32x4{0u, 0u, 0u, 0u};
+    for (int i = tid; i < TL::VCHUNKS + TL::VSLACK; i += kWaves * 64) vbuf1[i] = u32x4{0u, 0u, 0u, 0u};
     prep_q();
     wait_vm();
     __syncthreads();
@@ -950,7 +1088,7 @@ __global__ __launch_bounds__(W * 64, (kGroupsPerCU<D, W>)) void attn_fwd_bf16_ke
     // S(0) alone at t = 0, both products for t < n, the last PV product
     // alone at t = n, and nothing after that. The loop is unrolled by two so
     // every access names one fixed LDS buffer.
-    f32x16 sacc[kQB][KB];
+    Acc sacc[QB][KB];
     // modes: 0 loads and barrier only, 1 first tile (QK), 2 both products, 3 last PV
     auto iteration = [&](auto parity, auto mode, int t) __attribute__((always_inline)) {
       constexpr int PAR = decltype(parity)::value;
@@ -973,7 +1111,7 @@ __global__ __launch_bounds__(W * 64, (kGroupsPerCU<D, W>)) void attn_fwd_bf16_ke
         if constexpr (MODE != 3) {
           const bool masked = t >= my_full;
 #pragma unroll
-          for (int qb = 0; qb < kQB; ++qb) {
+          for (int qb = 0; qb < QB; ++qb) {
             bf16x8 pnew[PS];
             const float alpha = softmax(sacc[qb], qb, tile_of(t), masked, pnew);
             rescale(qb, alpha);
@@ -1030,9 +1168,39 @@ __global__ __launch_bounds__(W * 64, (kGroupsPerCU<D, W>)) void attn_fwd_bf16_ke
     // columns of group 2q and lane l + 32 those of group 2q+1: half as many
     // stores, 16 bytes each. The swap runs in every lane; only the stores
     // depend on the row.
-    if (active) {
+    if (active && M16) {
+      // 16 x 16 tiles: lane l holds d = 16 b + 4 (l / 16) + 0..3 of query
+      // row0 + 16 qb + l % 16, so 16-lane rows 2j and 2j + 1 hold the two
+      // halves of columns 16 b + 8 j .. + 7. One row-pair swap per pair of d
+      // blocks (2m, 2m + 1) gives the even row those eight columns of block 2m
+      // and the odd row those of block 2m + 1: 16-byte stores.
 #pragma unroll
-      for (int qb = 0; qb < kQB; ++qb) {
+      for (int qb = 0; qb < QB; ++qb) {
+        const float l = quarters_sum(l_run[qb]);
+        const float inv = (l > 0.f) ? 1.f / l : 0.f;
+        const int row = me.row0 + QR * qb + qcol;
+        __bf16* orow = og + (size_t)row * q_rs;
+#pragma unroll
+        for (int m = 0; m < DB / 2; ++m) {
+          uint32_t w[2][2];
+#pragma unroll
+          for (int k = 0; k < 2; ++k)
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+              const bf16x2 h = {(__bf16)(oacc[qb][2 * m + k][2 * e] * inv),
+                                (__bf16)(oacc[qb][2 * m + k][2 * e + 1] * inv)};
+              w[k][e] = __builtin_bit_cast(uint32_t, h);
+            }
+          const auto s0 = __builtin_amdgcn_permlane16_swap(w[0][0], w[1][0], false, false);
+          const auto s1 = __builtin_amdgcn_permlane16_swap(w[0][1], w[1][1], false, false);
+          const u32x4 v = {s0[0], s1[0], s0[1], s1[1]};
+          const int b = 2 * m + (qgrp & 1);
+          if (row < me.lq) *(u32x4*)(orow + b * 16 + 8 * (qgrp >> 1)) = v;
+        }
+      }
+    } else if (active) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
         const float l = halves_sum(l_run[qb]);
         const float inv = (l > 0.f) ? 1.f / l : 0.f;
         const int row = me.row0 + 32 * qb + col;
