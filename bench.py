@@ -166,6 +166,15 @@ class Runner:
             self.work = torch.empty(w.k.shape[0] + 1, dtype=torch.int32, device="cuda")
         import tiled_attention_attn_amd as taa
         self.taa = taa
+        # Whether the library runs this problem on its 8-wave d = 128 schedule, whose
+        # products use v_mfma_f32_16x16x32_bf16 (the library's rule: bf16, d = 128, at
+        # least 4096 keys, block-sparse blocks a multiple of 256 rows, no override).
+        m = w.meta
+        lk = m.get("Lk", m.get("max_Lk", 0))
+        forced = os.environ.get("ATTN_BF16_WAVES", "")
+        self.m16 = (w.dtype == "bf16" and m.get("d") == 128 and
+                    ((lk >= 4096 and forced in ("", "0")) or forced == "8") and
+                    (w.block_mask is None or w.blk % 256 == 0))
 
     def __call__(self):
         if self.qknorm:
@@ -605,8 +614,10 @@ def ceiling(reps: int = 3) -> dict:
     wg, waves, iters = 512, 8, 40000
     sink = torch.empty(wg * waves * 64, dtype=torch.float32, device="cuda")
     flops = wg * waves * iters * 8 * 32768
-    for name, ops in (("mfma_bf16_normal_operands", ops_n), ("mfma_bf16_constant_operands", ops_c)):
-        ms = timed(lambda: b.ceiling_mfma_bf16(ops, sink, wg, waves, iters))
+    for name, probe, ops in (("mfma_bf16_normal_operands", b.ceiling_mfma_bf16, ops_n),
+                             ("mfma_bf16_constant_operands", b.ceiling_mfma_bf16, ops_c),
+                             ("mfma16_bf16_normal_operands", b.ceiling_mfma16_bf16, ops_n)):
+        ms = timed(lambda: probe(ops, sink, wg, waves, iters))
         tf = flops / (ms * 1e-3) / 1e12
         out[name] = {"TFLOP/s": round(tf, 1), "frac_of_spec": round(tf / PEAK_TFLOPS["bf16"], 4),
                      "ms": round(ms, 3)}
@@ -729,7 +740,10 @@ def main():
     del run
     torch.cuda.empty_cache()
     ceil = None if args.no_ceiling else ceiling()
-    measured = None if ceil is None else ceil["mfma_bf16_normal_operands"]["TFLOP/s"]
+    # the probe of the matrix-core shape the measured kernel runs (16 x 16 x 32 for
+    # the 8-wave d = 128 schedule, 32 x 32 x 16 otherwise)
+    probe = "mfma16_bf16_normal_operands" if run.m16 else "mfma_bf16_normal_operands"
+    measured = None if ceil is None else ceil[probe]["TFLOP/s"]
     roofline = {"bound": "mfma", "achieved": round(tflops, 3), "peak": peak, "unit": "TFLOP/s",
                 "frac": round(tflops / peak, 4), "traffic": traffic,
                 "achieved_cold": round(tf_cold, 3), "frac_cold": round(tf_cold / peak, 4),
@@ -737,8 +751,9 @@ def main():
     if measured and w.dtype == "bf16":
         roofline.update({
             "measured_peak": measured,
-            "measured_peak_source": "ceiling.mfma_bf16_normal_operands: v_mfma_f32_32x32x16_bf16 "
-                                    "from registers, N(0,1) operands, this GPU, this run",
+            "measured_peak_source": f"ceiling.{probe}: "
+                                    + ("v_mfma_f32_16x16x32_bf16" if run.m16 else "v_mfma_f32_32x32x16_bf16")
+                                    + " from registers, N(0,1) operands, this GPU, this run",
             "frac_of_measured_peak": round(tflops / measured, 4),
             "frac_cold_of_measured_peak": round(tf_cold / measured, 4)})
     out = {

@@ -40,6 +40,15 @@ int attn_ceiling_mfma_bf16(const void* operands, int64_t operand_lanes, float* o
                            int workgroups, int waves, int iters, void* stream);
 
 /*
+ * The same on v_mfma_f32_16x16x32_bf16: each wave runs `iters` iterations of
+ * 16 of them (16384 FLOPs each) on 8 independent accumulators, from the same
+ * operand buffer and with the same arguments as attn_ceiling_mfma_bf16.
+ * FLOPs = workgroups * waves * iters * 16 * 16384.
+ */
+int attn_ceiling_mfma16_bf16(const void* operands, int64_t operand_lanes, float* out,
+                             int workgroups, int waves, int iters, void* stream);
+
+/*
  * Exponential rate: 256 threads per workgroup, 16 independent chains x <- 2^-x
  * per thread (one v_exp_f32 each). Exponentials = workgroups * 256 * iters * 16.
  *   out  workgroups x 256 floats (written)

@@ -51,7 +51,7 @@ def test_header_declares_the_entry_points():
                                           "attn_version", "ikbo_linear"]
     assert declared_functions(os.path.join(INCLUDE, "attn_ceiling.h")) == [
         "attn_ceiling_copy", "attn_ceiling_exp2", "attn_ceiling_exp2_fma", "attn_ceiling_fma",
-        "attn_ceiling_lds_read", "attn_ceiling_mfma_bf16"]
+        "attn_ceiling_lds_read", "attn_ceiling_mfma16_bf16", "attn_ceiling_mfma_bf16"]
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -268,6 +268,8 @@ def test_ceiling_probe_argument_checks(lib):
     assert lib.attn_ceiling_mfma_bf16(FAKE, 1, FAKE, 1, 6, 1, None) == -1    # waves not 4 or 8
     assert lib.attn_ceiling_mfma_bf16(MISALIGNED, 1, FAKE, 1, 8, 1, None) == -1
     assert lib.attn_ceiling_mfma_bf16(FAKE, 1, FAKE, 0, 8, 1, None) == -1    # no workgroups
+    assert lib.attn_ceiling_mfma16_bf16(None, 1, FAKE, 1, 8, 1, None) == -1
+    assert lib.attn_ceiling_mfma16_bf16(FAKE, 1, FAKE, 1, 6, 1, None) == -1  # waves not 4 or 8
     assert lib.attn_ceiling_exp2(None, 1, 1, None) == -1
     assert lib.attn_ceiling_exp2(FAKE, 0, 1, None) == -1
     assert lib.attn_ceiling_fma(FAKE, 1, 0, None) == -1                      # no iterations

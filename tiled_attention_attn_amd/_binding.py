@@ -76,12 +76,14 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.attn_version.restype = i32
     i64 = ctypes.c_int64
     lib.attn_ceiling_mfma_bf16.argtypes = [vp, i64, vp, i32, i32, i32, vp]
+    lib.attn_ceiling_mfma16_bf16.argtypes = [vp, i64, vp, i32, i32, i32, vp]
     lib.attn_ceiling_exp2.argtypes = [vp, i32, i32, vp]
     lib.attn_ceiling_fma.argtypes = [vp, i32, i32, vp]
     lib.attn_ceiling_exp2_fma.argtypes = [vp, i32, i32, vp]
     lib.attn_ceiling_lds_read.argtypes = [vp, i32, i32, i32, vp]
     lib.attn_ceiling_copy.argtypes = [vp, vp, i64, vp]
-    for fn in (lib.attn_ceiling_mfma_bf16, lib.attn_ceiling_exp2, lib.attn_ceiling_fma,
+    for fn in (lib.attn_ceiling_mfma_bf16, lib.attn_ceiling_mfma16_bf16, lib.attn_ceiling_exp2,
+               lib.attn_ceiling_fma,
                lib.attn_ceiling_exp2_fma,
                lib.attn_ceiling_lds_read, lib.attn_ceiling_copy):
         fn.restype = i32
@@ -421,6 +423,17 @@ def ceiling_mfma_bf16(operands, out, workgroups, waves, iters, stream=None):
     _probe_check(load_library().attn_ceiling_mfma_bf16(_ptr(operands), lanes, _ptr(out),
                                                        int(workgroups), int(waves), int(iters),
                                                        _stream(stream)), "attn_ceiling_mfma_bf16")
+
+
+def ceiling_mfma16_bf16(operands, out, workgroups, waves, iters, stream=None):
+    """Enqueue the same probe on v_mfma_f32_16x16x32_bf16 (the same arguments).
+    FLOPs = workgroups*waves*iters*16*16384."""
+    lanes = operands.numel() // 128
+    if out.numel() < workgroups * waves * 64 or lanes < 1:
+        raise ValueError("ceiling_mfma16_bf16: buffers too small")
+    _probe_check(load_library().attn_ceiling_mfma16_bf16(_ptr(operands), lanes, _ptr(out),
+                                                         int(workgroups), int(waves), int(iters),
+                                                         _stream(stream)), "attn_ceiling_mfma16_bf16")
 
 
 def ceiling_exp2(out, workgroups, iters, stream=None):

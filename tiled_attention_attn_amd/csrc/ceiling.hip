@@ -3,7 +3,8 @@
 // runs them, so that a kernel's achieved rate can be read against both the
 // published peak and what the chip sustains under the same operand data.
 //
-//   mfma   v_mfma_f32_32x32x16_bf16 from registers, four independent
+//   mfma   v_mfma_f32_32x32x16_bf16 (or, mfma16, v_mfma_f32_16x16x32_bf16)
+//          from registers, four (eight) independent
 //          accumulator chains, eight distinct operand pairs per wave taken from
 //          the caller's buffer (N(0,1) data switches the operand bits the way
 //          attention inputs do; constant data does not)
@@ -29,6 +30,7 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
@@ -65,6 +67,40 @@ __global__ __launch_bounds__(W * 64) void mfma_kernel(const bf16x8* __restrict__
   for (int c = 0; c < 4; ++c)
 #pragma unroll
     for (int i = 0; i < 16; ++i) s += acc[c][i];
+  out[gl] = s;
+}
+
+// The same stream on v_mfma_f32_16x16x32_bf16: 16 per iteration (the same
+// FLOPs as 8 of the 32 x 32 x 16 shape) into 8 independent accumulators.
+template <int W>
+__global__ __launch_bounds__(W * 64) void mfma16_kernel(const bf16x8* __restrict__ ops,
+                                                        int64_t op_lanes, float* __restrict__ out,
+                                                        int iters) {
+  const int64_t gl = (int64_t)blockIdx.x * (W * 64) + threadIdx.x;
+  const bf16x8* src = ops + (gl % op_lanes) * (2 * kOpPairs);
+  bf16x8 a[kOpPairs], b[kOpPairs];
+#pragma unroll
+  for (int j = 0; j < kOpPairs; ++j) {
+    a[j] = src[j];
+    b[j] = src[kOpPairs + j];
+  }
+  f32x4 acc[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[c][i] = 0.f;
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+#pragma unroll
+      for (int j = 0; j < kOpPairs; ++j)
+        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[j], b[(j + r) % kOpPairs], acc[j], 0, 0, 0);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int c = 0; c < 8; ++c)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s += acc[c][i];
   out[gl] = s;
 }
 
@@ -204,6 +240,21 @@ int attn_ceiling_mfma_bf16(const void* operands, int64_t operand_lanes, float* o
                        (const bf16x8*)operands, operand_lanes, out, iters);
   else
     hipLaunchKernelGGL(mfma_kernel<8>, dim3(workgroups), dim3(512), 0, (hipStream_t)stream,
+                       (const bf16x8*)operands, operand_lanes, out, iters);
+  return launched();
+}
+
+int attn_ceiling_mfma16_bf16(const void* operands, int64_t operand_lanes, float* out,
+                           int workgroups, int waves, int iters, void* stream) {
+  if (operands == nullptr || out == nullptr || operand_lanes < 1 || workgroups < 1 ||
+      iters < 1 || (waves != 4 && waves != 8) || ((uintptr_t)operands & 15u) != 0)
+    return -1;
+  (void)hipGetLastError();
+  if (waves == 4)
+    hipLaunchKernelGGL(mfma16_kernel<4>, dim3(workgroups), dim3(256), 0, (hipStream_t)stream,
+                       (const bf16x8*)operands, operand_lanes, out, iters);
+  else
+    hipLaunchKernelGGL(mfma16_kernel<8>, dim3(workgroups), dim3(512), 0, (hipStream_t)stream,
                        (const bf16x8*)operands, operand_lanes, out, iters);
   return launched();
 }
