@@ -737,12 +737,13 @@ def main():
     peak = PEAK_TFLOPS[w.dtype]
     err, err_at = sampled_error(run)
     traffic = traffic_for(args.workload)
+    m16 = run.m16
     del run
     torch.cuda.empty_cache()
     ceil = None if args.no_ceiling else ceiling()
     # the probe of the matrix-core shape the measured kernel runs (16 x 16 x 32 for
     # the 8-wave d = 128 schedule, 32 x 32 x 16 otherwise)
-    probe = "mfma16_bf16_normal_operands" if run.m16 else "mfma_bf16_normal_operands"
+    probe = "mfma16_bf16_normal_operands" if m16 else "mfma_bf16_normal_operands"
     measured = None if ceil is None else ceil[probe]["TFLOP/s"]
     roofline = {"bound": "mfma", "achieved": round(tflops, 3), "peak": peak, "unit": "TFLOP/s",
                 "frac": round(tflops / peak, 4), "traffic": traffic,
@@ -752,7 +753,7 @@ def main():
         roofline.update({
             "measured_peak": measured,
             "measured_peak_source": f"ceiling.{probe}: "
-                                    + ("v_mfma_f32_16x16x32_bf16" if run.m16 else "v_mfma_f32_32x32x16_bf16")
+                                    + ("v_mfma_f32_16x16x32_bf16" if m16 else "v_mfma_f32_32x32x16_bf16")
                                     + " from registers, N(0,1) operands, this GPU, this run",
             "frac_of_measured_peak": round(tflops / measured, 4),
             "frac_cold_of_measured_peak": round(tf_cold / measured, 4)})
