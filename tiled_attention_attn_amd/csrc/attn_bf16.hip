@@ -30,6 +30,17 @@
 // agree; it is chosen to match the C layout of S^T, so P needs no shuffle:
 //   slot j of half h in PV step t  <->  key 16t + (j/4)*8 + 4h + j%4.
 //
+// The 8-wave d = 128 schedule uses MFMA 16x16x32 bf16 instead (it sustains a
+// higher rate at the chip's power limit). Lane layout (checked on the device):
+//   A (16 x 32): lane l holds row l%16, k-slots (l/16)*8 .. +7
+//   B (32 x 16): lane l holds col l%16, k-slots (l/16)*8 .. +7
+//   C (16 x 16): lane l holds col l%16, rows (l/16)*4 + i, i < 4
+// A wave's 32 queries are two blocks of 16 (lane l holds query l%16 of each)
+// and a key tile is four blocks of 16 (lane l holds keys 4(l/16) .. +3 of
+// each); row reductions exchange across the four 16-lane rows. In PV step c
+// (32 keys), slot j of row g  <->  key 32c + 4g + j (j < 4), 32c + 16 + 4g +
+// j - 4 (j >= 4): key blocks 2c and 2c + 1 as the C layout holds them.
+//
 // Pipeline. K/V tiles move HBM -> LDS with direct-to-LDS buffer loads (no
 // register staging) into two buffers each, shared by all 8 waves. The waves
 // form two groups (waves 0-3 and 4-7; waves w and w+4 share a SIMD) that
