@@ -662,7 +662,8 @@ __global__ __launch_bounds__(W * 64, (kGroupsPerCU<D, W>)) void attn_fwd_bf16_ke
       // operands (one bf16 rounding of c * q), so the score MFMAs produce
       // base-2 logits directly. RMS normalisation of the query row is fused
       // the same way: the normalised queries never leave registers (the two
-      // lane halves hold the two halves of the row).
+      // lane halves, or with 16 x 16 tiles the four 16-lane rows, hold the parts
+      // of the row).
       if (!p.qnorm) {
 #pragma unroll
         for (int s = 0; s < QS; ++s)
@@ -958,8 +959,9 @@ __global__ __launch_bounds__(W * 64, (kGroupsPerCU<D, W>)) void attn_fwd_bf16_ke
           return 1.f;
         }
       }
-      // Exact path: the row max of sacc (max chains, then one exchange
-      // between the lane halves). The reference moves up to the row max, or,
+      // Exact path: the row max of sacc (max chains, then the exchange between
+      // the lane halves, and with 16 x 16 tiles between the 16-lane rows). The
+      // reference moves up to the row max, or,
       // on a row's first unmasked tile, to it from wherever it was.
       float pm[8];
       constexpr int NE = KB * AE;   // the lane's scores of the row (32 either way)
